@@ -1,0 +1,255 @@
+#!/usr/bin/env python3
+"""Benchmark of the LSA hot path on one MI355X.
+
+Default workload: prefill, 1 sequence of L = 32768 tokens (indexer H_I=64,
+d_I=128 int8; 4 sinks + 512 window + top-k to 2048 keys; 64 query heads on one
+bf16 KV head, head dim 128). One step = fused indexer scoring + top-k selection
+for every row, then sparse attention for every row. Inputs are synthetic,
+seeded, and resident in HBM before timing starts.
+
+Prints ONE JSON line with throughput, the roofline of the dominant call
+(timed live with HIP events on the stream the kernels run on), and the CPU
+oracle timed on a bounded sample of the same workload.
+
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--config c2]
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_I8_TOPS = 5000.0      # MI355X dense int8
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16
+PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=5)
+    p.add_argument("--warmup", type=int, default=2)
+    p.add_argument("--config", default="c2", choices=["c1", "c2", "c3", "c4", "c5"])
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-rows", type=int, default=0, help="oracle sample size (0: automatic)")
+    return p.parse_args()
+
+
+def candidate_pairs(L, n_sink, W, K_tot):
+    """Scored (query, key) pairs of a causal prefill: rows t >= K_tot score
+    the candidates n_sink..t-W; shorter rows keep every key unscored."""
+    s = 0
+    for t in range(K_tot, L):
+        s += t - W - n_sink + 1
+    return s
+
+
+class EventTimer:
+    """HIP events on the current stream around each call of a named part."""
+
+    def __init__(self, torch):
+        self.torch = torch
+        self.pending = {}
+
+    def __call__(self, name, fn, *a, **kw):
+        t = self.torch
+        e0, e1 = t.cuda.Event(enable_timing=True), t.cuda.Event(enable_timing=True)
+        e0.record()
+        r = fn(*a, **kw)
+        e1.record()
+        self.pending.setdefault(name, []).append((e0, e1))
+        return r
+
+    def ms(self, name):
+        ev = self.pending.get(name, [])
+        return sum(a.elapsed_time(b) for a, b in ev) / max(1, len(ev)), len(ev)
+
+
+def cpu_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        n = [i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"]
+        if n:
+            return int(max(n))
+    except Exception:
+        pass
+    return len(os.sched_getaffinity(0))
+
+
+def prefill_cpu_baseline(wl, q_idx, k_idx, w, q, k, v, rows):
+    """The oracle on `rows` sampled query rows: scoring, selection, attention."""
+    import numpy as np
+    import oracle as O
+    qn = q_idx[0].cpu().numpy()
+    kn = k_idx[0].cpu().numpy()
+    kf, vf = k[0].cpu().double().numpy(), v[0].cpu().double().numpy()
+    qrows = {t: q[0, t].cpu().double().numpy() for t in rows}
+    t0 = time.perf_counter()
+    for t in rows:
+        S = O.index_scores(qn[t:t + 1], kn[: t + 1], w, q_off=t)[0]
+        sel = O.select_flat(S, t, wl.n_sink, wl.n_window, wl.k_dyn)
+        for _ in range(wl.n_layers):
+            O.attend(qrows[t], kf, vf, sel, wl.scale)
+    dt = time.perf_counter() - t0
+    return len(rows) / dt, dt
+
+
+def run_prefill(args, wl, torch):
+    from long_context_sparse_lsa_amd import _lib as L
+    from long_context_sparse_lsa_amd import synth
+    dev = "cuda"
+    q_idx, k_idx, w = synth.indexer_inputs(wl, dev)
+    layers = [synth.attention_inputs(wl, layer, dev) for layer in range(wl.n_layers)]
+    torch.cuda.synchronize()
+    timer = EventTimer(torch)
+
+    def step(tm):
+        idx, n_sel = tm("select", L.lsa_select_topk, q_idx, k_idx, w, wl.n_sink, wl.n_window, wl.k_dyn, q_off=0)
+        for q, k, v in layers:
+            tm("attn", L.lsa_sparse_attn_prefill, q, k, v, idx, n_sel)
+        return idx, n_sel
+
+    plain = lambda name, fn, *a, **kw: fn(*a, **kw)  # noqa: E731
+    for _ in range(args.warmup):
+        step(plain)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        idx, n_sel = step(timer)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = wall * 1e3 / args.steps
+    sel_ms, _ = timer.ms("select")
+    attn_ms, n_attn = timer.ms("attn")
+
+    pairs = candidate_pairs(wl.L, wl.n_sink, wl.n_window, wl.K_tot)
+    i8_ops = 2.0 * wl.H_I * wl.d_I * pairs
+    n_sel_sum = float(n_sel.sum().item())
+    attn_flop = 4.0 * wl.H * wl.D * n_sel_sum
+    sel_tops = i8_ops / (sel_ms * 1e-3) / 1e12
+    attn_tflops = attn_flop / (attn_ms * 1e-3) / 1e12
+    if sel_ms * 1 >= attn_ms * wl.n_layers:
+        roof = {"bound": "mfma", "kernel": "lsa_select_topk (fused int8 indexer + top-k)",
+                "achieved": round(sel_tops, 2), "peak": PEAK_I8_TOPS, "unit": "TFLOP/s",
+                "frac": round(sel_tops / PEAK_I8_TOPS, 4), "traffic": None,
+                "work_per_launch": f"{i8_ops:.4e} int8 op (2*H_I*d_I per scored pair)"}
+    else:
+        roof = {"bound": "mfma", "kernel": "lsa_sparse_attn_prefill (bf16)",
+                "achieved": round(attn_tflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                "work_per_launch": f"{attn_flop:.4e} flop (4*H*D per selected key)"}
+    out = {
+        "metric": "LSA prefill tokens/s",
+        "value": round(wl.L / (ms_step * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "int8+bf16", "data": "synthetic",
+        "config": {"workload": wl.name, "global_batch": wl.B, "seq_len": wl.L, "layers": wl.n_layers,
+                   "H_I": wl.H_I, "d_I": wl.d_I, "H": wl.H, "D": wl.D,
+                   "n_sink": wl.n_sink, "n_window": wl.n_window, "K_tot": wl.K_tot, "parallelism": "none"},
+        "parts": {"select_ms": round(sel_ms, 4), "select_int8_tops": round(sel_tops, 1),
+                  "attn_ms_per_layer": round(attn_ms, 4), "attn_bf16_tflops": round(attn_tflops, 1),
+                  "attn_calls": n_attn},
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        import numpy as np
+        n_rows = args.cpu_rows or (8 if wl.L >= 100000 else 24)
+        rng = np.random.default_rng(5)
+        rows = sorted(int(x) for x in rng.integers(wl.K_tot, wl.L, n_rows))
+        q, k, v = layers[0]
+        rate, dt = prefill_cpu_baseline(wl, q_idx, k_idx, w, q, k, v, rows)
+        out["cpu_baseline"] = {"value": round(rate, 3), "unit": "tokens/s", "cores": cpu_threads(),
+                               "kind": "oracle",
+                               "sample": f"{len(rows)} rows drawn uniformly from [{wl.K_tot}, {wl.L}), "
+                                         f"full score+select+{wl.n_layers}x attention per row, {dt:.1f} s"}
+    return out
+
+
+def run_decode(args, wl, torch):
+    from long_context_sparse_lsa_amd import _lib as L
+    from long_context_sparse_lsa_amd import synth
+    dev = "cuda"
+    q_idx, k_idx, w = synth.indexer_inputs(wl, dev)
+    q, kc, vc = synth.attention_inputs(wl, 0, dev)
+    q1 = q_idx[:, None].contiguous()
+    kblk = L.lsa_block_summary(k_idx, wl.blk) if wl.blk else None
+    torch.cuda.synchronize()
+    timer = EventTimer(torch)
+    N = wl.L
+
+    def step(tm):
+        if wl.blk:
+            idx, n_sel = tm("select", L.lsa_hier_select, q_idx, k_idx, kblk, w, wl.blk, wl.n_blk_recall,
+                            wl.n_sink, wl.n_window, wl.k_dyn)
+            idx, n_sel = idx[:, None], n_sel[:, None]
+        else:
+            idx, n_sel = tm("select", L.lsa_select_topk, q1, k_idx, w, wl.n_sink, wl.n_window, wl.k_dyn,
+                            q_off=N - 1)
+        return tm("attn", L.lsa_sparse_attn_decode, q, kc, vc, idx, n_sel, n_split=wl.n_split)
+
+    plain = lambda name, fn, *a, **kw: fn(*a, **kw)  # noqa: E731
+    for _ in range(args.warmup):
+        step(plain)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(timer)
+    torch.cuda.synchronize()
+    us_step = (time.perf_counter() - t0) * 1e6 / args.steps
+    sel_ms, _ = timer.ms("select")
+    attn_ms, _ = timer.ms("attn")
+    K_tot = wl.K_tot
+    kv_bytes = wl.B * K_tot * wl.D * 2 * 2
+    qo_bytes = 2 * wl.B * wl.n_q * wl.H * wl.D * 2
+    if wl.blk:
+        nb = N // wl.blk
+        idx_bytes = wl.B * (nb * wl.d_I + wl.n_blk_recall * wl.blk * wl.d_I)
+    else:
+        idx_bytes = wl.B * N * wl.d_I
+    step_bytes = idx_bytes + kv_bytes + qo_bytes
+    sel_gbs = idx_bytes / (sel_ms * 1e-3) / 1e9
+    out = {
+        "metric": "LSA decode us/step",
+        "value": round(us_step, 2), "unit": "us/step",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(us_step / 1e3, 5),
+        "higher_is_better": False, "scaling": "weak", "vs_baseline": None,
+        "dtype": "int8+bf16", "data": "synthetic",
+        "config": {"workload": wl.name, "global_batch": wl.B, "context": N, "n_q": wl.n_q, "H": wl.H,
+                   "K_tot": K_tot, "n_split": wl.n_split, "hier_blk": wl.blk, "parallelism": "none"},
+        "parts": {"select_us": round(sel_ms * 1e3, 2), "attn_us": round(attn_ms * 1e3, 2),
+                  "step_bytes": step_bytes, "step_hbm_frac": round(step_bytes / (us_step * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)},
+        "roofline": {"bound": "hbm", "kernel": "decode select (indexer key scan + top-k)",
+                     "achieved": round(sel_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(sel_gbs / PEAK_HBM_GBS, 4), "traffic": None,
+                     "work_per_launch": f"{idx_bytes} B of indexer keys"},
+    }
+    return out
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(the sharding design is described in DESIGN.md). Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from long_context_sparse_lsa_amd import configs
+    from long_context_sparse_lsa_amd import _lib as L
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    L.load()
+    wl = configs.BY_ID[args.config]
+    out = run_prefill(args, wl, torch) if wl.kind == "prefill" else run_decode(args, wl, torch)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

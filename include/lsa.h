@@ -1,0 +1,147 @@
+/*
+ * lsa.h — C ABI of the LongCat Sparse Attention (LSA) hot path on MI355X (gfx950).
+ *
+ * What the calls compute (page title, section):
+ *   LongCat-2.0 release article (techsir.com), section "LongCat 稀疏注意力":
+ *     a lightweight indexer scores the cached keys for each query; the
+ *     streaming-aware indexing (SI) paragraph mixes a contiguous, hardware-
+ *     aligned read with dynamically chosen keys; the cross-layer indexing (CLI)
+ *     paragraph reuses one index across consecutive layers and across the
+ *     three MTP draft steps; the hierarchical indexing (HI) paragraph scores
+ *     blocks coarsely and then tokens inside the recalled blocks.
+ *   "如何在 5 万张国产芯片训练出 1.6T 万亿参数模型？", section "架构拆解 ① LSA":
+ *     each query reads only the top-k keys plus a few fixed sink tokens.
+ *   same page, section "③ KVP 解码切分示意": partial attention over parts of
+ *     the KV cache, merged afterwards (here: split-KV with a log-sum-exp merge).
+ *
+ * Indexer arithmetic (the pages leave it open; this library fixes it):
+ *   S[t, s] = sum_h w[h] * max(0, sum_d q_idx[t, h, d] * k_idx[s, d])
+ * with int8 q_idx / k_idx, int32 weights and an exact int32 result. Selection
+ * keeps sinks 0..n_sink-1, the window t-n_window+1..t and the k_dyn best of the
+ * candidates n_sink..t-n_window by (score descending, position ascending); a
+ * query with t+1 <= K_tot keeps every key 0..t. Output lists are ascending,
+ * padded with -1 past n_sel.
+ *
+ * Conventions for every entry point:
+ *   - Tensors are caller-owned, contiguous, row-major DEVICE buffers, 16-byte
+ *     aligned, except `w`, which is a short HOST array (copied into the kernel
+ *     arguments at the call). The library never allocates or frees memory.
+ *   - All work is enqueued on `stream` (a hipStream_t passed as void*; NULL is
+ *     the null stream) and the call returns after enqueueing.
+ *   - Argument errors are returned synchronously before anything is launched;
+ *     a kernel fault surfaces at the caller's next synchronisation.
+ *   - Position lists (`idx`) given to the attention calls are trusted to be
+ *     < n_k; entries outside [0, n_k) are skipped rather than read.
+ *   - Workspace: pass ws = NULL to get the byte count in *ws_needed; then pass
+ *     a device buffer of at least that size. Workspace content is scratch.
+ *   - Results are deterministic: repeated calls give bit-identical outputs
+ *     (no floating-point atomics; fixed reduction and merge orders).
+ */
+#ifndef LSA_H
+#define LSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef uint16_t lsa_bf16; /* bfloat16 bit pattern */
+
+/* Selection budget: K_tot = n_sink + n_window + k_dyn. n_window = 0 turns the
+ * SI window off; k_dyn = 0 keeps only sinks and window. */
+typedef struct {
+  int32_t n_sink;
+  int32_t n_window;
+  int32_t k_dyn;
+} lsa_select_cfg;
+
+enum {
+  LSA_OK = 0,
+  LSA_INVALID_ARG = 1, /* NULL, misaligned, non-positive or inconsistent sizes */
+  LSA_UNSUPPORTED = 2, /* shape outside the tuned set (see each call)         */
+  LSA_WORKSPACE = 3,   /* workspace too small                                 */
+  LSA_RANGE = 4,       /* sum_h |w[h]| * d_I * 128 * 128 >= 2^31: int32 not exact */
+  LSA_HIP = 5          /* a HIP launch reported an error                       */
+};
+
+/* Human-readable name of a status code (static storage). */
+const char* lsa_status_string(int32_t status);
+
+/* Indexer scores (step "index first" of the LSA section).
+ *   q_idx  [B, n_q, H_I, d_I] int8 ; query row i of each sequence sits at
+ *                                    position q_off + i
+ *   k_idx  [B, n_k, d_I] int8
+ *   w      [H_I] int32, HOST array
+ *   scores [B, n_q, n_k] int32 out: S for s <= q_off + i, INT32_MIN otherwise
+ * Supported: d_I in {64, 128}; H_I in {4, 8, 16, 32, 64, 128}. */
+int32_t lsa_index_score(const int8_t* q_idx, const int8_t* k_idx, const int32_t* w,
+                        int32_t B, int32_t n_q, int32_t n_k, int32_t H_I, int32_t d_I,
+                        int32_t q_off, int32_t* scores, void* stream);
+
+/* Flat selection: sinks + SI window + dynamic top-k (SI paragraph; sinks).
+ *   scores  [B, n_q, n_k] int32 as written by lsa_index_score, or NULL: then
+ *           the call scores q_idx / k_idx / w itself (fused indexer + top-k)
+ *   idx     [B, n_q, K_tot] int32 out, ascending, -1 padded
+ *   n_sel   [B, n_q] int32 out, min(q_off + i + 1, K_tot)
+ * Requires q_off + n_q <= n_k. */
+int32_t lsa_select_topk(const int32_t* scores, const int8_t* q_idx, const int8_t* k_idx,
+                        const int32_t* w, int32_t B, int32_t n_q, int32_t n_k, int32_t H_I,
+                        int32_t d_I, int32_t q_off, lsa_select_cfg cfg, int32_t* idx,
+                        int32_t* n_sel, void* ws, size_t ws_bytes, size_t* ws_needed,
+                        void* stream);
+
+/* HI block summary: k_blk[b, j, :] = clamp(round-half-even(mean of the keys of
+ * block j), -128, 127); a tail block of c < blk keys uses its own mean.
+ *   k_idx [B, n_k, d_I] int8 -> k_blk [B, ceil(n_k / blk), d_I] int8
+ * Supported: blk in [1, 1024]; d_I in {64, 128}. */
+int32_t lsa_block_summary(const int8_t* k_idx, int32_t B, int32_t n_k, int32_t d_I,
+                          int32_t blk, int8_t* k_blk, void* stream);
+
+/* HI decode selection for the query at position n_k - 1 (HI paragraph).
+ * Coarse: blocks intersecting the candidate range are scored with the indexer
+ * formula against k_blk; the n_blk_recall best (score desc, block asc) are
+ * recalled. Fine: candidate tokens inside them are scored and the best
+ * min(k_dyn, #candidates) kept; sinks and window added as in the flat case.
+ *   q_idx [B, H_I, d_I] int8, k_idx [B, n_k, d_I], k_blk from lsa_block_summary
+ *   idx [B, K_tot] int32 out (ascending, -1 padded), n_sel [B] int32 out
+ * Supported: blk a multiple of 32 in [32, 1024]. */
+int32_t lsa_hier_select(const int8_t* q_idx, const int8_t* k_idx, const int8_t* k_blk,
+                        const int32_t* w, int32_t B, int32_t n_k, int32_t H_I, int32_t d_I,
+                        int32_t blk, int32_t n_blk_recall, lsa_select_cfg cfg, int32_t* idx,
+                        int32_t* n_sel, void* ws, size_t ws_bytes, size_t* ws_needed,
+                        void* stream);
+
+/* Sparse attention, prefill: query row t of sequence b attends over the keys
+ * idx[b, t, 0 .. n_sel[b, t]-1] of its sequence (one KV head shared by H query
+ * heads); softmax(scale * q.k) in fp32, output bf16. Passing the same idx to
+ * consecutive layers is cross-layer index reuse (CLI paragraph).
+ *   q [B, L, H, D] bf16, k / v [B, n_k, D] bf16, idx [B, L, K_tot], n_sel [B, L]
+ *   o [B, L, H, D] bf16 out; lse [B, L, H] fp32 out (natural log) or NULL
+ * Supported: D = 128; H in {16, 32, 64, 128}. */
+int32_t lsa_sparse_attn_prefill(const lsa_bf16* q, const lsa_bf16* k, const lsa_bf16* v,
+                                const int32_t* idx, const int32_t* n_sel, int32_t B,
+                                int32_t L, int32_t n_k, int32_t H, int32_t D, int32_t K_tot,
+                                float scale, lsa_bf16* o, float* lse, void* stream);
+
+/* Sparse attention, decode with split-KV and a log-sum-exp merge (KVP section,
+ * one-GPU form). The selected list of each index row is cut into n_split
+ * contiguous parts of ceil(n_sel / n_split) entries; each part yields
+ * (max, sum, output) partials, merged over parts in a fixed binary tree.
+ *   q [B, n_q, H, D] bf16; k_cache / v_cache [B, n_k, D] bf16
+ *   idx [B, n_idx, K_tot], n_sel [B, n_idx]; n_idx = 1: every query row of a
+ *   sequence uses the one index (MTP draft reuse), else n_idx = n_q
+ *   o [B, n_q, H, D] bf16 out; lse [B, n_q, H] fp32 out or NULL
+ * Supported: D = 128; H in {16, 32, 64, 128}; n_split in [1, 64]. */
+int32_t lsa_sparse_attn_decode(const lsa_bf16* q, const lsa_bf16* k_cache,
+                               const lsa_bf16* v_cache, const int32_t* idx,
+                               const int32_t* n_sel, int32_t n_idx, int32_t B, int32_t n_q,
+                               int32_t n_k, int32_t H, int32_t D, int32_t K_tot,
+                               int32_t n_split, float scale, lsa_bf16* o, float* lse,
+                               void* ws, size_t ws_bytes, size_t* ws_needed, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* LSA_H */

@@ -1,0 +1,247 @@
+"""ctypes binding of liblsa.so (include/lsa.h).
+
+Argument marshalling only: each function takes torch device tensors, checks
+dtypes and shapes, allocates outputs and workspace with torch, and calls the
+C entry point of the same name on the current torch stream. There is no
+fallback: if the library is missing or a call fails, an exception is raised.
+"""
+import ctypes
+import os
+
+import numpy as np
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "liblsa.so")
+
+LSA_OK, LSA_INVALID_ARG, LSA_UNSUPPORTED, LSA_WORKSPACE, LSA_RANGE, LSA_HIP = range(6)
+
+
+class LSAError(RuntimeError):
+    def __init__(self, fn, status, msg):
+        super().__init__(f"{fn}: {msg}")
+        self.status = status
+
+
+class LSAUnavailable(RuntimeError):
+    pass
+
+
+class SelectCfg(ctypes.Structure):
+    _fields_ = [("n_sink", ctypes.c_int32), ("n_window", ctypes.c_int32), ("k_dyn", ctypes.c_int32)]
+
+
+_P = ctypes.c_void_p
+_I = ctypes.c_int32
+_F = ctypes.c_float
+_Z = ctypes.c_size_t
+_ZP = ctypes.POINTER(ctypes.c_size_t)
+
+SIGNATURES = {
+    "lsa_status_string": (ctypes.c_char_p, [_I]),
+    "lsa_index_score": (_I, [_P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _P]),
+    "lsa_select_topk": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, SelectCfg, _P, _P, _P, _Z, _ZP, _P]),
+    "lsa_block_summary": (_I, [_P, _I, _I, _I, _I, _P, _P]),
+    "lsa_hier_select": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, SelectCfg, _P, _P, _P, _Z, _ZP, _P]),
+    "lsa_sparse_attn_prefill": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _P, _P, _P]),
+    "lsa_sparse_attn_decode": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _F, _P, _P, _P, _Z, _ZP, _P]),
+}
+
+_lib = None
+
+
+def load(path=LIB_PATH):
+    """Load liblsa.so (after torch, so both share torch's HIP runtime)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise LSAUnavailable(f"{path} is missing: build it with python -m long_context_sparse_lsa_amd.build")
+    lib = ctypes.CDLL(path)
+    for name, (res, args) in SIGNATURES.items():
+        f = getattr(lib, name)
+        f.restype = res
+        f.argtypes = args
+    _lib = lib
+    return lib
+
+
+def status_string(s):
+    return load().lsa_status_string(int(s)).decode()
+
+
+def _check(fn, s):
+    if s != LSA_OK:
+        raise LSAError(fn, s, status_string(s))
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _dev(t, dtype, name):
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a CUDA (HIP) tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def _weights(w, H_I):
+    w = np.ascontiguousarray(np.asarray(w, dtype=np.int32).reshape(-1))
+    if w.shape[0] != H_I:
+        raise ValueError(f"w has {w.shape[0]} entries, H_I = {H_I}")
+    return w, w.ctypes.data_as(ctypes.c_void_p)
+
+
+def _workspace(nbytes, device):
+    return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
+
+
+# ----------------------------------------------------------------------------
+def lsa_index_score(q_idx, k_idx, w, q_off=None, out=None):
+    """q_idx [B, n_q, H_I, d_I] int8, k_idx [B, n_k, d_I] int8, w [H_I] host ints.
+    Returns scores [B, n_q, n_k] int32 (INT32_MIN where s > q_off + i).
+    q_off defaults to n_k - n_q (the rows are the last n_q positions)."""
+    lib = load()
+    _dev(q_idx, torch.int8, "q_idx")
+    _dev(k_idx, torch.int8, "k_idx")
+    B, n_q, H_I, d_I = q_idx.shape
+    n_k = k_idx.shape[1]
+    if k_idx.shape != (B, n_k, d_I):
+        raise ValueError("k_idx shape mismatch")
+    q_off = n_k - n_q if q_off is None else int(q_off)
+    wh, wp = _weights(w, H_I)
+    if out is None:
+        out = torch.empty((B, n_q, n_k), dtype=torch.int32, device=q_idx.device)
+    _check("lsa_index_score", lib.lsa_index_score(_ptr(q_idx), _ptr(k_idx), wp, B, n_q, n_k, H_I, d_I,
+                                                  q_off, _ptr(out), _stream()))
+    return out
+
+
+def lsa_select_topk(q_idx=None, k_idx=None, w=None, n_sink=4, n_window=0, k_dyn=0, q_off=None,
+                    scores=None, n_k=None, out=None):
+    """Flat selection. Either scores [B, n_q, n_k] int32 or (q_idx, k_idx, w)
+    for the fused path. Returns (idx [B, n_q, K_tot] int32, n_sel [B, n_q] int32)."""
+    lib = load()
+    K_tot = n_sink + n_window + k_dyn
+    cfg = SelectCfg(n_sink, n_window, k_dyn)
+    if scores is not None:
+        _dev(scores, torch.int32, "scores")
+        B, n_q, n_k = scores.shape
+        H_I = d_I = 0
+        wp = None
+        dev = scores.device
+    else:
+        _dev(q_idx, torch.int8, "q_idx")
+        _dev(k_idx, torch.int8, "k_idx")
+        B, n_q, H_I, d_I = q_idx.shape
+        n_k = k_idx.shape[1]
+        if k_idx.shape != (B, n_k, d_I):
+            raise ValueError("k_idx shape mismatch")
+        wh, wp = _weights(w, H_I)
+        dev = q_idx.device
+    q_off = n_k - n_q if q_off is None else int(q_off)
+    need = ctypes.c_size_t(0)
+    args = (_ptr(scores), _ptr(q_idx) if scores is None else None, _ptr(k_idx) if scores is None else None,
+            wp, B, n_q, n_k, H_I, d_I, q_off, cfg)
+    _check("lsa_select_topk", lib.lsa_select_topk(*args, None, None, None, 0, ctypes.byref(need), None))
+    ws = _workspace(need.value, dev)
+    if out is None:
+        idx = torch.empty((B, n_q, K_tot), dtype=torch.int32, device=dev)
+        n_sel = torch.empty((B, n_q), dtype=torch.int32, device=dev)
+    else:
+        idx, n_sel = out
+    _check("lsa_select_topk", lib.lsa_select_topk(*args, _ptr(idx), _ptr(n_sel), _ptr(ws), ws.numel(),
+                                                  None, _stream()))
+    return idx, n_sel
+
+
+def lsa_block_summary(k_idx, blk):
+    """k_idx [B, n_k, d_I] int8 -> k_blk [B, ceil(n_k/blk), d_I] int8."""
+    lib = load()
+    _dev(k_idx, torch.int8, "k_idx")
+    B, n_k, d_I = k_idx.shape
+    nb = -(-n_k // blk)
+    out = torch.empty((B, nb, d_I), dtype=torch.int8, device=k_idx.device)
+    _check("lsa_block_summary", lib.lsa_block_summary(_ptr(k_idx), B, n_k, d_I, blk, _ptr(out), _stream()))
+    return out
+
+
+def lsa_hier_select(q_idx, k_idx, k_blk, w, blk, n_blk_recall, n_sink, n_window, k_dyn):
+    """HI decode selection for the query at n_k - 1.
+    q_idx [B, H_I, d_I] int8. Returns (idx [B, K_tot], n_sel [B])."""
+    lib = load()
+    _dev(q_idx, torch.int8, "q_idx")
+    _dev(k_idx, torch.int8, "k_idx")
+    _dev(k_blk, torch.int8, "k_blk")
+    B, H_I, d_I = q_idx.shape
+    n_k = k_idx.shape[1]
+    wh, wp = _weights(w, H_I)
+    cfg = SelectCfg(n_sink, n_window, k_dyn)
+    K_tot = n_sink + n_window + k_dyn
+    need = ctypes.c_size_t(0)
+    args = (_ptr(q_idx), _ptr(k_idx), _ptr(k_blk), wp, B, n_k, H_I, d_I, blk, n_blk_recall, cfg)
+    _check("lsa_hier_select", lib.lsa_hier_select(*args, None, None, None, 0, ctypes.byref(need), None))
+    ws = _workspace(need.value, q_idx.device)
+    idx = torch.empty((B, K_tot), dtype=torch.int32, device=q_idx.device)
+    n_sel = torch.empty((B,), dtype=torch.int32, device=q_idx.device)
+    _check("lsa_hier_select", lib.lsa_hier_select(*args, _ptr(idx), _ptr(n_sel), _ptr(ws), ws.numel(),
+                                                  None, _stream()))
+    return idx, n_sel
+
+
+def lsa_sparse_attn_prefill(q, k, v, idx, n_sel, scale=None, want_lse=False, out=None):
+    """q [B, L, H, D] bf16, k/v [B, n_k, D] bf16, idx [B, L, K_tot] int32, n_sel [B, L].
+    Returns o [B, L, H, D] bf16 (and lse [B, L, H] fp32 if want_lse)."""
+    lib = load()
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _dev(t, torch.bfloat16, n)
+    _dev(idx, torch.int32, "idx")
+    _dev(n_sel, torch.int32, "n_sel")
+    B, L, H, D = q.shape
+    n_k = k.shape[1]
+    K_tot = idx.shape[-1]
+    if idx.shape != (B, L, K_tot) or n_sel.shape != (B, L) or v.shape != k.shape:
+        raise ValueError("shape mismatch")
+    scale = D ** -0.5 if scale is None else float(scale)
+    o = torch.empty_like(q) if out is None else out
+    lse = torch.empty((B, L, H), dtype=torch.float32, device=q.device) if want_lse else None
+    _check("lsa_sparse_attn_prefill", lib.lsa_sparse_attn_prefill(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(idx), _ptr(n_sel), B, L, n_k, H, D, K_tot, scale,
+        _ptr(o), _ptr(lse), _stream()))
+    return (o, lse) if want_lse else o
+
+
+def lsa_sparse_attn_decode(q, k_cache, v_cache, idx, n_sel, n_split=8, scale=None, want_lse=False, ws=None):
+    """q [B, n_q, H, D] bf16; caches [B, n_k, D]; idx [B, n_idx, K_tot] (n_idx 1 or n_q).
+    Returns o [B, n_q, H, D] bf16 (and lse [B, n_q, H] if want_lse)."""
+    lib = load()
+    for t, n in ((q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache")):
+        _dev(t, torch.bfloat16, n)
+    _dev(idx, torch.int32, "idx")
+    _dev(n_sel, torch.int32, "n_sel")
+    B, n_q, H, D = q.shape
+    n_k = k_cache.shape[1]
+    n_idx, K_tot = idx.shape[1], idx.shape[2]
+    if idx.shape[0] != B or n_sel.shape != (B, n_idx):
+        raise ValueError("shape mismatch")
+    scale = D ** -0.5 if scale is None else float(scale)
+    need = ctypes.c_size_t(0)
+    args = (_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(idx), _ptr(n_sel), n_idx, B, n_q, n_k, H, D, K_tot,
+            n_split, scale)
+    _check("lsa_sparse_attn_decode", lib.lsa_sparse_attn_decode(*args, None, None, None, 0, ctypes.byref(need),
+                                                                None))
+    if ws is None or ws.numel() < need.value:
+        ws = _workspace(need.value, q.device)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, n_q, H), dtype=torch.float32, device=q.device) if want_lse else None
+    _check("lsa_sparse_attn_decode", lib.lsa_sparse_attn_decode(*args, _ptr(o), _ptr(lse), _ptr(ws), ws.numel(),
+                                                                None, _stream()))
+    return (o, lse) if want_lse else o

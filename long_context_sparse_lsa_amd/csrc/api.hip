@@ -1,0 +1,429 @@
+// C ABI of the LSA hot path: argument checks, workspace sizing, launches.
+//
+// Every check that the host can make runs before the first launch, so an
+// argument error never leaves half of the work enqueued. The library keeps no
+// state and allocates nothing: workspace comes from the caller.
+#include <math.h>
+#include <stdint.h>
+
+#include <algorithm>
+
+#include "lsa.h"
+#include "lsa_internal.h"
+
+using namespace lsa;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+bool al16(const void* p) { return p != nullptr && ((uintptr_t)p & 15u) == 0; }
+bool al4(const void* p) { return p != nullptr && ((uintptr_t)p & 3u) == 0; }
+bool hi_ok(int h) { return h == 4 || h == 8 || h == 16 || h == 32 || h == 64 || h == 128; }
+bool di_ok(int d) { return d == 64 || d == 128; }
+bool heads_ok(int h) { return h == 16 || h == 32 || h == 64 || h == 128; }
+
+int32_t load_weights(const int32_t* w, int H_I, int d_I, WArgs& wa) {
+  if (w == nullptr) return LSA_INVALID_ARG;
+  int64_t s = 0;
+  for (int h = 0; h < 128; ++h) wa.w[h] = 0;
+  for (int h = 0; h < H_I; ++h) {
+    wa.w[h] = w[h];
+    s += w[h] < 0 ? -(int64_t)w[h] : (int64_t)w[h];
+  }
+  // every |q.k| <= d_I * 128 * 128, so |S| <= sum|w| * d_I * 2^14
+  if (s * d_I * 16384 >= ((int64_t)1 << 31)) return LSA_RANGE;
+  return LSA_OK;
+}
+
+int32_t cfg_ok(const lsa_select_cfg& c) {
+  if (c.n_sink < 0 || c.n_window < 0 || c.k_dyn < 0) return LSA_INVALID_ARG;
+  if ((int64_t)c.n_sink + c.n_window + c.k_dyn < 1) return LSA_INVALID_ARG;
+  if ((int64_t)c.n_sink + c.n_window + c.k_dyn > (1 << 20)) return LSA_UNSUPPORTED;
+  return LSA_OK;
+}
+
+int32_t hip_status(hipError_t e) { return e == hipSuccess ? LSA_OK : LSA_HIP; }
+
+int k_cap_of(int k) { return std::max(4, (k + 3) / 4 * 4); }
+
+int chunks_of(int64_t nc) { return (int)std::max<int64_t>(1, (nc + kSelChunk - 1) / kSelChunk); }
+
+// Rows per pass of the fused (score + select) prefill path: the score buffer
+// of one pass is at most kFusedScoreBytes.
+constexpr size_t kFusedScoreBytes = (size_t)512 << 20;
+int fused_rows(int n_q, int n_k) {
+  int64_t r = (int64_t)(kFusedScoreBytes / sizeof(int32_t)) / n_k;
+  r = std::max<int64_t>(4, r / 4 * 4);
+  return (int)std::min<int64_t>(r, n_q);
+}
+
+}  // namespace
+
+extern "C" const char* lsa_status_string(int32_t s) {
+  switch (s) {
+    case LSA_OK: return "LSA_OK";
+    case LSA_INVALID_ARG: return "LSA_INVALID_ARG: null, misaligned, non-positive or inconsistent argument";
+    case LSA_UNSUPPORTED: return "LSA_UNSUPPORTED: shape outside the supported set";
+    case LSA_WORKSPACE: return "LSA_WORKSPACE: workspace too small";
+    case LSA_RANGE: return "LSA_RANGE: sum|w| * d_I * 128^2 >= 2^31, scores would not be exact int32";
+    case LSA_HIP: return "LSA_HIP: a HIP launch failed";
+    default: return "LSA_UNKNOWN_STATUS";
+  }
+}
+
+extern "C" int32_t lsa_index_score(const int8_t* q_idx, const int8_t* k_idx, const int32_t* w,
+                                   int32_t B, int32_t n_q, int32_t n_k, int32_t H_I, int32_t d_I,
+                                   int32_t q_off, int32_t* scores, void* stream) {
+  if (!al16(q_idx) || !al16(k_idx) || !al4(scores)) return LSA_INVALID_ARG;
+  if (B <= 0 || n_q <= 0 || n_k <= 0 || q_off < 0) return LSA_INVALID_ARG;
+  if (!hi_ok(H_I) || !di_ok(d_I)) return LSA_UNSUPPORTED;
+  ScoreArgs a{};
+  int32_t s = load_weights(w, H_I, d_I, a.w);
+  if (s != LSA_OK) return s;
+  a.q = q_idx;
+  a.k = k_idx;
+  a.B = B;
+  a.n_q = n_q;
+  a.n_k = n_k;
+  a.H_I = H_I;
+  a.d_I = d_I;
+  a.q_bstride = (int64_t)n_q * H_I * d_I;
+  a.k_bstride = (int64_t)n_k * d_I;
+  a.s_bstride = (int64_t)n_q * n_k;
+  a.ld = n_k;
+  a.n_keys = n_k;
+  a.mask_off = q_off;
+  a.pos_lo = 0;
+  a.blocks = nullptr;
+  a.fill_masked = 1;
+  a.scores = scores;
+  return hip_status(launch_index_score(a, (hipStream_t)stream));
+}
+
+extern "C" int32_t lsa_select_topk(const int32_t* scores, const int8_t* q_idx, const int8_t* k_idx,
+                                   const int32_t* w, int32_t B, int32_t n_q, int32_t n_k,
+                                   int32_t H_I, int32_t d_I, int32_t q_off, lsa_select_cfg cfg,
+                                   int32_t* idx, int32_t* n_sel, void* ws, size_t ws_bytes,
+                                   size_t* ws_needed, void* stream) {
+  int32_t s = cfg_ok(cfg);
+  if (s != LSA_OK) return s;
+  if (B <= 0 || n_q <= 0 || n_k <= 0 || q_off < 0 || (int64_t)q_off + n_q > n_k) return LSA_INVALID_ARG;
+  const int K_tot = cfg.n_sink + cfg.n_window + cfg.k_dyn;
+  const int k_cap = k_cap_of(cfg.k_dyn);
+  const int64_t max_nc = (int64_t)q_off + n_q - cfg.n_window - cfg.n_sink;  // last row's candidates
+  WArgs wa{};
+  if (scores == nullptr) {
+    if (!al16(q_idx) || !al16(k_idx)) return LSA_INVALID_ARG;
+    if (!hi_ok(H_I) || !di_ok(d_I)) return LSA_UNSUPPORTED;
+    s = load_weights(w, H_I, d_I, wa);
+    if (s != LSA_OK) return s;
+  } else if (!al4(scores)) {
+    return LSA_INVALID_ARG;
+  }
+
+  // workspace
+  size_t need;
+  int R = 0;
+  int rows_pass = B * n_q;
+  if (scores != nullptr) {
+    const size_t per_row = select_ws_bytes(1, chunks_of(max_nc), k_cap);
+    if (per_row > 0)
+      rows_pass = (int)std::max<size_t>(1, std::min<size_t>(rows_pass, kFusedScoreBytes / per_row));
+    need = select_ws_bytes(rows_pass, chunks_of(max_nc), k_cap);
+  } else {
+    R = fused_rows(n_q, n_k);
+    need = align_up((size_t)R * n_k * sizeof(int32_t)) + select_ws_bytes(R, chunks_of(max_nc), k_cap);
+  }
+  need = align_up(std::max<size_t>(need, 1));
+  if (ws_needed) *ws_needed = need;
+  if (ws == nullptr) return ws_needed ? LSA_OK : LSA_WORKSPACE;  // size query
+  if (!al4(idx) || !al4(n_sel) || !al16(ws)) return LSA_INVALID_ARG;
+  if (ws_bytes < need) return LSA_WORKSPACE;
+  hipStream_t st = (hipStream_t)stream;
+
+  SelectArgs sa{};
+  sa.mode = SEL_FLAT;
+  sa.n_sink = cfg.n_sink;
+  sa.n_window = cfg.n_window;
+  sa.k_dyn = cfg.k_dyn;
+  sa.out_ld = K_tot;
+  sa.k_cap = k_cap;
+  if (scores != nullptr) {
+    // passes of rows_pass rows (b, i) in flattened order; a pass never mixes
+    // the row -> position mapping because position = q_off + (row % n_q)
+    for (int64_t r0 = 0; r0 < (int64_t)B * n_q; r0 += rows_pass) {
+      const int Rr = (int)std::min<int64_t>(rows_pass, (int64_t)B * n_q - r0);
+      sa.scores = scores + r0 * n_k;
+      sa.ld = n_k;
+      sa.n_rows = Rr;
+      sa.n_q = n_q;
+      sa.q_off = q_off;
+      sa.row0 = (int)(r0 % n_q);
+      sa.idx = idx + r0 * K_tot;
+      sa.n_sel = n_sel + r0;
+      sa.max_chunks = chunks_of(max_nc);
+      select_bind_ws(sa, ws, Rr);
+      s = hip_status(launch_select(sa, st));
+      if (s != LSA_OK) return s;
+    }
+    return LSA_OK;
+  }
+
+  // Fused path: score a pass of R rows (candidates only) into workspace, then select.
+  int32_t* sbuf = (int32_t*)ws;
+  void* sel_ws = (char*)ws + align_up((size_t)R * n_k * sizeof(int32_t));
+  for (int b = 0; b < B; ++b) {
+    for (int r0 = 0; r0 < n_q; r0 += R) {
+      const int Rr = std::min(R, n_q - r0);
+      const int t_last = q_off + r0 + Rr - 1;
+      const int64_t nc_last = (int64_t)t_last - cfg.n_window - cfg.n_sink + 1;
+      if (nc_last > 0 && t_last + 1 > K_tot) {
+        ScoreArgs a{};
+        a.w = wa;
+        a.q = q_idx + ((int64_t)b * n_q + r0) * H_I * d_I;
+        a.k = k_idx + (int64_t)b * n_k * d_I;
+        a.B = 1;
+        a.n_q = Rr;
+        a.n_k = n_k;
+        a.H_I = H_I;
+        a.d_I = d_I;
+        a.q_bstride = 0;
+        a.k_bstride = 0;
+        a.s_bstride = 0;
+        a.ld = n_k;
+        a.n_keys = std::min<int64_t>(n_k, (int64_t)t_last - cfg.n_window + 1);
+        a.mask_off = q_off + r0 - cfg.n_window;
+        a.pos_lo = cfg.n_sink;
+        a.blocks = nullptr;
+        a.fill_masked = 0;
+        a.scores = sbuf;
+        if (a.n_keys > 0) {
+          s = hip_status(launch_index_score(a, st));
+          if (s != LSA_OK) return s;
+        }
+      }
+      sa.scores = sbuf;
+      sa.ld = n_k;
+      sa.n_rows = Rr;
+      sa.n_q = Rr;
+      sa.q_off = q_off + r0;
+      sa.idx = idx + ((int64_t)b * n_q + r0) * K_tot;
+      sa.n_sel = n_sel + (int64_t)b * n_q + r0;
+      sa.max_chunks = chunks_of(nc_last);
+      select_bind_ws(sa, sel_ws, Rr);
+      s = hip_status(launch_select(sa, st));
+      if (s != LSA_OK) return s;
+    }
+  }
+  return LSA_OK;
+}
+
+extern "C" int32_t lsa_block_summary(const int8_t* k_idx, int32_t B, int32_t n_k, int32_t d_I,
+                                     int32_t blk, int8_t* k_blk, void* stream) {
+  if (!al16(k_idx) || !al16(k_blk)) return LSA_INVALID_ARG;
+  if (B <= 0 || n_k <= 0 || blk <= 0) return LSA_INVALID_ARG;
+  if (!di_ok(d_I) || blk > 1024) return LSA_UNSUPPORTED;
+  return hip_status(launch_block_summary(k_idx, B, n_k, d_I, blk, k_blk, (hipStream_t)stream));
+}
+
+extern "C" int32_t lsa_hier_select(const int8_t* q_idx, const int8_t* k_idx, const int8_t* k_blk,
+                                   const int32_t* w, int32_t B, int32_t n_k, int32_t H_I,
+                                   int32_t d_I, int32_t blk, int32_t n_blk_recall,
+                                   lsa_select_cfg cfg, int32_t* idx, int32_t* n_sel, void* ws,
+                                   size_t ws_bytes, size_t* ws_needed, void* stream) {
+  int32_t s = cfg_ok(cfg);
+  if (s != LSA_OK) return s;
+  if (B <= 0 || n_k <= 0 || blk <= 0 || n_blk_recall <= 0) return LSA_INVALID_ARG;
+  if (!hi_ok(H_I) || !di_ok(d_I) || blk % 32 != 0 || blk > 1024) return LSA_UNSUPPORTED;
+  if ((int64_t)n_blk_recall * blk > (1 << 30)) return LSA_UNSUPPORTED;
+  WArgs wa{};
+  const int K_tot = cfg.n_sink + cfg.n_window + cfg.k_dyn;
+  const int t = n_k - 1;
+  const bool trivial = t + 1 <= K_tot;
+  const int lo = cfg.n_sink, hi = t - cfg.n_window;
+  const int nblocks = (n_k + blk - 1) / blk;
+  const int b_lo = trivial ? 0 : lo / blk, b_hi = trivial ? 0 : hi / blk;
+  const int n_elig = trivial ? 0 : b_hi - b_lo + 1;
+  const int n_virt = n_blk_recall * blk;
+  const int kc_coarse = k_cap_of(n_blk_recall), kc_fine = k_cap_of(cfg.k_dyn);
+
+  const size_t sz_coarse = align_up((size_t)B * nblocks * sizeof(int32_t));
+  const size_t sz_blocks = align_up((size_t)B * n_blk_recall * sizeof(int32_t));
+  const size_t sz_nblk = align_up((size_t)B * sizeof(int32_t));
+  const size_t sz_fine = align_up((size_t)B * n_virt * sizeof(int32_t));
+  const size_t sz_sel = align_up(std::max(select_ws_bytes(B, chunks_of(n_elig), kc_coarse),
+                                          select_ws_bytes(B, chunks_of(n_virt), kc_fine)));
+  const size_t need = trivial ? kAlign : sz_coarse + sz_blocks + sz_nblk + sz_fine + sz_sel;
+  if (ws_needed) *ws_needed = need;
+  if (ws == nullptr) return ws_needed ? LSA_OK : LSA_WORKSPACE;  // size query
+  if (!al16(q_idx) || !al16(k_idx) || !al16(k_blk) || !al4(idx) || !al4(n_sel) || !al16(ws))
+    return LSA_INVALID_ARG;
+  s = load_weights(w, H_I, d_I, wa);
+  if (s != LSA_OK) return s;
+  if (ws_bytes < need) return LSA_WORKSPACE;
+  hipStream_t st = (hipStream_t)stream;
+
+  if (trivial) {
+    SelectArgs sa{};
+    sa.mode = SEL_FLAT;
+    sa.n_rows = B;
+    sa.n_q = 1;
+    sa.q_off = t;
+    sa.n_sink = cfg.n_sink;
+    sa.n_window = cfg.n_window;
+    sa.k_dyn = cfg.k_dyn;
+    sa.idx = idx;
+    sa.n_sel = n_sel;
+    sa.out_ld = K_tot;
+    sa.max_chunks = 1;
+    sa.k_cap = kc_fine;
+    return hip_status(launch_select(sa, st));
+  }
+
+  char* p = (char*)ws;
+  int32_t* coarse = (int32_t*)p;
+  p += sz_coarse;
+  int32_t* blocks = (int32_t*)p;
+  p += sz_blocks;
+  int32_t* nblk = (int32_t*)p;
+  p += sz_nblk;
+  int32_t* fine = (int32_t*)p;
+  p += sz_fine;
+  void* sel_ws = p;
+
+  // coarse scores of the eligible blocks
+  ScoreArgs a{};
+  a.w = wa;
+  a.q = q_idx;
+  a.k = k_blk;
+  a.B = B;
+  a.n_q = 1;
+  a.n_k = nblocks;
+  a.H_I = H_I;
+  a.d_I = d_I;
+  a.q_bstride = (int64_t)H_I * d_I;
+  a.k_bstride = (int64_t)nblocks * d_I;
+  a.s_bstride = nblocks;
+  a.ld = nblocks;
+  a.n_keys = b_hi + 1;
+  a.mask_off = b_hi;
+  a.pos_lo = b_lo;
+  a.blocks = nullptr;
+  a.fill_masked = 0;
+  a.scores = coarse;
+  s = hip_status(launch_index_score(a, st));
+  if (s != LSA_OK) return s;
+
+  // recall the best blocks (ascending ids, -1 padded)
+  SelectArgs sc{};
+  sc.mode = SEL_RAW;
+  sc.scores = coarse;
+  sc.ld = nblocks;
+  sc.n_rows = B;
+  sc.raw_lo = b_lo;
+  sc.raw_hi = b_hi;
+  sc.raw_k = n_blk_recall;
+  sc.idx = blocks;
+  sc.n_sel = nblk;
+  sc.out_ld = n_blk_recall;
+  sc.max_chunks = chunks_of(n_elig);
+  sc.k_cap = kc_coarse;
+  select_bind_ws(sc, sel_ws, B);
+  s = hip_status(launch_select(sc, st));
+  if (s != LSA_OK) return s;
+
+  // fine scores of the candidate tokens inside the recalled blocks
+  ScoreArgs f = a;
+  f.k = k_idx;
+  f.n_k = n_k;
+  f.k_bstride = (int64_t)n_k * d_I;
+  f.s_bstride = n_virt;
+  f.ld = n_virt;
+  f.n_keys = n_virt;
+  f.mask_off = hi;
+  f.pos_lo = lo;
+  f.blocks = blocks;
+  f.blk = blk;
+  f.nbr = n_blk_recall;
+  f.fill_masked = 1;
+  f.scores = fine;
+  s = hip_status(launch_index_score(f, st));
+  if (s != LSA_OK) return s;
+
+  SelectArgs sf{};
+  sf.mode = SEL_INDIRECT;
+  sf.scores = fine;
+  sf.ld = n_virt;
+  sf.n_rows = B;
+  sf.n_sink = cfg.n_sink;
+  sf.n_window = cfg.n_window;
+  sf.k_dyn = cfg.k_dyn;
+  sf.blocks = blocks;
+  sf.blk = blk;
+  sf.nbr = n_blk_recall;
+  sf.n_virt = n_virt;
+  sf.t_fixed = t;
+  sf.idx = idx;
+  sf.n_sel = n_sel;
+  sf.out_ld = K_tot;
+  sf.max_chunks = chunks_of(n_virt);
+  sf.k_cap = kc_fine;
+  select_bind_ws(sf, sel_ws, B);
+  return hip_status(launch_select(sf, st));
+}
+
+extern "C" int32_t lsa_sparse_attn_prefill(const lsa_bf16* q, const lsa_bf16* k, const lsa_bf16* v,
+                                           const int32_t* idx, const int32_t* n_sel, int32_t B,
+                                           int32_t L, int32_t n_k, int32_t H, int32_t D,
+                                           int32_t K_tot, float scale, lsa_bf16* o, float* lse,
+                                           void* stream) {
+  if (!al16(q) || !al16(k) || !al16(v) || !al4(idx) || !al4(n_sel) || !al16(o)) return LSA_INVALID_ARG;
+  if (lse != nullptr && !al4(lse)) return LSA_INVALID_ARG;
+  if (B <= 0 || L <= 0 || n_k <= 0 || K_tot <= 0 || !(scale > 0.f) || !isfinite(scale)) return LSA_INVALID_ARG;
+  if (D != 128 || !heads_ok(H)) return LSA_UNSUPPORTED;
+  PrefillArgs a{q, k, v, idx, n_sel, B, L, n_k, H, K_tot, scale * 1.4426950408889634f, o, lse};
+  return hip_status(launch_attn_prefill(a, (hipStream_t)stream));
+}
+
+extern "C" int32_t lsa_sparse_attn_decode(const lsa_bf16* q, const lsa_bf16* k_cache,
+                                          const lsa_bf16* v_cache, const int32_t* idx,
+                                          const int32_t* n_sel, int32_t n_idx, int32_t B,
+                                          int32_t n_q, int32_t n_k, int32_t H, int32_t D,
+                                          int32_t K_tot, int32_t n_split, float scale, lsa_bf16* o,
+                                          float* lse, void* ws, size_t ws_bytes, size_t* ws_needed,
+                                          void* stream) {
+  if (B <= 0 || n_q <= 0 || n_k <= 0 || K_tot <= 0 || !(scale > 0.f) || !isfinite(scale)) return LSA_INVALID_ARG;
+  if (n_idx != 1 && n_idx != n_q) return LSA_INVALID_ARG;
+  if (D != 128 || !heads_ok(H) || n_split < 1 || n_split > 64) return LSA_UNSUPPORTED;
+  const size_t need = align_up(decode_ws_bytes(B, n_q, H, n_split));
+  if (ws_needed) *ws_needed = need;
+  if (ws == nullptr) return ws_needed ? LSA_OK : LSA_WORKSPACE;  // size query
+  if (!al16(q) || !al16(k_cache) || !al16(v_cache) || !al4(idx) || !al4(n_sel) || !al16(o) ||
+      !al16(ws))
+    return LSA_INVALID_ARG;
+  if (lse != nullptr && !al4(lse)) return LSA_INVALID_ARG;
+  if (ws_bytes < need) return LSA_WORKSPACE;
+  const size_t rows = (size_t)B * n_split * n_q * H;
+  DecodeArgs a{};
+  a.q = q;
+  a.k = k_cache;
+  a.v = v_cache;
+  a.idx = idx;
+  a.n_sel = n_sel;
+  a.n_idx = n_idx;
+  a.B = B;
+  a.n_q = n_q;
+  a.n_k = n_k;
+  a.H = H;
+  a.K_tot = K_tot;
+  a.n_split = n_split;
+  a.sl2 = scale * 1.4426950408889634f;
+  a.o = o;
+  a.lse = lse;
+  a.ws_m = (float*)ws;
+  a.ws_l = a.ws_m + rows;
+  a.ws_o = (float*)((char*)ws + align_up(rows * 2 * sizeof(float)));
+  return hip_status(launch_attn_decode(a, (hipStream_t)stream));
+}

@@ -1,0 +1,329 @@
+// Sparse attention over gathered keys on bf16 MFMA (gfx950).
+//
+// Each query row attends only to its selected keys (the top-k keys plus the
+// sink tokens: "架构拆解 ① LSA" section of the 1.6T training write-up; the
+// LongCat-2.0 release article, section "LongCat 稀疏注意力", for SI / CLI).
+// All query heads share one KV head, so a wave computes every head of a query
+// (or of a group of decode rows) against one gathered key tile at a time.
+//
+// Wave tile (32 keys x 32*NB heads), transposed products so that no
+// register shuffles are needed between the two GEMMs:
+//   S^T = K * Q^T  : A = gathered K rows (lane = key), B = Q^T (lane = head)
+//   O^T += V^T * P^T: A = V^T from LDS (lane = dim),   B = P^T (lane = head)
+// The S^T accumulator gives lane l the head l%32 and 16 keys; those are
+// exactly the keys the P^T operand of the second product needs in that lane,
+// so softmax probabilities go from accumulator to operand in place. The V
+// tile is transposed through a per-wave LDS buffer (4x4 register transposes,
+// 8-byte LDS writes and reads). Online softmax runs in fp32 in base 2.
+//
+// Decode splits the selected list into n_split contiguous parts (the one-GPU
+// form of the KV-cache parallel decode of the "③ KVP 解码切分示意" section) and
+// merges the (max, sum, output) partials with a fixed-shape binary tree.
+#include <math.h>
+
+#include "lsa_device.h"
+#include "lsa_internal.h"
+
+namespace lsa {
+
+constexpr int kD = 128;
+constexpr int kVStride = 72;                 // bytes per V^T row in LDS (32 keys + pad)
+constexpr int kVLds = kD * kVStride;         // bytes per wave
+
+template <int NB>
+struct AttnState {
+  v16f o[4][NB];
+  float m[NB], l[NB];
+};
+
+__device__ __forceinline__ v8bf load_v8bf(const uint16_t* p) { return *(const v8bf*)p; }
+
+template <int NB>
+__device__ __forceinline__ void attn_init(AttnState<NB>& st) {
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    st.m[nb] = -INFINITY;
+    st.l[nb] = 0.f;
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) st.o[mb][nb] = v16f{};
+  }
+}
+
+// Load the B operand Q^T for heads [h0, h0 + 32*NB) of one query row
+// (row base pointer qrow -> [H][128]); heads >= H are zero.
+template <int NB>
+__device__ __forceinline__ void load_q(const uint16_t* qrow, int h0, int H, v8bf (&Q)[NB][8]) {
+  const int l = lane_id(), g = l >> 5, c = l & 31;
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    const int h = h0 + 32 * nb + c;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      if (h < H) Q[nb][j] = load_v8bf(qrow + (int64_t)h * kD + g * 64 + 8 * j);
+      else Q[nb][j] = v8bf{};
+    }
+  }
+}
+
+// Attend the wave's rows over keys ids[kb .. ke) of one sequence.
+template <int NB>
+__device__ void attn_keys(const v8bf (&Q)[NB][8], const uint16_t* K, const uint16_t* V,
+                          const int32_t* ids, int kb, int ke, int n_k, float sl2,
+                          AttnState<NB>& st, char* vlds) {
+  const int l = lane_id(), g = l >> 5, c = l & 31;
+  const int kg = l >> 3, dc = l & 7;
+  for (int s0 = kb; s0 < ke; s0 += 32) {
+    const int kk = s0 + c;
+    const int pos = kk < ke ? ids[kk] : -1;
+    const bool valid = (unsigned)pos < (unsigned)n_k;
+    const uint32_t vmask = (uint32_t)__ballot(valid);
+
+    // ---- S^T = K * Q^T
+    v8bf Ka[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      Ka[j] = valid ? load_v8bf(K + (int64_t)pos * kD + g * 64 + 8 * j) : v8bf{};
+
+    // V rows of keys 4kg..4kg+3, dims 16dc..16dc+15 (issued early)
+    v4u Vr[4][2];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int pe = __shfl(pos, 4 * kg + e, 64);
+      const bool ve = (unsigned)pe < (unsigned)n_k;
+      const v4u* src = (const v4u*)(V + (int64_t)pe * kD + 16 * dc);
+      Vr[e][0] = ve ? src[0] : v4u{0, 0, 0, 0};
+      Vr[e][1] = ve ? src[1] : v4u{0, 0, 0, 0};
+    }
+
+    v16f S[NB];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      S[nb] = v16f{};
+#pragma unroll
+      for (int j = 0; j < 8; ++j) S[nb] = mfma_bf16_32x32x16(Ka[j], Q[nb][j], S[nb]);
+    }
+
+    // ---- V^T into LDS: dim-major rows of 32 keys
+#pragma unroll
+    for (int x = 0; x < 8; ++x) {
+      uint32_t w[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) w[e] = Vr[e][x >> 2][x & 3];
+      const uint32_t lo01 = (w[0] & 0xffffu) | (w[1] << 16);
+      const uint32_t lo23 = (w[2] & 0xffffu) | (w[3] << 16);
+      const uint32_t hi01 = (w[0] >> 16) | (w[1] & 0xffff0000u);
+      const uint32_t hi23 = (w[2] >> 16) | (w[3] & 0xffff0000u);
+      const int d0 = 16 * dc + 2 * x;
+      *(v2u*)(vlds + d0 * kVStride + kg * 8) = v2u{lo01, lo23};
+      *(v2u*)(vlds + (d0 + 1) * kVStride + kg * 8) = v2u{hi01, hi23};
+    }
+
+    // ---- online softmax (base 2), per head = per lane
+    v8bf P[NB][2];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      float z[16];
+      float mx = -INFINITY;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int kt = 8 * (i >> 2) + 4 * g + (i & 3);
+        z[i] = ((vmask >> kt) & 1u) ? S[nb][i] * sl2 : -INFINITY;
+        mx = fmaxf(mx, z[i]);
+      }
+      mx = fmaxf(mx, shfl_xor_f(mx, 32));
+      const float mnew = fmaxf(st.m[nb], mx);
+      const float mref = mnew == -INFINITY ? 0.f : mnew;
+      const float alpha = exp2f(st.m[nb] - mref);
+      float rs = 0.f;
+      float p[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        p[i] = exp2f(z[i] - mref);
+        rs += p[i];
+      }
+      rs += shfl_xor_f(rs, 32);
+      st.l[nb] = st.l[nb] * alpha + rs;
+      st.m[nb] = mnew;
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb) st.o[mb][nb] *= alpha;
+#pragma unroll
+      for (int js = 0; js < 2; ++js) {
+        v4u u;
+#pragma unroll
+        for (int w2 = 0; w2 < 4; ++w2) u[w2] = pack_bf16x2(p[8 * js + 2 * w2], p[8 * js + 2 * w2 + 1]);
+        P[nb][js] = __builtin_bit_cast(v8bf, u);
+      }
+    }
+
+    // ---- O^T += V^T * P^T
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) {
+      const char* rowp = vlds + (32 * mb + c) * kVStride;
+#pragma unroll
+      for (int js = 0; js < 2; ++js) {
+        const v2u a0 = *(const v2u*)(rowp + (16 * js + 4 * g) * 2);
+        const v2u a1 = *(const v2u*)(rowp + (16 * js + 4 * g + 8) * 2);
+        const v4u au = v4u{a0[0], a0[1], a1[0], a1[1]};
+        const v8bf Va = __builtin_bit_cast(v8bf, au);
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) st.o[mb][nb] = mfma_bf16_32x32x16(Va, P[nb][js], st.o[mb][nb]);
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------------ prefill
+template <int NB>
+__global__ __launch_bounds__(256) void attn_prefill_kernel(PrefillArgs a) {
+  __shared__ __attribute__((aligned(16))) char vlds_all[4 * kVLds];
+  const int wv = wave_id();
+  const int HB = (a.H + 32 * NB - 1) / (32 * NB);
+  const int64_t gi = (int64_t)blockIdx.x * 4 + wv;
+  if (gi >= (int64_t)a.B * a.L * HB) return;
+  const int64_t gq = gi / HB;
+  const int hb = (int)(gi % HB);
+  const int b = (int)(gq / a.L);
+  const int l = lane_id(), g = l >> 5, c = l & 31;
+  v8bf Q[NB][8];
+  load_q<NB>(a.q + gq * a.H * kD, hb * 32 * NB, a.H, Q);
+  AttnState<NB> st;
+  attn_init(st);
+  const int n = min(max(a.n_sel[gq], 0), a.K_tot);
+  const uint16_t* K = a.k + (int64_t)b * a.n_k * kD;
+  const uint16_t* V = a.v + (int64_t)b * a.n_k * kD;
+  attn_keys<NB>(Q, K, V, a.idx + gq * a.K_tot, 0, n, a.n_k, a.sl2, st, vlds_all + wv * kVLds);
+
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    const int h = hb * 32 * NB + 32 * nb + c;
+    if (h >= a.H) continue;
+    const float inv = st.l[nb] > 0.f ? 1.f / st.l[nb] : 0.f;
+    uint16_t* orow = a.o + (gq * a.H + h) * kD;
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4) {
+        const v16f& O = st.o[mb][nb];
+        const uint32_t w0 = pack_bf16x2(O[4 * i4] * inv, O[4 * i4 + 1] * inv);
+        const uint32_t w1 = pack_bf16x2(O[4 * i4 + 2] * inv, O[4 * i4 + 3] * inv);
+        *(v2u*)(orow + 32 * mb + 8 * i4 + 4 * g) = v2u{w0, w1};
+      }
+    if (a.lse && g == 0)
+      a.lse[gq * a.H + h] = st.l[nb] > 0.f ? (st.m[nb] + log2f(st.l[nb])) * 0.69314718055994531f : -INFINITY;
+  }
+}
+
+hipError_t launch_attn_prefill(const PrefillArgs& a, hipStream_t st) {
+  const int NB = a.H <= 32 ? 1 : 2;
+  const int HB = (a.H + 32 * NB - 1) / (32 * NB);
+  const int64_t groups = (int64_t)a.B * a.L * HB;
+  dim3 grid((unsigned)((groups + 3) / 4));
+  if (NB == 1) hipLaunchKernelGGL(attn_prefill_kernel<1>, grid, dim3(256), 0, st, a);
+  else hipLaunchKernelGGL(attn_prefill_kernel<2>, grid, dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------------ decode
+// Partials: ws_m / ws_l [B, n_split, R], ws_o [B, n_split, R, 128] with
+// R = n_q * H; o is unnormalised, m in base-2 units.
+template <int NB>
+__global__ __launch_bounds__(256) void attn_decode_partial(DecodeArgs a) {
+  __shared__ __attribute__((aligned(16))) char vlds_all[4 * kVLds];
+  const int wv = wave_id();
+  const int HB = (a.H + 32 * NB - 1) / (32 * NB);
+  const int gi = blockIdx.x * 4 + wv;
+  if (gi >= a.n_q * HB) return;
+  const int qr = gi / HB, hb = gi % HB;
+  const int split = blockIdx.y, b = blockIdx.z;
+  const int l = lane_id(), g = l >> 5, c = l & 31;
+  const int R = a.n_q * a.H;
+  v8bf Q[NB][8];
+  load_q<NB>(a.q + ((int64_t)b * a.n_q + qr) * a.H * kD, hb * 32 * NB, a.H, Q);
+  AttnState<NB> st;
+  attn_init(st);
+  const int irow = a.n_idx == 1 ? 0 : qr;
+  const int64_t ibase = (int64_t)b * a.n_idx + irow;
+  const int n = min(max(a.n_sel[ibase], 0), a.K_tot);
+  const int cs = (n + a.n_split - 1) / a.n_split;
+  const int kb = min(n, split * cs), ke = min(n, (split + 1) * cs);
+  const uint16_t* K = a.k + (int64_t)b * a.n_k * kD;
+  const uint16_t* V = a.v + (int64_t)b * a.n_k * kD;
+  attn_keys<NB>(Q, K, V, a.idx + ibase * a.K_tot, kb, ke, a.n_k, a.sl2, st, vlds_all + wv * kVLds);
+
+  const int64_t pbase = ((int64_t)b * a.n_split + split) * R;
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    const int h = hb * 32 * NB + 32 * nb + c;
+    if (h >= a.H) continue;
+    const int64_t row = pbase + (int64_t)qr * a.H + h;
+    if (g == 0) {
+      a.ws_m[row] = st.m[nb];
+      a.ws_l[row] = st.l[nb];
+    }
+    float* orow = a.ws_o + row * kD;
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4) {
+        const v16f& O = st.o[mb][nb];
+        *(v4f*)(orow + 32 * mb + 8 * i4 + 4 * g) =
+            v4f{O[4 * i4], O[4 * i4 + 1], O[4 * i4 + 2], O[4 * i4 + 3]};
+      }
+  }
+}
+
+constexpr int kMaxSplit = 64;
+
+// One block per (sequence, row); thread = output dim. Weighted sums over the
+// splits use a fixed 64-leaf binary tree (absent splits are exact zeros).
+__global__ __launch_bounds__(128) void attn_decode_merge(DecodeArgs a) {
+  const int R = a.n_q * a.H;
+  const int64_t brow = blockIdx.x;
+  const int b = (int)(brow / R), r = (int)(brow % R);
+  const int d = threadIdx.x;
+  float M = -INFINITY;
+  for (int j = 0; j < a.n_split; ++j) M = fmaxf(M, a.ws_m[((int64_t)b * a.n_split + j) * R + r]);
+  float lv[kMaxSplit], ov[kMaxSplit];
+#pragma unroll
+  for (int j = 0; j < kMaxSplit; ++j) {
+    lv[j] = 0.f;
+    ov[j] = 0.f;
+    if (j < a.n_split && M != -INFINITY) {
+      const int64_t row = ((int64_t)b * a.n_split + j) * R + r;
+      const float wj = exp2f(a.ws_m[row] - M);
+      lv[j] = wj * a.ws_l[row];
+      ov[j] = wj * a.ws_o[row * kD + d];
+    }
+  }
+#pragma unroll
+  for (int s = 1; s < kMaxSplit; s <<= 1)
+#pragma unroll
+    for (int j = 0; j + s < kMaxSplit; j += 2 * s) {
+      lv[j] += lv[j + s];
+      ov[j] += ov[j + s];
+    }
+  const float Lam = lv[0];
+  const float out = Lam > 0.f ? ov[0] / Lam : 0.f;
+  a.o[brow * kD + d] = (uint16_t)f32_to_bf16_bits(out);
+  if (a.lse && d == 0) a.lse[brow] = Lam > 0.f ? (M + log2f(Lam)) * 0.69314718055994531f : -INFINITY;
+}
+
+size_t decode_ws_bytes(int B, int n_q, int H, int n_split) {
+  const size_t rows = (size_t)B * n_split * n_q * H;
+  return rows * sizeof(float) * (2 + kD) + 256;
+}
+
+hipError_t launch_attn_decode(const DecodeArgs& a, hipStream_t st) {
+  const int NB = a.H <= 32 ? 1 : 2;
+  const int HB = (a.H + 32 * NB - 1) / (32 * NB);
+  const int groups = a.n_q * HB;
+  dim3 grid((groups + 3) / 4, a.n_split, a.B);
+  if (NB == 1) hipLaunchKernelGGL(attn_decode_partial<1>, grid, dim3(256), 0, st, a);
+  else hipLaunchKernelGGL(attn_decode_partial<2>, grid, dim3(256), 0, st, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(attn_decode_merge, dim3((unsigned)((int64_t)a.B * a.n_q * a.H)), dim3(kD), 0, st, a);
+  return hipGetLastError();
+}
+
+}  // namespace lsa

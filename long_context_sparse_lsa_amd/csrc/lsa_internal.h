@@ -1,0 +1,99 @@
+// Host-side launch interfaces shared between the LSA translation units.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "lsa.h"
+
+namespace lsa {
+
+// Per-head indexer weights travel in the kernel arguments.
+struct WArgs {
+  int32_t w[128];
+};
+
+// Indexer score launch. Row i of sequence b scores the virtual keys
+// [0, n_keys); virtual key v sits at position v, or, when `blocks` is given, at
+// blocks[b * nbr + v / blk] * blk + v % blk (a negative block id is invalid).
+// A key at position p is visible to row i iff pos_lo <= p <= mask_off + i.
+// Visible scores go to scores[b * s_bstride + i * ld + v]; invisible ones get
+// INT32_MIN when fill_masked, else are left untouched.
+struct ScoreArgs {
+  const int8_t* q;
+  const int8_t* k;
+  WArgs w;
+  int B, n_q, n_k, H_I, d_I;
+  int64_t q_bstride, k_bstride, s_bstride, ld;
+  int n_keys;
+  int mask_off, pos_lo;
+  const int32_t* blocks;
+  int blk, nbr;
+  int fill_masked;
+  int32_t* scores;
+};
+hipError_t launch_index_score(const ScoreArgs& a, hipStream_t st);
+
+// Selection launch.
+enum SelMode { SEL_FLAT = 0, SEL_RAW = 1, SEL_INDIRECT = 2 };
+struct SelectArgs {
+  int mode;
+  const int32_t* scores;  // row r's scores at scores + r * ld, indexed by virtual key
+  int64_t ld;
+  int n_rows;
+  // FLAT: row r is query r % n_q at t = q_off + r % n_q; candidates are the
+  // positions [n_sink, t - n_window]; virtual key == position.
+  // (row0 offsets the row count when a launch covers a slice of the rows.)
+  int n_q, q_off, row0, n_sink, n_window, k_dyn;
+  // RAW: candidates [raw_lo, raw_hi] (virtual == position), keep raw_k.
+  int raw_lo, raw_hi, raw_k;
+  // INDIRECT: candidates are virtual keys [0, n_virt) of row r, at positions
+  // blocks[r * nbr + v / blk] * blk + v % blk, valid iff score != INT32_MIN;
+  // the query sits at t_fixed; keep k_dyn; sinks and window as in FLAT.
+  const int32_t* blocks;
+  int blk, nbr, n_virt, t_fixed;
+  // outputs: FLAT / INDIRECT write the assembled list (sinks, top-k, window),
+  // RAW writes only the kept positions; both ascending, -1 padded to out_ld.
+  int32_t* idx;
+  int32_t* n_sel;
+  int out_ld;
+  // multi-chunk rows: per-chunk candidates in workspace
+  int32_t* ws_score;
+  int32_t* ws_pos;
+  int32_t* ws_cnt;
+  int max_chunks;
+  int k_cap;
+};
+constexpr int kSelChunk = 8192;  // candidates per first-stage workgroup
+size_t select_ws_bytes(int n_rows, int max_chunks, int k_cap);
+void select_bind_ws(SelectArgs& a, void* ws, int n_rows);
+hipError_t launch_select(const SelectArgs& a, hipStream_t st);
+
+// Sparse attention launches (bf16 bit patterns as uint16_t; sl2 is
+// scale * log2(e): softmax runs in base 2).
+struct PrefillArgs {
+  const uint16_t *q, *k, *v;
+  const int32_t *idx, *n_sel;
+  int B, L, n_k, H, K_tot;
+  float sl2;
+  uint16_t* o;
+  float* lse;
+};
+hipError_t launch_attn_prefill(const PrefillArgs& a, hipStream_t st);
+
+struct DecodeArgs {
+  const uint16_t *q, *k, *v;
+  const int32_t *idx, *n_sel;
+  int n_idx, B, n_q, n_k, H, K_tot, n_split;
+  float sl2;
+  uint16_t* o;
+  float* lse;
+  float *ws_m, *ws_l, *ws_o;
+};
+size_t decode_ws_bytes(int B, int n_q, int H, int n_split);
+hipError_t launch_attn_decode(const DecodeArgs& a, hipStream_t st);
+
+// HI block summary launch.
+hipError_t launch_block_summary(const int8_t* k, int B, int n_k, int d_I, int blk, int8_t* kb,
+                                hipStream_t st);
+
+}  // namespace lsa

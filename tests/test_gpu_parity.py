@@ -1,0 +1,306 @@
+"""GPU parity of every C-ABI entry point against the CPU oracle.
+
+Shapes span several MFMA / selection tiles with ragged tails. Indices must
+match bit-exactly; attention outputs must be within max-abs 1e-2 and
+mean-abs 1e-3 of the float64 oracle. Every call also runs twice and must be
+bit-identical (determinism).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from long_context_sparse_lsa_amd import _lib as L
+from long_context_sparse_lsa_amd import configs, synth
+from tests._util import assert_attn_close, f64, need_gpu, np_, say
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    need_gpu()
+    L.load()
+
+
+def i8(shape, lo, hi, *seed):
+    return synth.int8_uniform(shape, lo, hi, synth.seed_of("parity", *seed), DEV)
+
+
+def bf(shape, *seed):
+    return synth.bf16_normal(shape, synth.seed_of("parity", *seed), DEV)
+
+
+def weights(H_I, d_I, seed, lo=None, hi=None):
+    wmax = max(1, ((1 << 31) - 1) // (d_I * 16384 * H_I))
+    lo = -wmax if lo is None else lo
+    hi = wmax if hi is None else hi
+    return synth.int_weights(H_I, lo, hi, synth.seed_of("parity-w", seed))
+
+
+def check_idx(idx_row, n_sel, ref, K_tot, what):
+    got = np.asarray(idx_row)
+    assert n_sel == len(ref), f"{what}: n_sel {n_sel} != {len(ref)}"
+    assert np.array_equal(got[:n_sel], ref), f"{what}: idx differs"
+    assert np.all(got[n_sel:K_tot] == -1), f"{what}: padding"
+
+
+# ------------------------------------------------------------------ indexer
+@pytest.mark.parametrize("H_I,d_I", [(4, 64), (8, 128), (16, 64), (32, 128), (64, 128), (64, 64), (128, 128)])
+def test_index_score_exact(H_I, d_I):
+    B, n_q, n_k = 2, 37, 333
+    say(f"index_score H_I={H_I} d_I={d_I}")
+    q = i8((B, n_q, H_I, d_I), -128, 127, "q", H_I, d_I)
+    k = i8((B, n_k, d_I), -128, 127, "k", H_I, d_I)
+    w = weights(H_I, d_I, (H_I, d_I))
+    S = L.lsa_index_score(q, k, w, q_off=n_k - n_q)
+    S2 = L.lsa_index_score(q, k, w, q_off=n_k - n_q)
+    torch.cuda.synchronize()
+    assert torch.equal(S, S2)
+    for b in range(B):
+        ref = O.index_scores(np_(q[b]), np_(k[b]), w, q_off=n_k - n_q)
+        assert np.array_equal(np_(S[b]), ref)
+
+
+def test_index_score_decode_and_full_causal():
+    say("index_score decode / causal")
+    B, H_I, d_I, n_k = 3, 64, 128, 5000
+    q = i8((B, 1, H_I, d_I), -16, 15, "qd")
+    k = i8((B, n_k, d_I), -16, 15, "kd")
+    w = synth.int_weights(H_I, 1, 8, 5)
+    S = L.lsa_index_score(q, k, w, q_off=n_k - 1)
+    for b in range(B):
+        assert np.array_equal(np_(S[b]), O.index_scores(np_(q[b]), np_(k[b]), w, q_off=n_k - 1))
+    # full causal square from position 0 (upper triangle masked)
+    q = i8((1, 200, 8, 64), -128, 127, "qc")
+    k = i8((1, 200, 64), -128, 127, "kc")
+    w = weights(8, 64, "c")
+    S = L.lsa_index_score(q, k, w, q_off=0)
+    assert np.array_equal(np_(S[0]), O.index_scores(np_(q[0]), np_(k[0]), w, q_off=0))
+
+
+# ------------------------------------------------------------------ selection
+@pytest.mark.parametrize("cfg", [(4, 64, 300), (0, 0, 50), (4, 0, 1000), (1, 16, 0), (4, 512, 9000),
+                                 (4, 512, 1532)])
+def test_select_given_scores_ties_and_chunks(cfg):
+    n_sink, W, kd = cfg
+    say(f"select scores-given cfg={cfg}")
+    B, n_q, n_k = 2, 6, 20000  # rows of ~20k candidates: two-stage path
+    g = torch.Generator(device=DEV)
+    g.manual_seed(77)
+    scores = torch.randint(0, 50, (B, n_q, n_k), dtype=torch.int32, generator=g, device=DEV)  # many ties
+    q_off = n_k - n_q
+    idx, n_sel = L.lsa_select_topk(scores=scores, n_sink=n_sink, n_window=W, k_dyn=kd, q_off=q_off)
+    idx2, n_sel2 = L.lsa_select_topk(scores=scores, n_sink=n_sink, n_window=W, k_dyn=kd, q_off=q_off)
+    torch.cuda.synchronize()
+    assert torch.equal(idx, idx2) and torch.equal(n_sel, n_sel2)
+    Sn, In, Nn = np_(scores), np_(idx), np_(n_sel)
+    K_tot = n_sink + W + kd
+    for b in range(B):
+        for i in range(n_q):
+            ref = O.select_flat(Sn[b, i], q_off + i, n_sink, W, kd)
+            check_idx(In[b, i], Nn[b, i], ref, K_tot, f"b{b} i{i}")
+
+
+def test_select_given_scores_short_rows():
+    say("select short rows")
+    n = 300
+    g = torch.Generator(device=DEV)
+    g.manual_seed(78)
+    scores = torch.randint(-1000, 1000, (1, n, n), dtype=torch.int32, generator=g, device=DEV)
+    idx, n_sel = L.lsa_select_topk(scores=scores, n_sink=4, n_window=64, k_dyn=188, q_off=0)
+    Sn, In, Nn = np_(scores), np_(idx), np_(n_sel)
+    for t in range(n):
+        check_idx(In[0, t], Nn[0, t], O.select_flat(Sn[0, t], t, 4, 64, 188), 256, f"t{t}")
+
+
+def test_fused_select_c1_full():
+    wl = configs.C1
+    say("fused select C1 full")
+    q_idx, k_idx, w = synth.indexer_inputs(wl, DEV)
+    idx, n_sel = L.lsa_select_topk(q_idx, k_idx, w, wl.n_sink, wl.n_window, wl.k_dyn, q_off=0)
+    idx2, _ = L.lsa_select_topk(q_idx, k_idx, w, wl.n_sink, wl.n_window, wl.k_dyn, q_off=0)
+    torch.cuda.synchronize()
+    assert torch.equal(idx, idx2)
+    qn, kn, In, Nn = np_(q_idx[0]), np_(k_idx[0]), np_(idx[0]), np_(n_sel[0])
+    for r0 in range(0, wl.L, 512):
+        S = O.index_scores(qn[r0:r0 + 512], kn, w, q_off=r0)
+        for i in range(S.shape[0]):
+            t = r0 + i
+            check_idx(In[t], Nn[t], O.select_flat(S[i], t, wl.n_sink, wl.n_window, wl.k_dyn), wl.K_tot, f"t{t}")
+
+
+def test_fused_select_multichunk_matches_unfused_and_oracle():
+    say("fused select 9000 x H_I 64")
+    wl = configs.C2
+    Lq = 9000
+    q_idx, k_idx, w = synth.indexer_inputs(wl, DEV, L=Lq)
+    idx, n_sel = L.lsa_select_topk(q_idx, k_idx, w, wl.n_sink, wl.n_window, wl.k_dyn, q_off=0)
+    S = L.lsa_index_score(q_idx, k_idx, w, q_off=0)
+    idx_u, n_sel_u = L.lsa_select_topk(scores=S, n_sink=wl.n_sink, n_window=wl.n_window, k_dyn=wl.k_dyn, q_off=0)
+    torch.cuda.synchronize()
+    assert torch.equal(idx, idx_u) and torch.equal(n_sel, n_sel_u)
+    del S
+    qn, kn, In, Nn = np_(q_idx[0]), np_(k_idx[0]), np_(idx[0]), np_(n_sel[0])
+    rows = [0, 1, 2046, 2047, 2048, 2049, 5000, 8700, 8707, 8708, 8709, 8998, 8999]
+    for t in rows:
+        S_t = O.index_scores(qn[t:t + 1], kn[: t + 1], w, q_off=t)[0]
+        check_idx(In[t], Nn[t], O.select_flat(S_t, t, wl.n_sink, wl.n_window, wl.k_dyn), wl.K_tot, f"t{t}")
+
+
+# ------------------------------------------------------------------ HI
+@pytest.mark.parametrize("blk", [32, 64, 128])
+def test_block_summary(blk):
+    say(f"block summary blk={blk}")
+    n_k = blk * 37 + 13
+    k = i8((2, n_k, 128), -128, 127, "bs", blk)
+    kb = L.lsa_block_summary(k, blk)
+    for b in range(2):
+        assert np.array_equal(np_(kb[b]).astype(np.int64), O.block_summary(np_(k[b]), blk))
+    for v in (-128, 127, -1):
+        k = torch.full((1, 64 * 3, 64), v, dtype=torch.int8, device=DEV)
+        assert torch.all(L.lsa_block_summary(k, 64) == v)
+
+
+@pytest.mark.parametrize("rec,ns,W,kd", [(32, 4, 512, 300), (8, 4, 64, 1000), (1000, 4, 128, 500), (3, 0, 0, 64)])
+def test_hier_select_matches_oracle(rec, ns, W, kd):
+    say(f"hier select rec={rec} ns={ns} W={W} kd={kd}")
+    B, n_k, H_I, d_I, blk = 2, 20000, 64, 128, 64
+    q = i8((B, H_I, d_I), -16, 15, "hq")
+    k = i8((B, n_k, d_I), -16, 15, "hk")
+    w = synth.int_weights(H_I, 1, 8, 9)
+    kb = L.lsa_block_summary(k, blk)
+    idx, n_sel = L.lsa_hier_select(q, k, kb, w, blk, rec, ns, W, kd)
+    idx2, _ = L.lsa_hier_select(q, k, kb, w, blk, rec, ns, W, kd)
+    torch.cuda.synchronize()
+    assert torch.equal(idx, idx2)
+    In, Nn = np_(idx), np_(n_sel)
+    for b in range(B):
+        kn = np_(k[b])
+        ref = O.hier_select(np_(q[b]), kn, O.block_summary(kn, blk), w, blk, rec, ns, W, kd)
+        check_idx(In[b], Nn[b], ref, ns + W + kd, f"b{b}")
+    if rec >= n_k // blk:   # every eligible block recalled: HI equals flat selection
+        flat, nf = L.lsa_select_topk(q[:, None].contiguous(), k, w, ns, W, kd, q_off=n_k - 1)
+        assert torch.equal(flat[:, 0], idx) and torch.equal(nf[:, 0], n_sel)
+
+
+def test_hier_planted_block():
+    say("hier planted block")
+    n_k, blk = 8192, 64
+    k = i8((1, n_k, 128), -2, 2, "pk")
+    k[0, 40 * blk:41 * blk] = 15
+    q = torch.ones((1, 8, 128), dtype=torch.int8, device=DEV)
+    kb = L.lsa_block_summary(k, blk)
+    idx, n_sel = L.lsa_hier_select(q, k, kb, [1] * 8, blk, 1, 4, 8, 16)
+    fine = np_(idx[0])[4:4 + 16]
+    assert int(n_sel[0]) == 28 and np.all((fine >= 40 * blk) & (fine < 41 * blk))
+
+
+# ------------------------------------------------------------------ attention
+def random_index(B, rows, K_tot, t_of_row, n_k, seed):
+    rng = np.random.default_rng(seed)
+    idx = np.full((B, rows, K_tot), -1, dtype=np.int32)
+    n_sel = np.zeros((B, rows), dtype=np.int32)
+    for b in range(B):
+        for r in range(rows):
+            t = t_of_row(r)
+            n = min(t + 1, K_tot)
+            sel = np.sort(rng.choice(t + 1, n, replace=False))
+            idx[b, r, :n] = sel
+            n_sel[b, r] = n
+    return idx, n_sel
+
+
+@pytest.mark.parametrize("H", [16, 64, 128])
+def test_prefill_attention(H):
+    say(f"prefill attention H={H}")
+    B, Lq, K_tot = 2, 333, 96
+    q = bf((B, Lq, H, 128), "pq", H)
+    k = bf((B, Lq, 128), "pk", H)
+    v = bf((B, Lq, 128), "pv", H)
+    idx, n_sel = random_index(B, Lq, K_tot, lambda r: r, Lq, H)
+    idx[1, 200, 7] = Lq + 5          # out-of-range entry: skipped by the kernel
+    idx_t, ns_t = torch.from_numpy(idx).to(DEV), torch.from_numpy(n_sel).to(DEV)
+    o, lse = L.lsa_sparse_attn_prefill(q, k, v, idx_t, ns_t, want_lse=True)
+    o2, lse2 = L.lsa_sparse_attn_prefill(q, k, v, idx_t, ns_t, want_lse=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o2) and torch.equal(lse, lse2)
+    qf, kf, vf, of, lf = f64(q), f64(k), f64(v), f64(o), np_(lse)
+    scale = 128 ** -0.5
+    for b in range(B):
+        ref_o = np.zeros((Lq, H, 128))
+        ref_l = np.zeros((Lq, H))
+        for t in range(Lq):
+            sel = idx[b, t, : n_sel[b, t]]
+            sel = sel[(sel >= 0) & (sel < Lq)]
+            ref_o[t], ref_l[t] = O.attend(qf[b, t], kf[b], vf[b], sel, scale)
+        assert_attn_close(of[b], ref_o, f"o b{b}")
+        assert np.abs(lf[b] - ref_l).max() < 1e-3
+
+
+@pytest.mark.parametrize("H,n_q,n_idx,n_split", [(64, 4, 1, 8), (64, 4, 4, 3), (16, 2, 1, 5), (128, 1, 1, 1),
+                                                 (64, 1, 1, 64)])
+def test_decode_attention(H, n_q, n_idx, n_split):
+    say(f"decode attention H={H} n_q={n_q} n_idx={n_idx} n_split={n_split}")
+    B, n_k, K_tot = 3, 5000, 700
+    q = bf((B, n_q, H, 128), "dq", H, n_q)
+    kc = bf((B, n_k, 128), "dk", H)
+    vc = bf((B, n_k, 128), "dv", H)
+    rng = np.random.default_rng(n_split)
+    idx = np.full((B, n_idx, K_tot), -1, dtype=np.int32)
+    n_sel = np.zeros((B, n_idx), dtype=np.int32)
+    for b in range(B):
+        for r in range(n_idx):
+            n = [700, 650, 5][b]   # the last has fewer keys than splits
+            idx[b, r, :n] = np.sort(rng.choice(n_k, n, replace=False))
+            n_sel[b, r] = n
+    idx_t, ns_t = torch.from_numpy(idx).to(DEV), torch.from_numpy(n_sel).to(DEV)
+    o, lse = L.lsa_sparse_attn_decode(q, kc, vc, idx_t, ns_t, n_split=n_split, want_lse=True)
+    o2, lse2 = L.lsa_sparse_attn_decode(q, kc, vc, idx_t, ns_t, n_split=n_split, want_lse=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o2) and torch.equal(lse, lse2)
+    qf, kf, vf, of, lf = f64(q), f64(kc), f64(vc), f64(o), np_(lse)
+    scale = 128 ** -0.5
+    for b in range(B):
+        for r in range(n_q):
+            sel = idx[b, 0 if n_idx == 1 else r, : n_sel[b, 0 if n_idx == 1 else r]]
+            ref_o, ref_l = O.attend(qf[b, r], kf[b], vf[b], sel, scale)
+            assert_attn_close(of[b, r], ref_o, f"o b{b} r{r}")
+            assert np.abs(lf[b, r] - ref_l).max() < 1e-3
+    if n_split > 1:   # the split count changes rounding only: n_split = 1 is in tolerance too
+        o1 = f64(L.lsa_sparse_attn_decode(q, kc, vc, idx_t, ns_t, n_split=1))
+        for b in range(B):
+            for r in range(n_q):
+                sel = idx[b, 0 if n_idx == 1 else r, : n_sel[b, 0 if n_idx == 1 else r]]
+                ref_o, _ = O.attend(qf[b, r], kf[b], vf[b], sel, scale)
+                assert_attn_close(o1[b, r], ref_o, f"n_split=1 b{b} r{r}")
+
+
+# ------------------------------------------------------------------ whole path
+def test_c1_end_to_end_and_cli_reuse():
+    wl = configs.C1
+    say("C1 end to end")
+    q_idx, k_idx, w = synth.indexer_inputs(wl, DEV)
+    idx, n_sel = L.lsa_select_topk(q_idx, k_idx, w, wl.n_sink, wl.n_window, wl.k_dyn, q_off=0)
+    outs = []
+    for layer in range(2):   # two layers reuse the layer-1 index (CLI)
+        q, k, v = synth.attention_inputs(wl, layer, DEV)
+        outs.append((L.lsa_sparse_attn_prefill(q, k, v, idx, n_sel), q, k, v))
+    # reuse equals recomputing the index
+    idx_re, n_sel_re = L.lsa_select_topk(q_idx, k_idx, w, wl.n_sink, wl.n_window, wl.k_dyn, q_off=0)
+    q, k, v = outs[1][1:]
+    o_re = L.lsa_sparse_attn_prefill(q, k, v, idx_re, n_sel_re)
+    torch.cuda.synchronize()
+    assert torch.equal(idx, idx_re) and torch.equal(outs[1][0], o_re)
+    In, Nn = np_(idx[0]), np_(n_sel[0])
+    qn, kn = np_(q_idx[0]), np_(k_idx[0])
+    rows = list(range(0, 8)) + list(range(250, 262)) + list(range(4090, 4096)) + list(range(1000, 4000, 97))
+    for o, q, k, v in outs:
+        qf, kf, vf, of = f64(q[0]), f64(k[0]), f64(v[0]), f64(o[0])
+        for t in rows:
+            S = O.index_scores(qn[t:t + 1], kn[: t + 1], w, q_off=t)[0]
+            sel = O.select_flat(S, t, wl.n_sink, wl.n_window, wl.k_dyn)
+            assert np.array_equal(In[t, : Nn[t]], sel)
+            ref, _ = O.attend(qf[t], kf, vf, sel, wl.scale)
+            assert_attn_close(of[t], ref, f"t{t}")
