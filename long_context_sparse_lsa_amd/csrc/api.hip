@@ -53,10 +53,19 @@ int chunks_of(int64_t nc) { return (int)std::max<int64_t>(1, (nc + kSelChunk - 1
 // Rows per pass of the fused (score + select) prefill path: the score buffer
 // of one pass is at most kFusedScoreBytes.
 constexpr size_t kFusedScoreBytes = (size_t)512 << 20;
-int fused_rows(int n_q, int n_k) {
+// Returns the rows of one query range (R) and the sequences per pass (nb):
+// a long prefill is cut into row ranges of one sequence (nb = 1), a short
+// decode batch puts many whole sequences into one pass.
+void fused_pass(int B, int n_q, int n_k, int& R, int& nb) {
   int64_t r = (int64_t)(kFusedScoreBytes / sizeof(int32_t)) / n_k;
   r = std::max<int64_t>(4, r / 4 * 4);
-  return (int)std::min<int64_t>(r, n_q);
+  if (r <= n_q) {
+    R = (int)r;
+    nb = 1;
+  } else {
+    R = n_q;
+    nb = (int)std::min<int64_t>(B, r / n_q);
+  }
 }
 
 }  // namespace
@@ -125,7 +134,7 @@ extern "C" int32_t lsa_select_topk(const int32_t* scores, const int8_t* q_idx, c
 
   // workspace
   size_t need;
-  int R = 0;
+  int R = 0, nb_pass = 1;
   int rows_pass = B * n_q;
   if (scores != nullptr) {
     const size_t per_row = select_ws_bytes(1, chunks_of(max_nc), k_cap);
@@ -133,8 +142,9 @@ extern "C" int32_t lsa_select_topk(const int32_t* scores, const int8_t* q_idx, c
       rows_pass = (int)std::max<size_t>(1, std::min<size_t>(rows_pass, kFusedScoreBytes / per_row));
     need = select_ws_bytes(rows_pass, chunks_of(max_nc), k_cap);
   } else {
-    R = fused_rows(n_q, n_k);
-    need = align_up((size_t)R * n_k * sizeof(int32_t)) + select_ws_bytes(R, chunks_of(max_nc), k_cap);
+    fused_pass(B, n_q, n_k, R, nb_pass);
+    const size_t rows = (size_t)R * nb_pass;
+    need = align_up(rows * n_k * sizeof(int32_t)) + select_ws_bytes((int)rows, chunks_of(max_nc), k_cap);
   }
   need = align_up(std::max<size_t>(need, 1));
   if (ws_needed) *ws_needed = need;
@@ -171,10 +181,12 @@ extern "C" int32_t lsa_select_topk(const int32_t* scores, const int8_t* q_idx, c
     return LSA_OK;
   }
 
-  // Fused path: score a pass of R rows (candidates only) into workspace, then select.
+  // Fused path: score a pass of rows (candidates only) into workspace, then
+  // select. A pass covers nb sequences times one range of Rr query rows.
   int32_t* sbuf = (int32_t*)ws;
-  void* sel_ws = (char*)ws + align_up((size_t)R * n_k * sizeof(int32_t));
-  for (int b = 0; b < B; ++b) {
+  void* sel_ws = (char*)ws + align_up((size_t)R * nb_pass * n_k * sizeof(int32_t));
+  for (int b0 = 0; b0 < B; b0 += nb_pass) {
+    const int nb = std::min(nb_pass, B - b0);
     for (int r0 = 0; r0 < n_q; r0 += R) {
       const int Rr = std::min(R, n_q - r0);
       const int t_last = q_off + r0 + Rr - 1;
@@ -182,16 +194,16 @@ extern "C" int32_t lsa_select_topk(const int32_t* scores, const int8_t* q_idx, c
       if (nc_last > 0 && t_last + 1 > K_tot) {
         ScoreArgs a{};
         a.w = wa;
-        a.q = q_idx + ((int64_t)b * n_q + r0) * H_I * d_I;
-        a.k = k_idx + (int64_t)b * n_k * d_I;
-        a.B = 1;
+        a.q = q_idx + ((int64_t)b0 * n_q + r0) * H_I * d_I;
+        a.k = k_idx + (int64_t)b0 * n_k * d_I;
+        a.B = nb;
         a.n_q = Rr;
         a.n_k = n_k;
         a.H_I = H_I;
         a.d_I = d_I;
-        a.q_bstride = 0;
-        a.k_bstride = 0;
-        a.s_bstride = 0;
+        a.q_bstride = (int64_t)n_q * H_I * d_I;
+        a.k_bstride = (int64_t)n_k * d_I;
+        a.s_bstride = (int64_t)Rr * n_k;
         a.ld = n_k;
         a.n_keys = std::min<int64_t>(n_k, (int64_t)t_last - cfg.n_window + 1);
         a.mask_off = q_off + r0 - cfg.n_window;
@@ -204,15 +216,19 @@ extern "C" int32_t lsa_select_topk(const int32_t* scores, const int8_t* q_idx, c
           if (s != LSA_OK) return s;
         }
       }
+      // rows of the pass: sequence b0 + j, query r0 + i at row j * Rr + i
       sa.scores = sbuf;
       sa.ld = n_k;
-      sa.n_rows = Rr;
+      sa.n_rows = nb * Rr;
       sa.n_q = Rr;
       sa.q_off = q_off + r0;
-      sa.idx = idx + ((int64_t)b * n_q + r0) * K_tot;
-      sa.n_sel = n_sel + (int64_t)b * n_q + r0;
+      sa.row0 = 0;
       sa.max_chunks = chunks_of(nc_last);
-      select_bind_ws(sa, sel_ws, Rr);
+      select_bind_ws(sa, sel_ws, nb * Rr);
+      // nb > 1 only when Rr == n_q (r0 == 0), so the pass's output rows are
+      // contiguous in idx / n_sel
+      sa.idx = idx + ((int64_t)b0 * n_q + r0) * K_tot;
+      sa.n_sel = n_sel + (int64_t)b0 * n_q + r0;
       s = hip_status(launch_select(sa, st));
       if (s != LSA_OK) return s;
     }

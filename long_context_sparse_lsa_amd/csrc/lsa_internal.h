@@ -32,6 +32,10 @@ struct ScoreArgs {
   int32_t* scores;
 };
 hipError_t launch_index_score(const ScoreArgs& a, hipStream_t st);
+// Many-row variant (LDS-shared key tiles); covers direct keys (no blocks),
+// H_I in {32, 64}, n_q >= 8.
+bool index_prefill_supported(const ScoreArgs& a);
+hipError_t launch_index_prefill(const ScoreArgs& a, hipStream_t st);
 
 // Selection launch.
 enum SelMode { SEL_FLAT = 0, SEL_RAW = 1, SEL_INDIRECT = 2 };
