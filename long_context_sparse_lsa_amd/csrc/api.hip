@@ -48,7 +48,13 @@ int32_t hip_status(hipError_t e) { return e == hipSuccess ? LSA_OK : LSA_HIP; }
 
 int k_cap_of(int k) { return std::max(4, (k + 3) / 4 * 4); }
 
-int chunks_of(int64_t nc) { return (int)std::max<int64_t>(1, (nc + kSelChunk - 1) / kSelChunk); }
+int chunks_of(int64_t nc) { return select_chunks(nc); }
+
+// Stage two of a multi-chunk selection holds every chunk's survivors at once.
+bool survivors_ok(int64_t max_nc, int k_cap) {
+  const int ch = chunks_of(max_nc);
+  return ch <= 1 || (int64_t)ch * k_cap <= kSelMaxSurvivors;
+}
 
 // Rows per pass of the fused (score + select) prefill path: the score buffer
 // of one pass is at most kFusedScoreBytes.
@@ -122,6 +128,7 @@ extern "C" int32_t lsa_select_topk(const int32_t* scores, const int8_t* q_idx, c
   const int K_tot = cfg.n_sink + cfg.n_window + cfg.k_dyn;
   const int k_cap = k_cap_of(cfg.k_dyn);
   const int64_t max_nc = (int64_t)q_off + n_q - cfg.n_window - cfg.n_sink;  // last row's candidates
+  if (!survivors_ok(max_nc, k_cap)) return LSA_UNSUPPORTED;
   WArgs wa{};
   if (scores == nullptr) {
     if (!al16(q_idx) || !al16(k_idx)) return LSA_INVALID_ARG;
@@ -173,7 +180,7 @@ extern "C" int32_t lsa_select_topk(const int32_t* scores, const int8_t* q_idx, c
       sa.row0 = (int)(r0 % n_q);
       sa.idx = idx + r0 * K_tot;
       sa.n_sel = n_sel + r0;
-      sa.max_chunks = chunks_of(max_nc);
+      select_plan(sa, max_nc);
       select_bind_ws(sa, ws, Rr);
       s = hip_status(launch_select(sa, st));
       if (s != LSA_OK) return s;
@@ -223,7 +230,7 @@ extern "C" int32_t lsa_select_topk(const int32_t* scores, const int8_t* q_idx, c
       sa.n_q = Rr;
       sa.q_off = q_off + r0;
       sa.row0 = 0;
-      sa.max_chunks = chunks_of(nc_last);
+      select_plan(sa, nc_last);
       select_bind_ws(sa, sel_ws, nb * Rr);
       // nb > 1 only when Rr == n_q (r0 == 0), so the pass's output rows are
       // contiguous in idx / n_sel
@@ -264,6 +271,7 @@ extern "C" int32_t lsa_hier_select(const int8_t* q_idx, const int8_t* k_idx, con
   const int n_elig = trivial ? 0 : b_hi - b_lo + 1;
   const int n_virt = n_blk_recall * blk;
   const int kc_coarse = k_cap_of(n_blk_recall), kc_fine = k_cap_of(cfg.k_dyn);
+  if (!survivors_ok(n_elig, kc_coarse) || !survivors_ok(n_virt, kc_fine)) return LSA_UNSUPPORTED;
 
   const size_t sz_coarse = align_up((size_t)B * nblocks * sizeof(int32_t));
   const size_t sz_blocks = align_up((size_t)B * n_blk_recall * sizeof(int32_t));
@@ -293,7 +301,7 @@ extern "C" int32_t lsa_hier_select(const int8_t* q_idx, const int8_t* k_idx, con
     sa.idx = idx;
     sa.n_sel = n_sel;
     sa.out_ld = K_tot;
-    sa.max_chunks = 1;
+    select_plan(sa, 1);
     sa.k_cap = kc_fine;
     return hip_status(launch_select(sa, st));
   }
@@ -344,7 +352,7 @@ extern "C" int32_t lsa_hier_select(const int8_t* q_idx, const int8_t* k_idx, con
   sc.idx = blocks;
   sc.n_sel = nblk;
   sc.out_ld = n_blk_recall;
-  sc.max_chunks = chunks_of(n_elig);
+  select_plan(sc, n_elig);
   sc.k_cap = kc_coarse;
   select_bind_ws(sc, sel_ws, B);
   s = hip_status(launch_select(sc, st));
@@ -384,7 +392,7 @@ extern "C" int32_t lsa_hier_select(const int8_t* q_idx, const int8_t* k_idx, con
   sf.idx = idx;
   sf.n_sel = n_sel;
   sf.out_ld = K_tot;
-  sf.max_chunks = chunks_of(n_virt);
+  select_plan(sf, n_virt);
   sf.k_cap = kc_fine;
   select_bind_ws(sf, sel_ws, B);
   return hip_status(launch_select(sf, st));

@@ -64,10 +64,16 @@ struct SelectArgs {
   int32_t* ws_score;
   int32_t* ws_pos;
   int32_t* ws_cnt;
-  int max_chunks;
+  int max_chunks;  // chunks of the longest row (select_chunks)
+  int chunk_e;     // candidates per thread of a chunk (select_plan)
   int k_cap;
 };
-constexpr int kSelChunk = 8192;  // candidates per first-stage workgroup
+// Chunk geometry for rows of at most max_nc candidates: the chunk count of
+// the longest row, and a plan that sets max_chunks and chunk_e together.
+int select_chunks(int64_t max_nc);
+void select_plan(SelectArgs& a, int64_t max_nc);
+// Largest stage-two input (max_chunks * k_cap) the selection supports.
+constexpr int64_t kSelMaxSurvivors = 32 * 1024;
 size_t select_ws_bytes(int n_rows, int max_chunks, int k_cap);
 void select_bind_ws(SelectArgs& a, void* ws, int n_rows);
 hipError_t launch_select(const SelectArgs& a, hipStream_t st);

@@ -6,28 +6,37 @@
 // paragraph pairs them with a contiguous window, and the sinks of the
 // "架构拆解 ① LSA" section of the 1.6T training write-up are always kept.)
 //
-// Method: radix select on the order-preserving uint32 image of the score,
-// 8 bits per pass, with LDS histograms (integer atomics: counts do not depend
-// on arrival order). It yields the exact k-th largest score T and how many of
-// the entries equal to T are taken; a stable, order-preserving compaction then
-// keeps every entry above T and the first r entries equal to T. Candidates are
-// laid out in ascending position, so the output is ascending and bit-exact.
+// One workgroup of 1024 threads takes a chunk of up to 1024 * E candidates of
+// one row and holds them in registers, E consecutive candidates per thread
+// (blocked layout, so thread order is candidate order). Scores map to
+// order-preserving uint32 keys (INT32_MIN, the "not a candidate" mark, maps to
+// 0). A radix select finds the exact k-th largest key T: the first digit
+// starts at the highest bit in which the chunk's smallest and largest keys
+// differ, so a chunk whose scores span 2^18 values needs two or three 8-bit
+// passes, each an LDS histogram of the keys that still match the prefix
+// (integer counts: independent of arrival order). A stable compaction (two
+// block-wide prefix sums in thread order) then keeps every key above T and
+// the first r keys equal to T, i.e. the lowest positions among the ties, and
+// writes them in ascending position order. The result is bit-exact.
 //
-// Rows with more than kSelChunk candidates run in two stages: stage A keeps
-// min(k, chunk) per chunk (a superset of the row's top-k within that chunk),
-// stage B selects the row's top-k from the concatenated chunk survivors.
+// Rows longer than one chunk run in two stages: stage A keeps the chunk-local
+// top min(k, valid) of every chunk (a superset of the row's top-k inside that
+// chunk), stage B selects the row's top-k from the concatenated survivors,
+// which are still in ascending position order.
 #include "lsa_device.h"
 #include "lsa_internal.h"
 
 namespace lsa {
 
-constexpr int SEL_NT = 512;
+namespace {
+
+constexpr int SEL_NT = 1024;
 constexpr int SEL_NW = SEL_NT / 64;
-constexpr int SEL_EPT = 4;
 
 struct SelShared {
   uint32_t hist[256];
-  int scan_tmp[SEL_NW];
+  int scan_w[SEL_NW];
+  uint32_t red_w[2][SEL_NW];
   int bcast[4];
 };
 
@@ -69,14 +78,15 @@ __device__ __forceinline__ int pos_of(const SelectArgs& a, int r, int v) {
   return bi * a.blk + v % a.blk;
 }
 
+// Exclusive prefix sum over the block in thread order; *total gets the sum.
 __device__ __forceinline__ int block_excl_scan(int v, SelShared& sh, int* total) {
   const int incl = wave_incl_scan(v);
-  if (lane_id() == 63) sh.scan_tmp[wave_id()] = incl;
+  if (lane_id() == 63) sh.scan_w[wave_id()] = incl;
   __syncthreads();
   int off = 0, tot = 0;
 #pragma unroll
   for (int w = 0; w < SEL_NW; ++w) {
-    const int x = sh.scan_tmp[w];
+    const int x = sh.scan_w[w];
     off += (w < wave_id()) ? x : 0;
     tot += x;
   }
@@ -85,36 +95,51 @@ __device__ __forceinline__ int block_excl_scan(int v, SelShared& sh, int* total)
   return off + incl - v;
 }
 
-__device__ __forceinline__ int block_sum(int v, SelShared& sh) {
-  int tot;
-  block_excl_scan(v, sh, &tot);
-  return tot;
+__device__ __forceinline__ uint32_t wave_max_u(uint32_t v) {
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, d, 64));
+  return v;
+}
+__device__ __forceinline__ uint32_t wave_min_u(uint32_t v) {
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) v = min(v, (uint32_t)__shfl_xor((int)v, d, 64));
+  return v;
 }
 
-// Threshold of the k-th largest key among get(0..n-1) (0 < k <= #nonzero keys).
-// Entry u is kept iff (u >> shift) > (T >> shift), or (u >> shift) == (T >> shift)
-// and it is among the first r_eq such entries in index order.
-template <class Get>
-__device__ void radix_select(Get get, int n, int k, SelShared& sh, uint32_t& T, int& shift_out,
-                             int& r_eq) {
-  const int tid = threadIdx.x;
-  uint32_t prefix = 0, mask = 0;
+// Threshold of the k-th largest nonzero key of the chunk (0 < k < #nonzero).
+// On return an entry u is kept iff (u >> shift) > (T >> shift), or
+// (u >> shift) == (T >> shift) and it is among the first r_eq such entries.
+template <int E>
+__device__ void radix_select(const uint32_t (&u)[E], uint32_t kmin, uint32_t kmax, int k,
+                             SelShared& sh, uint32_t& T, int& shift_out, int& r_eq) {
+  if (kmin == kmax) {  // every candidate has the same key: take the first k
+    T = kmax;
+    shift_out = 0;
+    r_eq = k;
+    return;
+  }
+  int hb = 31 - __clz(kmin ^ kmax);  // highest differing bit
+  uint32_t mask = hb == 31 ? 0u : ~((2u << hb) - 1u);
+  uint32_t prefix = kmax & mask;
   int k_rem = k;
-  for (int shift = 24; shift >= 0; shift -= 8) {
-    for (int i = tid; i < 256; i += SEL_NT) sh.hist[i] = 0;
+  const int tid = threadIdx.x;
+  while (true) {
+    const int lo = max(0, hb - 7);
+    const uint32_t dmask = (2u << (hb - lo)) - 1u;  // digit of hb - lo + 1 bits
+    if (tid < 256) sh.hist[tid] = 0;
     __syncthreads();
-    for (int i = tid; i < n; i += SEL_NT) {
-      const uint32_t u = get(i);
-      if ((u & mask) == prefix) atomicAdd(&sh.hist[(u >> shift) & 255u], 1u);
-    }
+#pragma unroll
+    for (int e = 0; e < E; ++e)
+      if (u[e] != 0u && (u[e] & mask) == prefix) atomicAdd(&sh.hist[(u[e] >> lo) & dmask], 1u);
     __syncthreads();
     if (wave_id() == 0) {
+      // lane l owns bins 4l .. 4l+3; find the bin holding the k_rem-th largest
       const int l = lane_id();
       int h[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) h[e] = (int)sh.hist[4 * l + e];
       const int s = h[0] + h[1] + h[2] + h[3];
-      int v = s;
+      int v = s;  // inclusive suffix sum over lanes
 #pragma unroll
       for (int d = 1; d < 64; d <<= 1) {
         const int t = __shfl_down(v, d, 64);
@@ -134,73 +159,46 @@ __device__ void radix_select(Get get, int n, int k, SelShared& sh, uint32_t& T, 
     __syncthreads();
     const uint32_t d = (uint32_t)sh.bcast[0];
     const int above = sh.bcast[1], eq = sh.bcast[2];
+    __syncthreads();  // bcast / hist are rewritten by the next pass
     k_rem -= above;
-    prefix |= d << shift;
-    mask |= 255u << shift;
-    if (eq == k_rem || shift == 0) {
+    prefix |= d << lo;
+    mask |= dmask << lo;
+    if (eq == k_rem || lo == 0) {
       T = prefix;
-      shift_out = shift;
+      shift_out = lo;
       r_eq = k_rem;
       return;
     }
+    hb = lo - 1;
   }
 }
 
-// Stable compaction: calls emit(out_pos, i, u) for every kept entry, in index
-// order; returns the number kept (uniform over the block).
-template <class Get, class Emit>
-__device__ int compact(Get get, int n, uint32_t T, int shift, int r_eq, SelShared& sh, Emit emit) {
+// Stable compaction over the chunk; emit(out_pos, e) for each kept entry e
+// of this thread, in candidate order. Returns the number kept.
+template <int E, class Emit>
+__device__ int compact(const uint32_t (&u)[E], uint32_t T, int shift, int r_eq, SelShared& sh, Emit emit) {
   const uint32_t Ts = T >> shift;
-  int eq_before = 0, sel_before = 0;
-  for (int base = 0; base < n; base += SEL_NT * SEL_EPT) {
-    const int i0 = base + threadIdx.x * SEL_EPT;
-    uint32_t u[SEL_EPT];
-    int gt[SEL_EPT], eq[SEL_EPT];
-    int n_eq = 0;
+  int n_eq = 0;
 #pragma unroll
-    for (int e = 0; e < SEL_EPT; ++e) {
-      const bool in = i0 + e < n;
-      u[e] = in ? get(i0 + e) : 0u;
-      const uint32_t us = u[e] >> shift;
-      gt[e] = in && us > Ts;
-      eq[e] = in && us == Ts;
-      n_eq += eq[e];
-    }
-    int eq_tot;
-    int eq_rank = eq_before + block_excl_scan(n_eq, sh, &eq_tot);
-    int sel[SEL_EPT], n_sel = 0;
+  for (int e = 0; e < E; ++e) n_eq += (u[e] != 0u && (u[e] >> shift) == Ts);
+  int eq_tot;
+  int eq_rank = block_excl_scan(n_eq, sh, &eq_tot);
+  uint32_t keep = 0;  // bit e: entry e kept (E <= 32)
 #pragma unroll
-    for (int e = 0; e < SEL_EPT; ++e) {
-      sel[e] = gt[e] || (eq[e] && eq_rank < r_eq);
-      eq_rank += eq[e];
-      n_sel += sel[e];
-    }
-    int sel_tot;
-    int opos = sel_before + block_excl_scan(n_sel, sh, &sel_tot);
-#pragma unroll
-    for (int e = 0; e < SEL_EPT; ++e)
-      if (sel[e]) emit(opos++, i0 + e, u[e]);
-    eq_before += eq_tot;
-    sel_before += sel_tot;
+  for (int e = 0; e < E; ++e) {
+    const bool valid = u[e] != 0u;
+    const uint32_t us = u[e] >> shift;
+    const bool eq = valid && us == Ts;
+    const bool sel = (valid && us > Ts) || (eq && eq_rank < r_eq);
+    eq_rank += eq;
+    keep |= (uint32_t)sel << e;
   }
-  return sel_before;
-}
-
-// Selection parameters for "keep k of the valid entries".
-__device__ __forceinline__ void plan(int k, int n_valid, uint32_t& T, int& shift, int& r_eq,
-                                     bool& need_radix) {
-  need_radix = false;
-  if (k <= 0) {
-    T = 0xffffffffu;
-    shift = 0;
-    r_eq = 0;  // nothing exceeds T; ties not taken
-  } else if (k >= n_valid) {
-    T = 0u;
-    shift = 0;
-    r_eq = 0;  // every nonzero key exceeds 0
-  } else {
-    need_radix = true;
-  }
+  int tot;
+  int o = block_excl_scan(__popc(keep), sh, &tot);
+#pragma unroll
+  for (int e = 0; e < E; ++e)
+    if ((keep >> e) & 1u) emit(o++, e);
+  return tot;
 }
 
 __device__ void write_trivial(const SelectArgs& a, int r, int t) {
@@ -225,74 +223,173 @@ __device__ void finalize(const SelectArgs& a, int r, const RowGeom& gm, int coun
   if (threadIdx.x == 0) a.n_sel[r] = w0 + W;
 }
 
+// Chunk statistics: number of nonzero keys, their min and max.
+template <int E>
+__device__ void chunk_stats(const uint32_t (&u)[E], SelShared& sh, int& n_valid, uint32_t& kmin,
+                            uint32_t& kmax) {
+  int cnt = 0;
+  uint32_t mn = 0xffffffffu, mx = 0u;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    cnt += u[e] != 0u;
+    if (u[e] != 0u) {
+      mn = min(mn, u[e]);
+      mx = max(mx, u[e]);
+    }
+  }
+  mn = wave_min_u(mn);
+  mx = wave_max_u(mx);
+  if (lane_id() == 0) {
+    sh.red_w[0][wave_id()] = mn;
+    sh.red_w[1][wave_id()] = mx;
+  }
+  int tot;
+  block_excl_scan(cnt, sh, &tot);  // its barriers also publish red_w
+  mn = 0xffffffffu;
+  mx = 0u;
+#pragma unroll
+  for (int w = 0; w < SEL_NW; ++w) {
+    mn = min(mn, sh.red_w[0][w]);
+    mx = max(mx, sh.red_w[1][w]);
+  }
+  n_valid = tot;
+  kmin = mn;
+  kmax = mx;
+}
+
+// Keys of candidates [v0, v0 + n) of a score row, E per thread (blocked).
+template <int E>
+__device__ void load_keys(const int32_t* row, int v0, int n, uint32_t (&u)[E]) {
+  const int i0 = threadIdx.x * E;
+  const int32_t* src = row + v0 + i0;
+  const bool vec = (((uintptr_t)src & 15u) == 0) && i0 + E <= n;
+  if (vec) {
+#pragma unroll
+    for (int e = 0; e < E; e += 4) {
+      const v4i x = *(const v4i*)(src + e);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) u[e + j] = score_key(x[j]);
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < E; ++e) u[e] = i0 + e < n ? score_key(src[e]) : 0u;
+  }
+}
+
+// Keep count for "k of n_valid" that needs no radix pass, or -1.
+__device__ __forceinline__ bool plan_trivial(int k, int n_valid, uint32_t& T, int& shift, int& r_eq) {
+  if (k <= 0) {
+    T = 0xffffffffu;  // nothing above, no ties taken
+    shift = 0;
+    r_eq = 0;
+    return true;
+  }
+  if (k >= n_valid) {
+    T = 0u;  // every nonzero key is above 0
+    shift = 0;
+    r_eq = 0;
+    return true;
+  }
+  return false;
+}
+
+template <int E>
 __global__ __launch_bounds__(SEL_NT) void select_stage_a(SelectArgs a) {
-  __shared__ uint32_t keys[kSelChunk];
   __shared__ SelShared sh;
+  constexpr int CH = SEL_NT * E;
   const int r = blockIdx.x, j = blockIdx.y;
   const RowGeom gm = row_geom(a, r);
   if (gm.trivial) {
     if (j == 0) write_trivial(a, r, gm.t);
     return;
   }
-  const int n_chunks = (gm.nc + kSelChunk - 1) / kSelChunk;
-  if (j >= max(n_chunks, 1)) return;
-  const int v0 = gm.c_lo + j * kSelChunk;
-  const int n = min(kSelChunk, gm.nc - j * kSelChunk);
+  const int n_chunks = max(1, (gm.nc + CH - 1) / CH);
+  if (j >= n_chunks) return;
+  const int v0 = gm.c_lo + j * CH;
+  const int n = max(0, min(CH, gm.nc - j * CH));
   const int32_t* row = a.scores + (int64_t)r * a.ld;
-  int valid = 0;
-  for (int i = threadIdx.x; i < n; i += SEL_NT) {
-    const uint32_t u = score_key(row[v0 + i]);
-    keys[i] = u;
-    valid += u != 0u;
-  }
-  const int n_valid = block_sum(valid, sh);  // includes a barrier: keys[] complete
-  uint32_t T;
+  uint32_t u[E];
+  load_keys<E>(row, v0, n, u);
+  int n_valid;
+  uint32_t kmin, kmax, T;
+  chunk_stats<E>(u, sh, n_valid, kmin, kmax);
   int shift, r_eq;
-  bool need;
-  plan(gm.k, n_valid, T, shift, r_eq, need);
-  auto get = [&](int i) -> uint32_t { return keys[i]; };
-  if (need) radix_select(get, n, gm.k, sh, T, shift, r_eq);
-  if (n_chunks <= 1) {
+  if (!plan_trivial(gm.k, n_valid, T, shift, r_eq)) radix_select<E>(u, kmin, kmax, gm.k, sh, T, shift, r_eq);
+  const int i0 = threadIdx.x * E;
+  if (n_chunks == 1) {
     int32_t* out = a.idx + (int64_t)r * a.out_ld + (a.mode == SEL_RAW ? 0 : a.n_sink);
-    const int cnt = compact(get, n, T, shift, r_eq, sh,
-                            [&](int o, int i, uint32_t) { out[o] = pos_of(a, r, v0 + i); });
+    const int cnt = compact<E>(u, T, shift, r_eq, sh, [&](int o, int e) { out[o] = pos_of(a, r, v0 + i0 + e); });
     finalize(a, r, gm, cnt);
   } else {
     const int64_t base = ((int64_t)r * a.max_chunks + j) * a.k_cap;
     int32_t* ws_s = a.ws_score + base;
     int32_t* ws_p = a.ws_pos + base;
-    const int cnt = compact(get, n, T, shift, r_eq, sh, [&](int o, int i, uint32_t u) {
-      ws_s[o] = (int32_t)(u ^ 0x80000000u);
-      ws_p[o] = pos_of(a, r, v0 + i);
+    const int cnt = compact<E>(u, T, shift, r_eq, sh, [&](int o, int e) {
+      ws_s[o] = (int32_t)(u[e] ^ 0x80000000u);
+      ws_p[o] = pos_of(a, r, v0 + i0 + e);
     });
     for (int i = cnt + threadIdx.x; i < a.k_cap; i += SEL_NT) ws_s[i] = kMasked;
   }
 }
 
-__global__ __launch_bounds__(SEL_NT) void select_stage_b(SelectArgs a) {
+// Stage B: top-k of the concatenated chunk survivors (n_chunks * k_cap
+// entries, padded with INT32_MIN) of one row.
+template <int E>
+__global__ __launch_bounds__(SEL_NT) void select_stage_b(SelectArgs a, int CH) {
   __shared__ SelShared sh;
   const int r = blockIdx.x;
   const RowGeom gm = row_geom(a, r);
   if (gm.trivial) return;
-  const int n_chunks = (gm.nc + kSelChunk - 1) / kSelChunk;
+  const int n_chunks = (gm.nc + CH - 1) / CH;
   if (n_chunks <= 1) return;
   const int n = n_chunks * a.k_cap;
   const int64_t base = (int64_t)r * a.max_chunks * a.k_cap;
   const int32_t* ws_s = a.ws_score + base;
   const int32_t* ws_p = a.ws_pos + base;
-  int valid = 0;
-  for (int i = threadIdx.x; i < n; i += SEL_NT) valid += ws_s[i] != kMasked;
-  const int n_valid = block_sum(valid, sh);
-  uint32_t T;
+  uint32_t u[E];
+  load_keys<E>(ws_s, 0, n, u);
+  int n_valid;
+  uint32_t kmin, kmax, T;
+  chunk_stats<E>(u, sh, n_valid, kmin, kmax);
   int shift, r_eq;
-  bool need;
-  plan(gm.k, n_valid, T, shift, r_eq, need);
-  auto get = [&](int i) -> uint32_t { return score_key(ws_s[i]); };
-  if (need) radix_select(get, n, gm.k, sh, T, shift, r_eq);
+  if (!plan_trivial(gm.k, n_valid, T, shift, r_eq)) radix_select<E>(u, kmin, kmax, gm.k, sh, T, shift, r_eq);
+  const int i0 = threadIdx.x * E;
   int32_t* out = a.idx + (int64_t)r * a.out_ld + (a.mode == SEL_RAW ? 0 : a.n_sink);
-  const int cnt =
-      compact(get, n, T, shift, r_eq, sh, [&](int o, int i, uint32_t) { out[o] = ws_p[i]; });
+  const int cnt = compact<E>(u, T, shift, r_eq, sh, [&](int o, int e) { out[o] = ws_p[i0 + e]; });
   finalize(a, r, gm, cnt);
+}
+
+int chunk_e(int64_t max_nc) {
+  if (max_nc <= SEL_NT * 4) return 4;
+  if (max_nc <= SEL_NT * 16) return 16;
+  return 32;
+}
+
+template <int E>
+hipError_t launch_e(const SelectArgs& a, hipStream_t st) {
+  constexpr int CH = SEL_NT * E;
+  dim3 ga(a.n_rows, max(a.max_chunks, 1));
+  hipLaunchKernelGGL((select_stage_a<E>), ga, dim3(SEL_NT), 0, st, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || a.max_chunks <= 1) return e;
+  // survivors of one row: max_chunks * k_cap
+  const int64_t nb = (int64_t)a.max_chunks * a.k_cap;
+  if (nb <= SEL_NT * 4) hipLaunchKernelGGL((select_stage_b<4>), dim3(a.n_rows), dim3(SEL_NT), 0, st, a, CH);
+  else if (nb <= SEL_NT * 16) hipLaunchKernelGGL((select_stage_b<16>), dim3(a.n_rows), dim3(SEL_NT), 0, st, a, CH);
+  else hipLaunchKernelGGL((select_stage_b<32>), dim3(a.n_rows), dim3(SEL_NT), 0, st, a, CH);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+int select_chunks(int64_t max_nc) {
+  const int64_t ch = (int64_t)SEL_NT * chunk_e(max_nc);
+  return (int)(max_nc <= ch ? 1 : (max_nc + ch - 1) / ch);
+}
+
+void select_plan(SelectArgs& a, int64_t max_nc) {
+  a.chunk_e = chunk_e(max_nc);
+  a.max_chunks = select_chunks(max_nc);
 }
 
 size_t select_ws_bytes(int n_rows, int max_chunks, int k_cap) {
@@ -309,14 +406,15 @@ void select_bind_ws(SelectArgs& a, void* ws, int n_rows) {
   a.ws_pos = a.ws_score + (size_t)n_rows * a.max_chunks * a.k_cap;
 }
 
+// max_chunks must equal select_chunks(max candidates per row) and the stage-B
+// survivor count max_chunks * k_cap must fit 32 * 1024 entries.
 hipError_t launch_select(const SelectArgs& a, hipStream_t st) {
   if (a.n_rows <= 0) return hipSuccess;
-  dim3 ga(a.n_rows, max(a.max_chunks, 1));
-  hipLaunchKernelGGL(select_stage_a, ga, dim3(SEL_NT), 0, st, a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess || a.max_chunks <= 1) return e;
-  hipLaunchKernelGGL(select_stage_b, dim3(a.n_rows), dim3(SEL_NT), 0, st, a);
-  return hipGetLastError();
+  if (a.max_chunks > 1 && (int64_t)a.max_chunks * a.k_cap > kSelMaxSurvivors) return hipErrorInvalidValue;
+  const int E = a.chunk_e;
+  if (E == 4) return launch_e<4>(a, st);
+  if (E == 16) return launch_e<16>(a, st);
+  return launch_e<32>(a, st);
 }
 
 }  // namespace lsa

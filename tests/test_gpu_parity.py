@@ -98,15 +98,18 @@ def test_index_score_decode_and_full_causal():
 
 
 # ------------------------------------------------------------------ selection
+@pytest.mark.parametrize("n_k,hi", [(20000, 50), (70000, 50), (70000, 1 << 24)])
 @pytest.mark.parametrize("cfg", [(4, 64, 300), (0, 0, 50), (4, 0, 1000), (1, 16, 0), (4, 512, 9000),
                                  (4, 512, 1532)])
-def test_select_given_scores_ties_and_chunks(cfg):
+def test_select_given_scores_ties_and_chunks(cfg, n_k, hi):
+    """20000 candidates fit one chunk; 70000 take the two-stage path. Scores
+    drawn from [0, 50) tie heavily; from [0, 2^24) they need several digits."""
     n_sink, W, kd = cfg
-    say(f"select scores-given cfg={cfg}")
-    B, n_q, n_k = 2, 6, 20000  # rows of ~20k candidates: two-stage path
+    say(f"select scores-given cfg={cfg} n_k={n_k} hi={hi}")
+    B, n_q = 2, 3
     g = torch.Generator(device=DEV)
     g.manual_seed(77)
-    scores = torch.randint(0, 50, (B, n_q, n_k), dtype=torch.int32, generator=g, device=DEV)  # many ties
+    scores = torch.randint(0, hi, (B, n_q, n_k), dtype=torch.int32, generator=g, device=DEV)
     q_off = n_k - n_q
     idx, n_sel = L.lsa_select_topk(scores=scores, n_sink=n_sink, n_window=W, k_dyn=kd, q_off=q_off)
     idx2, n_sel2 = L.lsa_select_topk(scores=scores, n_sink=n_sink, n_window=W, k_dyn=kd, q_off=q_off)
