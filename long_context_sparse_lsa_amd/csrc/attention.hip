@@ -29,6 +29,7 @@ namespace lsa {
 constexpr int kD = 128;
 constexpr int kVStride = 72;                 // bytes per V^T row in LDS (32 keys + pad)
 constexpr int kVLds = kD * kVStride;         // bytes per wave
+constexpr float kSlack = 8.f;                // softmax reference slack, log2 units
 
 template <int NB>
 struct AttnState {
@@ -65,42 +66,63 @@ __device__ __forceinline__ void load_q(const uint16_t* qrow, int h0, int H, v8bf
   }
 }
 
-// Attend the wave's rows over keys ids[kb .. ke) of one sequence.
+// K rows of one 32-key block for the A operand (lane = key, 8 dims per
+// register group).
+__device__ __forceinline__ void gather_k(const uint16_t* K, int pos, int n_k, v8bf (&k)[8]) {
+  const int g = lane_id() >> 5;
+  const bool valid = (unsigned)pos < (unsigned)n_k;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) k[j] = valid ? load_v8bf(K + (int64_t)pos * kD + g * 64 + 8 * j) : v8bf{};
+}
+
+// V rows of keys 4kg..4kg+3 of the block, dims 16dc..16dc+15 (for the LDS
+// transpose).
+__device__ __forceinline__ void gather_v(const uint16_t* V, int pos, int n_k, v4u (&v)[4][2]) {
+  const int l = lane_id();
+  const int kg = l >> 3, dc = l & 7;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int pe = __shfl(pos, 4 * kg + e, 64);
+    const bool ve = (unsigned)pe < (unsigned)n_k;
+    const v4u* src = (const v4u*)(V + (int64_t)pe * kD + 16 * dc);
+    v[e][0] = ve ? src[0] : v4u{0, 0, 0, 0};
+    v[e][1] = ve ? src[1] : v4u{0, 0, 0, 0};
+  }
+}
+
+// Attend the wave's rows over keys ids[kb .. ke) of one sequence. The K rows
+// of block i + 1 and the positions of block i + 2 are in flight while block i
+// is computed; block i's V rows are requested before its QK^T products.
 template <int NB>
 __device__ void attn_keys(const v8bf (&Q)[NB][8], const uint16_t* K, const uint16_t* V,
                           const int32_t* ids, int kb, int ke, int n_k, float sl2,
                           AttnState<NB>& st, char* vlds) {
   const int l = lane_id(), g = l >> 5, c = l & 31;
   const int kg = l >> 3, dc = l & 7;
+  auto pos_at = [&](int s0) { return s0 + c < ke ? ids[s0 + c] : -1; };
+  v8bf Kc[8], Kn[8];
+  int pos = kb < ke ? pos_at(kb) : -1;
+  if (kb < ke) gather_k(K, pos, n_k, Kc);
+  int pos_n = kb + 32 < ke ? pos_at(kb + 32) : -1;
   for (int s0 = kb; s0 < ke; s0 += 32) {
-    const int kk = s0 + c;
-    const int pos = kk < ke ? ids[kk] : -1;
+    const bool has_next = s0 + 32 < ke;
+    v4u Vr[4][2];
+    gather_v(V, pos, n_k, Vr);
+    int pos_nn = -1;
+    if (has_next) {
+      gather_k(K, pos_n, n_k, Kn);
+      if (s0 + 64 < ke) pos_nn = pos_at(s0 + 64);
+    }
     const bool valid = (unsigned)pos < (unsigned)n_k;
     const uint32_t vmask = (uint32_t)__ballot(valid);
 
     // ---- S^T = K * Q^T
-    v8bf Ka[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j)
-      Ka[j] = valid ? load_v8bf(K + (int64_t)pos * kD + g * 64 + 8 * j) : v8bf{};
-
-    // V rows of keys 4kg..4kg+3, dims 16dc..16dc+15 (issued early)
-    v4u Vr[4][2];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int pe = __shfl(pos, 4 * kg + e, 64);
-      const bool ve = (unsigned)pe < (unsigned)n_k;
-      const v4u* src = (const v4u*)(V + (int64_t)pe * kD + 16 * dc);
-      Vr[e][0] = ve ? src[0] : v4u{0, 0, 0, 0};
-      Vr[e][1] = ve ? src[1] : v4u{0, 0, 0, 0};
-    }
-
     v16f S[NB];
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
       S[nb] = v16f{};
 #pragma unroll
-      for (int j = 0; j < 8; ++j) S[nb] = mfma_bf16_32x32x16(Ka[j], Q[nb][j], S[nb]);
+      for (int j = 0; j < 8; ++j) S[nb] = mfma_bf16_32x32x16(Kc[j], Q[nb][j], S[nb]);
     }
 
     // ---- V^T into LDS: dim-major rows of 32 keys
@@ -118,40 +140,56 @@ __device__ void attn_keys(const v8bf (&Q)[NB][8], const uint16_t* K, const uint1
       *(v2u*)(vlds + (d0 + 1) * kVStride + kg * 8) = v2u{hi01, hi23};
     }
 
-    // ---- online softmax (base 2), per head = per lane
-    v8bf P[NB][2];
+    // ---- softmax numerators in base 2 against a per-head reference st.m:
+    // p = 2^(S * sl2 - m). The reference moves up only when a block's max
+    // exceeds it by more than kSlack, so p < 2^kSlack and the O / l rescale
+    // is rare; o / l does not depend on the reference. l is kept per lane
+    // half (16 of the 32 keys) and the halves are added at the end.
+    const bool full = (uint32_t)vmask == 0xffffffffu;
+    float mx[NB];
+    bool need = false;
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
-      float z[16];
-      float mx = -INFINITY;
+      float m = -INFINITY;
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const int kt = 8 * (i >> 2) + 4 * g + (i & 3);
-        z[i] = ((vmask >> kt) & 1u) ? S[nb][i] * sl2 : -INFINITY;
-        mx = fmaxf(mx, z[i]);
+        m = fmaxf(m, (full || ((vmask >> kt) & 1u)) ? S[nb][i] : -INFINITY);
       }
-      mx = fmaxf(mx, shfl_xor_f(mx, 32));
-      const float mnew = fmaxf(st.m[nb], mx);
-      const float mref = mnew == -INFINITY ? 0.f : mnew;
-      const float alpha = exp2f(st.m[nb] - mref);
+      mx[nb] = fmaxf(m, shfl_xor_f(m, 32)) * sl2;
+      need = need || mx[nb] > st.m[nb] + kSlack;
+    }
+    if (__any(need)) {
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        const float mnew = mx[nb] > st.m[nb] + kSlack ? mx[nb] : st.m[nb];
+        const float alpha = __builtin_amdgcn_exp2f(st.m[nb] - mnew);  // 0 when st.m is -inf
+        st.l[nb] *= alpha;
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb) st.o[mb][nb] *= alpha;
+        st.m[nb] = mnew;
+      }
+    }
+    v8bf P[NB][2];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      const float nm = -st.m[nb];
       float rs = 0.f;
       float p[16];
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        p[i] = exp2f(z[i] - mref);
+        const int kt = 8 * (i >> 2) + 4 * g + (i & 3);
+        p[i] = __builtin_amdgcn_exp2f(fmaf(S[nb][i], sl2, nm));
+        if (!full) p[i] = ((vmask >> kt) & 1u) ? p[i] : 0.f;
         rs += p[i];
       }
-      rs += shfl_xor_f(rs, 32);
-      st.l[nb] = st.l[nb] * alpha + rs;
-      st.m[nb] = mnew;
-#pragma unroll
-      for (int mb = 0; mb < 4; ++mb) st.o[mb][nb] *= alpha;
+      st.l[nb] += rs;
 #pragma unroll
       for (int js = 0; js < 2; ++js) {
-        v4u u;
+        v8bf x;
 #pragma unroll
-        for (int w2 = 0; w2 < 4; ++w2) u[w2] = pack_bf16x2(p[8 * js + 2 * w2], p[8 * js + 2 * w2 + 1]);
-        P[nb][js] = __builtin_bit_cast(v8bf, u);
+        for (int e = 0; e < 8; ++e) x[e] = (__bf16)p[8 * js + e];
+        P[nb][js] = x;
       }
     }
 
@@ -169,6 +207,12 @@ __device__ void attn_keys(const v8bf (&Q)[NB][8], const uint16_t* K, const uint1
         for (int nb = 0; nb < NB; ++nb) st.o[mb][nb] = mfma_bf16_32x32x16(Va, P[nb][js], st.o[mb][nb]);
       }
     }
+    if (has_next) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) Kc[j] = Kn[j];
+    }
+    pos = pos_n;
+    pos_n = pos_nn;
   }
 }
 
@@ -192,6 +236,8 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(PrefillArgs a) {
   const uint16_t* K = a.k + (int64_t)b * a.n_k * kD;
   const uint16_t* V = a.v + (int64_t)b * a.n_k * kD;
   attn_keys<NB>(Q, K, V, a.idx + gq * a.K_tot, 0, n, a.n_k, a.sl2, st, vlds_all + wv * kVLds);
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) st.l[nb] += shfl_xor_f(st.l[nb], 32);  // both key halves
 
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
@@ -249,6 +295,8 @@ __global__ __launch_bounds__(256) void attn_decode_partial(DecodeArgs a) {
   const uint16_t* K = a.k + (int64_t)b * a.n_k * kD;
   const uint16_t* V = a.v + (int64_t)b * a.n_k * kD;
   attn_keys<NB>(Q, K, V, a.idx + ibase * a.K_tot, kb, ke, a.n_k, a.sl2, st, vlds_all + wv * kVLds);
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) st.l[nb] += shfl_xor_f(st.l[nb], 32);  // both key halves
 
   const int64_t pbase = ((int64_t)b * a.n_split + split) * R;
 #pragma unroll
