@@ -1,15 +1,18 @@
 #!/usr/bin/env python3
 """Benchmark of the LSA hot path on one MI355X.
 
-Default workload: prefill, 1 sequence of L = 32768 tokens (indexer H_I=64,
-d_I=128 int8; 4 sinks + 512 window + top-k to 2048 keys; 64 query heads on one
-bf16 KV head, head dim 128). One step = fused indexer scoring + top-k selection
-for every row, then sparse attention for every row. Inputs are synthetic,
-seeded, and resident in HBM before timing starts.
+Default workload (--config c2): prefill of one sequence of L = 32768 tokens;
+indexer H_I = 64 heads, d_I = 128, int8; 4 sinks + 512-token window + top-k
+to 2048 keys; 64 query heads on one bf16 KV head of dim 128. One step =
+fused indexer scoring + top-k selection for every row (lsa_select_topk),
+then sparse attention for every row and layer (lsa_sparse_attn_prefill).
+Decode workloads (--config c3 / c4) time one decode step: selection for
+the target row of every sequence, then split-KV attention with the merge.
 
-Prints ONE JSON line with throughput, the roofline of the dominant call
-(timed live with HIP events on the stream the kernels run on), and the CPU
-oracle timed on a bounded sample of the same workload.
+Inputs are synthetic and seeded, and resident in HBM before timing starts.
+Prints ONE JSON line: throughput, per-call times measured with HIP events on
+the stream the kernels run on, the roofline of the dominant call, and the
+CPU oracle timed on a bounded sample of the same workload.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--config c2]
 """
@@ -22,9 +25,9 @@ import time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-PEAK_I8_TOPS = 5000.0      # MI355X dense int8
-PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16
-PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
+PEAK_I8_TOPS = 5000.0      # MI355X dense int8, TOP/s
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16, TFLOP/s
+PEAK_HBM_GBS = 8000.0      # MI355X HBM3E, GB/s
 
 
 def parse():
@@ -34,21 +37,23 @@ def parse():
     p.add_argument("--warmup", type=int, default=2)
     p.add_argument("--config", default="c2", choices=["c1", "c2", "c3", "c4", "c5"])
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--cpu-rows", type=int, default=0, help="oracle sample size (0: automatic)")
+    p.add_argument("--cpu-seconds", type=float, default=10.0, help="time budget of the oracle sample")
     return p.parse_args()
 
 
 def candidate_pairs(L, n_sink, W, K_tot):
     """Scored (query, key) pairs of a causal prefill: rows t >= K_tot score
     the candidates n_sink..t-W; shorter rows keep every key unscored."""
-    s = 0
-    for t in range(K_tot, L):
-        s += t - W - n_sink + 1
-    return s
+    n = L - K_tot
+    if n <= 0:
+        return 0
+    first = K_tot - W - n_sink + 1
+    return n * first + n * (n - 1) // 2
 
 
 class EventTimer:
-    """HIP events on the current stream around each call of a named part."""
+    """HIP events recorded on torch's current stream (the stream the binding
+    passes to the library) around each call of a named part."""
 
     def __init__(self, torch):
         self.torch = torch
@@ -79,22 +84,35 @@ def cpu_threads():
     return len(os.sched_getaffinity(0))
 
 
-def prefill_cpu_baseline(wl, q_idx, k_idx, w, q, k, v, rows):
-    """The oracle on `rows` sampled query rows: scoring, selection, attention."""
+def roofline(bound, name, kernels, work, ms, peak, unit):
+    """work: ops (unit T*/s) or bytes (unit GB/s) of one call; ms: mean call time."""
+    achieved = work / (ms * 1e-3) / (1e9 if unit == "GB/s" else 1e12)
+    return {"bound": bound, "kernel": name, "kernels": kernels, "achieved": round(achieved, 2), "peak": peak,
+            "unit": unit, "frac": round(achieved / peak, 4), "traffic": None,
+            "work_per_call": work, "ms_per_call": round(ms, 4)}
+
+
+def prefill_cpu_baseline(wl, q_idx, k_idx, w, q, k, v, seconds):
+    """The oracle on query rows drawn uniformly from [K_tot, L) until `seconds`
+    pass: scoring against every earlier key, selection, attention per layer."""
     import numpy as np
     import oracle as O
+    rng = np.random.default_rng(5)
     qn = q_idx[0].cpu().numpy()
     kn = k_idx[0].cpu().numpy()
     kf, vf = k[0].cpu().double().numpy(), v[0].cpu().double().numpy()
-    qrows = {t: q[0, t].cpu().double().numpy() for t in rows}
+    n = 0
     t0 = time.perf_counter()
-    for t in rows:
+    while time.perf_counter() - t0 < seconds:
+        t = int(rng.integers(wl.K_tot, wl.L))
         S = O.index_scores(qn[t:t + 1], kn[: t + 1], w, q_off=t)[0]
         sel = O.select_flat(S, t, wl.n_sink, wl.n_window, wl.k_dyn)
+        qt = q[0, t].cpu().double().numpy()
         for _ in range(wl.n_layers):
-            O.attend(qrows[t], kf, vf, sel, wl.scale)
+            O.attend(qt, kf, vf, sel, wl.scale)
+        n += 1
     dt = time.perf_counter() - t0
-    return len(rows) / dt, dt
+    return n / dt, n, dt
 
 
 def run_prefill(args, wl, torch):
@@ -108,7 +126,7 @@ def run_prefill(args, wl, torch):
 
     def step(tm):
         idx, n_sel = tm("select", L.lsa_select_topk, q_idx, k_idx, w, wl.n_sink, wl.n_window, wl.k_dyn, q_off=0)
-        for q, k, v in layers:
+        for q, k, v in layers:   # every layer reuses the one index (CLI)
             tm("attn", L.lsa_sparse_attn_prefill, q, k, v, idx, n_sel)
         return idx, n_sel
 
@@ -129,18 +147,16 @@ def run_prefill(args, wl, torch):
     i8_ops = 2.0 * wl.H_I * wl.d_I * pairs
     n_sel_sum = float(n_sel.sum().item())
     attn_flop = 4.0 * wl.H * wl.D * n_sel_sum
+    gathered = 2.0 * wl.D * 2 * n_sel_sum
     sel_tops = i8_ops / (sel_ms * 1e-3) / 1e12
     attn_tflops = attn_flop / (attn_ms * 1e-3) / 1e12
-    if sel_ms * 1 >= attn_ms * wl.n_layers:
-        roof = {"bound": "mfma", "kernel": "lsa_select_topk (fused int8 indexer + top-k)",
-                "achieved": round(sel_tops, 2), "peak": PEAK_I8_TOPS, "unit": "TFLOP/s",
-                "frac": round(sel_tops / PEAK_I8_TOPS, 4), "traffic": None,
-                "work_per_launch": f"{i8_ops:.4e} int8 op (2*H_I*d_I per scored pair)"}
+    if sel_ms >= attn_ms * wl.n_layers:  # the call that takes most of the step
+        roof = roofline("mfma", "lsa_select_topk",
+                        "index_prefill_kernel (int8 MFMA scores) + select_stage_a/b (top-k)",
+                        i8_ops, sel_ms, PEAK_I8_TOPS, "TOP/s")
     else:
-        roof = {"bound": "mfma", "kernel": "lsa_sparse_attn_prefill (bf16)",
-                "achieved": round(attn_tflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4), "traffic": None,
-                "work_per_launch": f"{attn_flop:.4e} flop (4*H*D per selected key)"}
+        roof = roofline("mfma", "lsa_sparse_attn_prefill", "attn_prefill_kernel (bf16 MFMA on gathered K/V)",
+                        attn_flop, attn_ms, PEAK_BF16_TFLOPS, "TFLOP/s")
     out = {
         "metric": "LSA prefill tokens/s",
         "value": round(wl.L / (ms_step * 1e-3), 1),
@@ -148,27 +164,47 @@ def run_prefill(args, wl, torch):
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(ms_step, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "int8+bf16", "data": "synthetic",
+        "dtype": "int8+bf16", "data": "synthetic (seeded int8 U[lo,hi] indexer, bf16 N(0,1) q/k/v)",
         "config": {"workload": wl.name, "global_batch": wl.B, "seq_len": wl.L, "layers": wl.n_layers,
                    "H_I": wl.H_I, "d_I": wl.d_I, "H": wl.H, "D": wl.D,
                    "n_sink": wl.n_sink, "n_window": wl.n_window, "K_tot": wl.K_tot, "parallelism": "none"},
         "parts": {"select_ms": round(sel_ms, 4), "select_int8_tops": round(sel_tops, 1),
+                  "scored_pairs": pairs,
                   "attn_ms_per_layer": round(attn_ms, 4), "attn_bf16_tflops": round(attn_tflops, 1),
-                  "attn_calls": n_attn},
+                  "attn_gather_gbs": round(gathered / (attn_ms * 1e-3) / 1e9, 1)},
         "roofline": roof,
     }
     if not args.no_cpu_baseline:
-        import numpy as np
-        n_rows = args.cpu_rows or (8 if wl.L >= 100000 else 24)
-        rng = np.random.default_rng(5)
-        rows = sorted(int(x) for x in rng.integers(wl.K_tot, wl.L, n_rows))
         q, k, v = layers[0]
-        rate, dt = prefill_cpu_baseline(wl, q_idx, k_idx, w, q, k, v, rows)
+        rate, n, dt = prefill_cpu_baseline(wl, q_idx, k_idx, w, q, k, v, args.cpu_seconds)
         out["cpu_baseline"] = {"value": round(rate, 3), "unit": "tokens/s", "cores": cpu_threads(),
                                "kind": "oracle",
-                               "sample": f"{len(rows)} rows drawn uniformly from [{wl.K_tot}, {wl.L}), "
-                                         f"full score+select+{wl.n_layers}x attention per row, {dt:.1f} s"}
+                               "sample": f"{n} query rows drawn uniformly from [{wl.K_tot}, {wl.L}) in {dt:.1f} s; "
+                                         f"each: exact scores against all earlier keys, top-k, "
+                                         f"{wl.n_layers}x float64 attention"}
     return out
+
+
+def decode_cpu_baseline(wl, q_idx, k_idx, w, q, kc, vc, seconds, blk_summary):
+    """The oracle on whole sequences of the decode step until `seconds` pass."""
+    import numpy as np
+    import oracle as O
+    n = 0
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds and n < wl.B:
+        b = n
+        kn = k_idx[b].cpu().numpy()
+        qn = q_idx[b].cpu().numpy()
+        if wl.blk:
+            sel = O.hier_select(qn, kn, blk_summary[b].cpu().numpy(), w, wl.blk, wl.n_blk_recall,
+                                wl.n_sink, wl.n_window, wl.k_dyn)
+        else:
+            sel = O.decode_select(qn, kn, w, wl.n_sink, wl.n_window, wl.k_dyn)
+        O.attend(q[b].reshape(-1, wl.D).cpu().double().numpy(), kc[b].cpu().double().numpy(),
+                 vc[b].cpu().double().numpy(), sel, wl.scale)
+        n += 1
+    dt = time.perf_counter() - t0
+    return n, dt
 
 
 def run_decode(args, wl, torch):
@@ -191,6 +227,7 @@ def run_decode(args, wl, torch):
         else:
             idx, n_sel = tm("select", L.lsa_select_topk, q1, k_idx, w, wl.n_sink, wl.n_window, wl.k_dyn,
                             q_off=N - 1)
+        # the n_q rows of a sequence (target + MTP drafts) share the one index (CLI)
         return tm("attn", L.lsa_sparse_attn_decode, q, kc, vc, idx, n_sel, n_split=wl.n_split)
 
     plain = lambda name, fn, *a, **kw: fn(*a, **kw)  # noqa: E731
@@ -213,23 +250,34 @@ def run_decode(args, wl, torch):
     else:
         idx_bytes = wl.B * N * wl.d_I
     step_bytes = idx_bytes + kv_bytes + qo_bytes
-    sel_gbs = idx_bytes / (sel_ms * 1e-3) / 1e9
+    if sel_ms >= attn_ms:
+        roof = roofline("hbm", "lsa_hier_select" if wl.blk else "lsa_select_topk",
+                        "index_score_kernel (indexer key scan) + select_stage_a/b", idx_bytes, sel_ms,
+                        PEAK_HBM_GBS, "GB/s")
+    else:
+        roof = roofline("hbm", "lsa_sparse_attn_decode", "attn_decode_partial + attn_decode_merge",
+                        kv_bytes + qo_bytes, attn_ms, PEAK_HBM_GBS, "GB/s")
     out = {
         "metric": "LSA decode us/step",
         "value": round(us_step, 2), "unit": "us/step",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(us_step / 1e3, 5),
         "higher_is_better": False, "scaling": "weak", "vs_baseline": None,
-        "dtype": "int8+bf16", "data": "synthetic",
+        "dtype": "int8+bf16", "data": "synthetic (seeded int8 U[-16,15] indexer, bf16 N(0,1) q and caches)",
         "config": {"workload": wl.name, "global_batch": wl.B, "context": N, "n_q": wl.n_q, "H": wl.H,
                    "K_tot": K_tot, "n_split": wl.n_split, "hier_blk": wl.blk, "parallelism": "none"},
         "parts": {"select_us": round(sel_ms * 1e3, 2), "attn_us": round(attn_ms * 1e3, 2),
-                  "step_bytes": step_bytes, "step_hbm_frac": round(step_bytes / (us_step * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)},
-        "roofline": {"bound": "hbm", "kernel": "decode select (indexer key scan + top-k)",
-                     "achieved": round(sel_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": round(sel_gbs / PEAK_HBM_GBS, 4), "traffic": None,
-                     "work_per_launch": f"{idx_bytes} B of indexer keys"},
+                  "step_bytes": step_bytes,
+                  "step_hbm_frac": round(step_bytes / (us_step * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)},
+        "roofline": roof,
     }
+    if not args.no_cpu_baseline:
+        n, dt = decode_cpu_baseline(wl, q_idx, k_idx, w, q, kc, vc, args.cpu_seconds, kblk)
+        out["cpu_baseline"] = {"value": round(dt / max(n, 1) * wl.B * 1e6, 1), "unit": "us/step",
+                               "cores": cpu_threads(), "kind": "oracle",
+                               "sample": f"{n} of {wl.B} sequences in {dt:.1f} s, scaled to the batch; "
+                                         f"each: exact scores and selection, float64 attention of "
+                                         f"{wl.n_q} rows"}
     return out
 
 

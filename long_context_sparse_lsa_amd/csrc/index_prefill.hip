@@ -6,23 +6,31 @@
 // head weights, int32 result -- is fixed by this library.)
 //
 // GEMM view: M = (query, head) rows, N = keys, K = d_I. A workgroup of 4 waves
-// owns 4 * QW queries and walks a chunk of keys in tiles of 128 keys that are
-// staged once in LDS and read by all four waves (each key byte feeds
-// 4 * QW * H_I multiply-adds). A wave keeps its QW queries (QW * H_I rows) in
-// registers as the A operand for the whole chunk.
+// (one per SIMD) owns 16 consecutive queries, 4 per wave, and walks a chunk
+// of keys in tiles of 128 keys that are staged once in LDS (double-buffered)
+// and read by all four waves. A wave keeps its 4 queries' rows (4 * H_I rows)
+// in registers as the A operand for the whole chunk, so every 16-byte LDS
+// read of the key operand feeds 4 * H_I / 32 MFMAs.
+//
+// Per 32-key block a wave runs, for each of its 4 queries, H_I/32 * d_I/32
+// MFMAs and a ReLU / head-sum epilogue on the VALU. The MFMA pipe and the
+// VALU overlap across waves, not within one: two workgroups share a CU, so
+// each SIMD holds two waves and one's epilogue runs under the other's MFMAs.
 //
 // Weight folding: w[h] * max(0, x) == max(0, w[h] * x) for w[h] >= 0, and
 // (w[h] q) . k == w[h] (q . k). When every weight is >= 0 and every product
-// w[h] * q[t, h, d] of a wave's rows fits int8, the wave multiplies the
+// w[h] * q[t, h, d] of the wave's queries fits int8, the wave multiplies the
 // weights into its A operand once, and the epilogue is a plain sum of ReLUs
 // (max + three-input add). Otherwise the wave keeps q as is and applies the
-// weights in the epilogue (max + 24-bit multiply-add). Both are exact, so the
-// choice never changes a score.
+// weights in the epilogue (max + 24-bit multiply-add, weights read from LDS).
+// Both are exact, so the choice never changes a score.
 //
 // Output layout of the 32x32x32 int8 MFMA: lane l holds key column l % 32 and
 // rows 8 * (i / 4) + 4 * (l / 32) + i % 4 of register i. A query owns H_I
-// consecutive rows, i.e. H_I / 32 whole M-blocks, so its head sum is a
-// per-lane sum over those blocks plus one exchange between lane halves.
+// consecutive rows (H_I / 32 whole M-blocks), so its head sum is a per-lane
+// sum plus one exchange between lane halves. Queries are finished in pairs:
+// lane half g ends up with query 2p + g's sums, and one 64-lane store writes
+// both queries' 32 scores.
 #include "lsa_device.h"
 #include "lsa_internal.h"
 
@@ -31,16 +39,19 @@ namespace lsa {
 namespace {
 
 constexpr int kTileKeys = 128;  // keys per LDS tile
-constexpr int kQW = 2;          // queries per wave
 constexpr int kWaves = 4;
-constexpr int kQT = kQW * kWaves;  // queries per workgroup
+constexpr int kQW = 4;                   // queries per wave
+constexpr int kQT = kWaves * kQW;        // queries per workgroup
+constexpr int kThreads = 64 * kWaves;
+constexpr int kChunkKeys = 4096;         // keys per workgroup
+constexpr int kBlocks = kTileKeys / 32;  // 32-key blocks per tile
 
 template <int DI>
 struct TileGeom {
   static constexpr int kRow = DI + 16;                 // padded LDS row: conflict-free b128 reads
   static constexpr int kBytes = kTileKeys * kRow;      // one stage
-  static constexpr int kChunks = kTileKeys * DI / 16;  // 16-byte pieces per tile
-  static constexpr int kPerThread = kChunks / (64 * kWaves);
+  static constexpr int kPieces = kTileKeys * DI / 16;  // 16-byte pieces per tile
+  static constexpr int kPerThread = kPieces / kThreads;
 };
 
 // True iff w times each of the 16 int8 values of v stays in [-128, 127].
@@ -72,6 +83,50 @@ __device__ __forceinline__ v4i scale_bytes(v4i v, int w) {
   return r;
 }
 
+// Lane-partial head sum of one 32-key block (this lane's rows, key l % 32).
+// Unfolded, the weights of this lane's rows come from LDS (wl holds w[h];
+// rows 8*(i/4) + 4*g + i%4 of block mb are four consecutive heads).
+template <int MB, bool FOLD>
+__device__ __forceinline__ int head_sum(const v16i (&acc)[MB], const int* wl) {
+  int s = 0;
+  if constexpr (FOLD) {
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int i = 0; i < 16; i += 2) s = s + max(acc[mb][i], 0) + max(acc[mb][i + 1], 0);
+  } else {
+    const int g = lane_id() >> 5;
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4) {
+        const v4i w4 = *(const v4i*)(wl + 32 * mb + 8 * i4 + 4 * g);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) s += __mul24(max(acc[mb][4 * i4 + e], 0), w4[e]);
+      }
+  }
+  return s;
+}
+
+template <int MB, int KS>
+__device__ __forceinline__ void block_mfma(const v4i (&A)[MB][KS], const v4i (&Bk)[KS], v16i (&acc)[MB]) {
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) acc[mb] = v16i{};
+#pragma unroll
+  for (int j = 0; j < KS; ++j)
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) acc[mb] = mfma_i8_32x32x32(A[mb][j], Bk[j], acc[mb]);
+}
+
+template <int DI, int KS>
+__device__ __forceinline__ void read_b(const char* tile, int nb, v4i (&Bk)[KS]) {
+  using G = TileGeom<DI>;
+  const int l = lane_id(), g = l >> 5, c = l & 31;
+#pragma unroll
+  for (int j = 0; j < KS; ++j) Bk[j] = *(const v4i*)(tile + (32 * nb + c) * G::kRow + g * (DI / 2) + 16 * j);
+}
+
+// Scores of this wave's queries row0 .. row0+3 against keys [v_begin, v_end).
 template <int HI, int DI, bool FOLD>
 __device__ __forceinline__ void score_chunk(const ScoreArgs& a, const v4i (&A)[kQW][HI / 32][DI / 32],
                                             const int* wl, const int8_t* kb, char* lds, int v_begin,
@@ -80,34 +135,24 @@ __device__ __forceinline__ void score_chunk(const ScoreArgs& a, const v4i (&A)[k
   constexpr int MB = HI / 32, KS = DI / 32;
   const int tid = threadIdx.x;
   const int l = lane_id(), g = l >> 5, c = l & 31;
-  // per-register head weights (rows 8*(i/4) + 4*g + i%4 of block mb); only
-  // the unfolded epilogue needs them
-  int W[MB][16];
-#pragma unroll
-  for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) W[mb][i] = FOLD ? 0 : wl[32 * mb + 8 * (i / 4) + 4 * g + (i % 4)];
-  // The two queries of this wave sit at rows row0 and row0 + 1; lane half g
-  // stores row row0 + g.
-  const int my_row = row0 + g;
-  const int vis_hi_row = a.mask_off + my_row;                 // last visible key of my row
-  const int vis_hi_wave = a.mask_off + min(row0 + kQW - 1, a.n_q - 1);
+  const int vis_lo_wave = a.mask_off + row0;  // last key visible to every query of the wave
+  const bool rows_ok = row0 + kQW <= a.n_q;
 
   // global -> register prefetch of one tile
   v4i pf[G::kPerThread];
   auto fetch = [&](int v0) {
 #pragma unroll
     for (int u = 0; u < G::kPerThread; ++u) {
-      const int id = tid + u * 64 * kWaves;
+      const int id = tid + u * kThreads;
       const int key = id / (DI / 16), part = id % (DI / 16);
-      const int v = v0 + key;
-      pf[u] = v < v_end ? *(const v4i*)(kb + (int64_t)v * DI + part * 16) : v4i{0, 0, 0, 0};
+      const int v = min(v0 + key, v_end - 1);  // clamped: keys past v_end are never stored
+      pf[u] = *(const v4i*)(kb + (int64_t)v * DI + part * 16);
     }
   };
   auto stash = [&](char* stage) {
 #pragma unroll
     for (int u = 0; u < G::kPerThread; ++u) {
-      const int id = tid + u * 64 * kWaves;
+      const int id = tid + u * kThreads;
       const int key = id / (DI / 16), part = id % (DI / 16);
       *(v4i*)(stage + key * G::kRow + part * 16) = pf[u];
     }
@@ -121,50 +166,56 @@ __device__ __forceinline__ void score_chunk(const ScoreArgs& a, const v4i (&A)[k
     const bool more = v0 + kTileKeys < v_end;
     if (more) fetch(v0 + kTileKeys);
     const char* tile = lds + stage * G::kBytes;
+    // every key of the tile visible to every query of the wave
+    const bool fast = rows_ok && v0 >= a.pos_lo && v0 + kTileKeys <= v_end && v0 + kTileKeys - 1 <= vis_lo_wave;
+    if (fast) {
+      // per block: each query's MFMAs and epilogue in turn, one 64-lane store
+      // per pair of queries; the other wave on the SIMD fills the MFMA pipe
+#pragma unroll
+      for (int nb = 0; nb < kBlocks; ++nb) {
+        v4i Bk[KS];
+        read_b<DI, KS>(tile, nb, Bk);
+#pragma unroll
+        for (int qp = 0; qp < kQW; qp += 2) {
+          v16i acc[MB];
+          block_mfma<MB, KS>(A[qp], Bk, acc);
+          const int s0 = head_sum<MB, FOLD>(acc, wl);
+          block_mfma<MB, KS>(A[qp + 1], Bk, acc);
+          const int s1 = head_sum<MB, FOLD>(acc, wl);
+          // half g keeps query qp + g's own partial and receives the other half's
+          const int recv = shfl_xor_i(g ? s0 : s1, 32);
+          sc[(int64_t)(row0 + qp + g) * a.ld + v0 + 32 * nb + c] = (g ? s1 : s0) + recv;
+        }
+      }
+    } else {
 #pragma unroll 1
-    for (int nb = 0; nb < kTileKeys / 32; ++nb) {
-      const int p0 = v0 + 32 * nb;  // first key of the block
-      if (p0 >= v_end) break;
-      const int v = p0 + c;
-      const bool blk_vis = p0 <= vis_hi_wave && p0 + 31 >= a.pos_lo;
-      if (!blk_vis) {
-        if (a.fill_masked && my_row < a.n_q && v < v_end) sc[(int64_t)my_row * a.ld + v] = kMasked;
-        continue;
-      }
-      v4i Bk[KS];
+      for (int nb = 0; nb < kBlocks; ++nb) {
+        const int p0 = v0 + 32 * nb;  // first key of the block
+        if (p0 >= v_end) break;
+        const int v = p0 + c;
+        v4i Bk[KS];
+        read_b<DI, KS>(tile, nb, Bk);
 #pragma unroll
-      for (int j = 0; j < KS; ++j) Bk[j] = *(const v4i*)(tile + (32 * nb + c) * G::kRow + g * (DI / 2) + 16 * j);
-      int part[kQW];
-#pragma unroll
-      for (int q = 0; q < kQW; ++q) {
-        v16i acc[MB];
-#pragma unroll
-        for (int mb = 0; mb < MB; ++mb) acc[mb] = v16i{};
-#pragma unroll
-        for (int j = 0; j < KS; ++j)
-#pragma unroll
-          for (int mb = 0; mb < MB; ++mb) acc[mb] = mfma_i8_32x32x32(A[q][mb][j], Bk[j], acc[mb]);
-        int s = 0;
-#pragma unroll
-        for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-          for (int i = 0; i < 16; i += 2) {
-            if constexpr (FOLD) {
-              s = s + max(acc[mb][i], 0) + max(acc[mb][i + 1], 0);
-            } else {
-              s += __mul24(max(acc[mb][i], 0), W[mb][i]) + __mul24(max(acc[mb][i + 1], 0), W[mb][i + 1]);
-            }
+        for (int qp = 0; qp < kQW; qp += 2) {
+          // the two queries of this pair; lane half g stores row0 + qp + g
+          const int rowA = row0 + qp, row = rowA + g;
+          const bool vis_any = rowA < a.n_q && p0 <= a.mask_off + rowA + 1 && p0 + 31 >= a.pos_lo;
+          int full = kMasked;
+          if (vis_any) {
+            v16i acc[MB];
+            block_mfma<MB, KS>(A[qp], Bk, acc);
+            const int s0 = head_sum<MB, FOLD>(acc, wl);
+            block_mfma<MB, KS>(A[qp + 1], Bk, acc);
+            const int s1 = head_sum<MB, FOLD>(acc, wl);
+            const int recv = shfl_xor_i(g ? s0 : s1, 32);
+            full = (g ? s1 : s0) + recv;
           }
-        part[q] = s;
-      }
-      // lane half g finishes query g: it keeps its own part of query g and
-      // receives the other half's part of query g
-      const int send = g ? part[0] : part[1];
-      const int recv = shfl_xor_i(send, 32);
-      const int full = (g ? part[1] : part[0]) + recv;
-      if (my_row < a.n_q && v < v_end) {
-        if (v >= a.pos_lo && v <= vis_hi_row) sc[(int64_t)my_row * a.ld + v] = full;
-        else if (a.fill_masked) sc[(int64_t)my_row * a.ld + v] = kMasked;
+          if (row < a.n_q && v < v_end) {
+            int32_t* dst = sc + (int64_t)row * a.ld + v;
+            if (v >= a.pos_lo && v <= a.mask_off + row) *dst = full;
+            else if (a.fill_masked) *dst = kMasked;
+          }
+        }
       }
     }
     if (more) {
@@ -176,64 +227,64 @@ __device__ __forceinline__ void score_chunk(const ScoreArgs& a, const v4i (&A)[k
 }
 
 template <int HI, int DI>
-__global__ __launch_bounds__(256, 2) void index_prefill_kernel(ScoreArgs a, int KC, int fold_ok) {
+__global__ __launch_bounds__(kThreads, 2) void index_prefill_kernel(ScoreArgs a, int fold_ok) {
   using G = TileGeom<DI>;
   constexpr int MB = HI / 32, KS = DI / 32;
   __shared__ __attribute__((aligned(16))) char lds[2 * G::kBytes];
-  __shared__ int wl[HI];
+  __shared__ __attribute__((aligned(16))) int wl[HI];
   const int chunk = blockIdx.x, qt = blockIdx.y, b = blockIdx.z;
   const int q0 = qt * kQT;
-  const int v_begin = chunk * KC;
-  const int v_end = min(v_begin + KC, a.n_keys);
+  const int v_begin = chunk * kChunkKeys;
+  const int v_end = min(v_begin + kChunkKeys, a.n_keys);
   const int last_row = min(q0 + kQT, a.n_q) - 1;
   int32_t* sc = a.scores + (int64_t)b * a.s_bstride;
   const int l = lane_id(), g = l >> 5, c = l & 31;
-  const int wv = wave_id();
 
-  // whole chunk invisible to every row of the tile
+  // whole chunk invisible to every row of the workgroup
   if (v_begin > a.mask_off + last_row || v_end <= a.pos_lo) {
     if (a.fill_masked) {
       for (int r = q0; r <= last_row; ++r)
-        for (int v = v_begin + threadIdx.x; v < v_end; v += 256) sc[(int64_t)r * a.ld + v] = kMasked;
+        for (int v = v_begin + threadIdx.x; v < v_end; v += kThreads) sc[(int64_t)r * a.ld + v] = kMasked;
     }
     return;
   }
   if (threadIdx.x < HI) wl[threadIdx.x] = a.w.w[threadIdx.x];
   __syncthreads();
 
-  const int row0 = q0 + wv * kQW;
+  const int row0 = q0 + kQW * wave_id();
   v4i A[kQW][MB][KS];
   const int8_t* qb = a.q + (int64_t)b * a.q_bstride;
 #pragma unroll
-  for (int q = 0; q < kQW; ++q)
+  for (int q = 0; q < kQW; ++q) {
+    const int qrow = min(row0 + q, a.n_q - 1);  // rows past n_q compute on a valid row, store nothing
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
-      const int row = row0 + q, h = 32 * mb + c;
-      const v4i* src = (const v4i*)(qb + ((int64_t)row * HI + h) * DI + g * (DI / 2));
+      const v4i* src = (const v4i*)(qb + ((int64_t)qrow * HI + 32 * mb + c) * DI + g * (DI / 2));
 #pragma unroll
-      for (int j = 0; j < KS; ++j) A[q][mb][j] = row < a.n_q ? src[j] : v4i{0, 0, 0, 0};
+      for (int j = 0; j < KS; ++j) A[q][mb][j] = src[j];
     }
+  }
   // fold the weights into A when that is exact for every row of the wave
   bool ok = fold_ok != 0;
 #pragma unroll
-  for (int q = 0; q < kQW; ++q)
+  for (int mb = 0; mb < MB; ++mb) {
+    const int wh = wl[32 * mb + c];
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb) {
-      const int wh = wl[32 * mb + c];
+    for (int q = 0; q < kQW; ++q)
 #pragma unroll
       for (int j = 0; j < KS; ++j) ok = ok && bytes_scale_fit(A[q][mb][j], wh);
-    }
+  }
   const bool fold = __all(ok);
   const int8_t* kb = a.k + (int64_t)b * a.k_bstride;
   if (fold) {
 #pragma unroll
-    for (int q = 0; q < kQW; ++q)
+    for (int mb = 0; mb < MB; ++mb) {
+      const int wh = wl[32 * mb + c];
 #pragma unroll
-      for (int mb = 0; mb < MB; ++mb) {
-        const int wh = wl[32 * mb + c];
+      for (int q = 0; q < kQW; ++q)
 #pragma unroll
         for (int j = 0; j < KS; ++j) A[q][mb][j] = scale_bytes(A[q][mb][j], wh);
-      }
+    }
     score_chunk<HI, DI, true>(a, A, wl, kb, lds, v_begin, v_end, row0, sc);
   } else {
     score_chunk<HI, DI, false>(a, A, wl, kb, lds, v_begin, v_end, row0, sc);
@@ -242,19 +293,16 @@ __global__ __launch_bounds__(256, 2) void index_prefill_kernel(ScoreArgs a, int 
 
 template <int HI, int DI>
 hipError_t launch_t(const ScoreArgs& a, int fold_ok, hipStream_t st) {
-  // keys per workgroup: long enough to amortise the A load, short enough to
-  // give the chip many workgroups
-  const int KC = 1024;
-  dim3 grid((a.n_keys + KC - 1) / KC, (a.n_q + kQT - 1) / kQT, a.B);
-  hipLaunchKernelGGL((index_prefill_kernel<HI, DI>), grid, dim3(256), 0, st, a, KC, fold_ok);
+  dim3 grid((a.n_keys + kChunkKeys - 1) / kChunkKeys, (a.n_q + kQT - 1) / kQT, a.B);
+  hipLaunchKernelGGL((index_prefill_kernel<HI, DI>), grid, dim3(kThreads), 0, st, a, fold_ok);
   return hipGetLastError();
 }
 
 }  // namespace
 
 bool index_prefill_supported(const ScoreArgs& a) {
-  return a.blocks == nullptr && (a.H_I == 32 || a.H_I == 64) &&
-         (a.d_I == 64 || a.d_I == 128) && a.n_q >= kQT;
+  return a.blocks == nullptr && (a.H_I == 32 || a.H_I == 64) && (a.d_I == 64 || a.d_I == 128) &&
+         a.n_q >= kQT;
 }
 
 hipError_t launch_index_prefill(const ScoreArgs& a, hipStream_t st) {
