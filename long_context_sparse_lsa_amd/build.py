@@ -27,9 +27,11 @@ CFLAGS = [
 ]
 
 
-# Per-file flags. The prefill indexer keeps its MFMA accumulators in
-# ordinary VGPRs, which its VALU epilogue reads directly.
-FILE_FLAGS = {"index_prefill.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+# Per-file flags. The indexer and attention kernels keep their MFMA
+# accumulators in ordinary VGPRs, which their VALU epilogues read directly
+# (no copies between accumulation and vector registers in the loops).
+_VGPR_FORM = ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]
+FILE_FLAGS = {"index_prefill.hip": _VGPR_FORM, "attention.hip": _VGPR_FORM}
 
 
 def sources():

@@ -67,54 +67,84 @@ __device__ __forceinline__ void load_q(const uint16_t* qrow, int h0, int H, v8bf
 }
 
 // K rows of one 32-key block for the A operand (lane = key, 8 dims per
-// register group).
+// register group). A key outside [0, n_k) loads row 0 instead: its score is
+// set to -inf and its probability to 0 before use, so only finiteness
+// matters, and the loads need no masking.
 __device__ __forceinline__ void gather_k(const uint16_t* K, int pos, int n_k, v8bf (&k)[8]) {
   const int g = lane_id() >> 5;
-  const bool valid = (unsigned)pos < (unsigned)n_k;
+  const int p = (unsigned)pos < (unsigned)n_k ? pos : 0;
 #pragma unroll
-  for (int j = 0; j < 8; ++j) k[j] = valid ? load_v8bf(K + (int64_t)pos * kD + g * 64 + 8 * j) : v8bf{};
+  for (int j = 0; j < 8; ++j) k[j] = load_v8bf(K + (int64_t)p * kD + g * 64 + 8 * j);
 }
 
 // V rows of keys 4kg..4kg+3 of the block, dims 16dc..16dc+15 (for the LDS
-// transpose).
+// transpose); invalid keys load row 0 (their probability is 0).
 __device__ __forceinline__ void gather_v(const uint16_t* V, int pos, int n_k, v4u (&v)[4][2]) {
   const int l = lane_id();
   const int kg = l >> 3, dc = l & 7;
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
     const int pe = __shfl(pos, 4 * kg + e, 64);
-    const bool ve = (unsigned)pe < (unsigned)n_k;
-    const v4u* src = (const v4u*)(V + (int64_t)pe * kD + 16 * dc);
-    v[e][0] = ve ? src[0] : v4u{0, 0, 0, 0};
-    v[e][1] = ve ? src[1] : v4u{0, 0, 0, 0};
+    const int p = (unsigned)pe < (unsigned)n_k ? pe : 0;
+    const v4u* src = (const v4u*)(V + (int64_t)p * kD + 16 * dc);
+    v[e][0] = src[0];
+    v[e][1] = src[1];
   }
 }
 
-// Attend the wave's rows over keys ids[kb .. ke) of one sequence. The K rows
-// of block i + 1 and the positions of block i + 2 are in flight while block i
-// is computed; block i's V rows are requested before its QK^T products.
+// V^T of one 32-key block into a per-wave LDS buffer: dim-major rows of 32
+// keys (4x4 register transposes, 8-byte writes). Lane (kg, dc) holds the V
+// rows of keys 4kg..4kg+3, dims 16dc..16dc+15.
+__device__ __forceinline__ void write_vt(const v4u (&Vr)[4][2], char* vlds) {
+  const int l = lane_id();
+  const int kg = l >> 3, dc = l & 7;
+#pragma unroll
+  for (int x = 0; x < 8; ++x) {
+    uint32_t w[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) w[e] = Vr[e][x >> 2][x & 3];
+    const uint32_t lo01 = (w[0] & 0xffffu) | (w[1] << 16);
+    const uint32_t lo23 = (w[2] & 0xffffu) | (w[3] << 16);
+    const uint32_t hi01 = (w[0] >> 16) | (w[1] & 0xffff0000u);
+    const uint32_t hi23 = (w[2] >> 16) | (w[3] & 0xffff0000u);
+    const int d0 = 16 * dc + 2 * x;
+    *(v2u*)(vlds + d0 * kVStride + kg * 8) = v2u{lo01, lo23};
+    *(v2u*)(vlds + (d0 + 1) * kVStride + kg * 8) = v2u{hi01, hi23};
+  }
+}
+
+// Attend the wave's rows over keys ids[kb .. ke) of one sequence. The gathers
+// run one block ahead: while block i is computed, the K rows of block i + 1
+// are loaded into registers and its V rows are loaded and then transposed
+// into the second of two per-wave LDS buffers (vlds holds 2 * kVLds bytes),
+// so the gather latency hides under a whole block of work.
 template <int NB>
 __device__ void attn_keys(const v8bf (&Q)[NB][8], const uint16_t* K, const uint16_t* V,
                           const int32_t* ids, int kb, int ke, int n_k, float sl2,
                           AttnState<NB>& st, char* vlds) {
   const int l = lane_id(), g = l >> 5, c = l & 31;
-  const int kg = l >> 3, dc = l & 7;
   auto pos_at = [&](int s0) { return s0 + c < ke ? ids[s0 + c] : -1; };
   v8bf Kc[8], Kn[8];
+  v4u Vn[4][2];
   int pos = kb < ke ? pos_at(kb) : -1;
-  if (kb < ke) gather_k(K, pos, n_k, Kc);
   int pos_n = kb + 32 < ke ? pos_at(kb + 32) : -1;
+  if (kb < ke) {
+    gather_k(K, pos, n_k, Kc);
+    gather_v(V, pos, n_k, Vn);
+    write_vt(Vn, vlds);
+  }
+  int buf = 0;
   for (int s0 = kb; s0 < ke; s0 += 32) {
     const bool has_next = s0 + 32 < ke;
-    v4u Vr[4][2];
-    gather_v(V, pos, n_k, Vr);
     int pos_nn = -1;
     if (has_next) {
       gather_k(K, pos_n, n_k, Kn);
+      gather_v(V, pos_n, n_k, Vn);
       if (s0 + 64 < ke) pos_nn = pos_at(s0 + 64);
     }
     const bool valid = (unsigned)pos < (unsigned)n_k;
     const uint32_t vmask = (uint32_t)__ballot(valid);
+    const char* vcur = vlds + buf * kVLds;
 
     // ---- S^T = K * Q^T
     v16f S[NB];
@@ -125,37 +155,29 @@ __device__ void attn_keys(const v8bf (&Q)[NB][8], const uint16_t* K, const uint1
       for (int j = 0; j < 8; ++j) S[nb] = mfma_bf16_32x32x16(Kc[j], Q[nb][j], S[nb]);
     }
 
-    // ---- V^T into LDS: dim-major rows of 32 keys
-#pragma unroll
-    for (int x = 0; x < 8; ++x) {
-      uint32_t w[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) w[e] = Vr[e][x >> 2][x & 3];
-      const uint32_t lo01 = (w[0] & 0xffffu) | (w[1] << 16);
-      const uint32_t lo23 = (w[2] & 0xffffu) | (w[3] << 16);
-      const uint32_t hi01 = (w[0] >> 16) | (w[1] & 0xffff0000u);
-      const uint32_t hi23 = (w[2] >> 16) | (w[3] & 0xffff0000u);
-      const int d0 = 16 * dc + 2 * x;
-      *(v2u*)(vlds + d0 * kVStride + kg * 8) = v2u{lo01, lo23};
-      *(v2u*)(vlds + (d0 + 1) * kVStride + kg * 8) = v2u{hi01, hi23};
-    }
-
     // ---- softmax numerators in base 2 against a per-head reference st.m:
     // p = 2^(S * sl2 - m). The reference moves up only when a block's max
     // exceeds it by more than kSlack, so p < 2^kSlack and the O / l rescale
     // is rare; o / l does not depend on the reference. l is kept per lane
     // half (16 of the 32 keys) and the halves are added at the end.
     const bool full = (uint32_t)vmask == 0xffffffffu;
+    if (!full) {
+      // a block with invalid keys (the ragged tail): scores to -inf
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int kt = 8 * (i >> 2) + 4 * g + (i & 3);
+          if (!((vmask >> kt) & 1u)) S[nb][i] = -INFINITY;
+        }
+    }
     float mx[NB];
     bool need = false;
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
-      float m = -INFINITY;
+      float m = S[nb][0];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int kt = 8 * (i >> 2) + 4 * g + (i & 3);
-        m = fmaxf(m, (full || ((vmask >> kt) & 1u)) ? S[nb][i] : -INFINITY);
-      }
+      for (int i = 1; i < 16; ++i) m = fmaxf(m, S[nb][i]);
       mx[nb] = fmaxf(m, shfl_xor_f(m, 32)) * sl2;
       need = need || mx[nb] > st.m[nb] + kSlack;
     }
@@ -170,33 +192,31 @@ __device__ void attn_keys(const v8bf (&Q)[NB][8], const uint16_t* K, const uint1
         st.m[nb] = mnew;
       }
     }
+    // p = 2^(S*sl2 - m) (exp2 of -inf is 0); l sums p in fp32, and P is
+    // rounded to bf16 for the PV product
     v8bf P[NB][2];
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
       const float nm = -st.m[nb];
       float rs = 0.f;
-      float p[16];
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int kt = 8 * (i >> 2) + 4 * g + (i & 3);
-        p[i] = __builtin_amdgcn_exp2f(fmaf(S[nb][i], sl2, nm));
-        if (!full) p[i] = ((vmask >> kt) & 1u) ? p[i] : 0.f;
-        rs += p[i];
-      }
-      st.l[nb] += rs;
 #pragma unroll
       for (int js = 0; js < 2; ++js) {
         v8bf x;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) x[e] = (__bf16)p[8 * js + e];
+        for (int e = 0; e < 8; ++e) {
+          const float p = __builtin_amdgcn_exp2f(fmaf(S[nb][8 * js + e], sl2, nm));
+          rs += p;
+          x[e] = (__bf16)p;
+        }
         P[nb][js] = x;
       }
+      st.l[nb] += rs;
     }
 
     // ---- O^T += V^T * P^T
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb) {
-      const char* rowp = vlds + (32 * mb + c) * kVStride;
+      const char* rowp = vcur + (32 * mb + c) * kVStride;
 #pragma unroll
       for (int js = 0; js < 2; ++js) {
         const v2u a0 = *(const v2u*)(rowp + (16 * js + 4 * g) * 2);
@@ -208,9 +228,11 @@ __device__ void attn_keys(const v8bf (&Q)[NB][8], const uint16_t* K, const uint1
       }
     }
     if (has_next) {
+      write_vt(Vn, vlds + (buf ^ 1) * kVLds);
 #pragma unroll
       for (int j = 0; j < 8; ++j) Kc[j] = Kn[j];
     }
+    buf ^= 1;
     pos = pos_n;
     pos_n = pos_nn;
   }
@@ -219,7 +241,7 @@ __device__ void attn_keys(const v8bf (&Q)[NB][8], const uint16_t* K, const uint1
 // ------------------------------------------------------------------ prefill
 template <int NB>
 __global__ __launch_bounds__(256) void attn_prefill_kernel(PrefillArgs a) {
-  __shared__ __attribute__((aligned(16))) char vlds_all[4 * kVLds];
+  __shared__ __attribute__((aligned(16))) char vlds_all[4 * 2 * kVLds];
   const int wv = wave_id();
   const int HB = (a.H + 32 * NB - 1) / (32 * NB);
   const int64_t gi = (int64_t)blockIdx.x * 4 + wv;
@@ -235,7 +257,7 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(PrefillArgs a) {
   const int n = min(max(a.n_sel[gq], 0), a.K_tot);
   const uint16_t* K = a.k + (int64_t)b * a.n_k * kD;
   const uint16_t* V = a.v + (int64_t)b * a.n_k * kD;
-  attn_keys<NB>(Q, K, V, a.idx + gq * a.K_tot, 0, n, a.n_k, a.sl2, st, vlds_all + wv * kVLds);
+  attn_keys<NB>(Q, K, V, a.idx + gq * a.K_tot, 0, n, a.n_k, a.sl2, st, vlds_all + wv * 2 * kVLds);
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) st.l[nb] += shfl_xor_f(st.l[nb], 32);  // both key halves
 
@@ -274,7 +296,7 @@ hipError_t launch_attn_prefill(const PrefillArgs& a, hipStream_t st) {
 // R = n_q * H; o is unnormalised, m in base-2 units.
 template <int NB>
 __global__ __launch_bounds__(256) void attn_decode_partial(DecodeArgs a) {
-  __shared__ __attribute__((aligned(16))) char vlds_all[4 * kVLds];
+  __shared__ __attribute__((aligned(16))) char vlds_all[4 * 2 * kVLds];
   const int wv = wave_id();
   const int HB = (a.H + 32 * NB - 1) / (32 * NB);
   const int gi = blockIdx.x * 4 + wv;
@@ -294,7 +316,7 @@ __global__ __launch_bounds__(256) void attn_decode_partial(DecodeArgs a) {
   const int kb = min(n, split * cs), ke = min(n, (split + 1) * cs);
   const uint16_t* K = a.k + (int64_t)b * a.n_k * kD;
   const uint16_t* V = a.v + (int64_t)b * a.n_k * kD;
-  attn_keys<NB>(Q, K, V, a.idx + ibase * a.K_tot, kb, ke, a.n_k, a.sl2, st, vlds_all + wv * kVLds);
+  attn_keys<NB>(Q, K, V, a.idx + ibase * a.K_tot, kb, ke, a.n_k, a.sl2, st, vlds_all + wv * 2 * kVLds);
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) st.l[nb] += shfl_xor_f(st.l[nb], 32);  // both key halves
 
