@@ -27,8 +27,8 @@
 namespace lsa {
 
 constexpr int kD = 128;
-constexpr int kVStride = 72;                 // bytes per V^T row in LDS (32 keys + pad)
-constexpr int kVLds = kD * kVStride;         // bytes per wave
+constexpr int kVRow = 320;                   // bytes per V row in LDS: 256 + pad, conflict-free transposed reads
+constexpr int kVLds = 32 * kVRow;            // one 32-key block of V rows
 constexpr float kSlack = 8.f;                // softmax reference slack, log2 units
 
 template <int NB>
@@ -77,40 +77,42 @@ __device__ __forceinline__ void gather_k(const uint16_t* K, int pos, int n_k, v8
   for (int j = 0; j < 8; ++j) k[j] = load_v8bf(K + (int64_t)p * kD + g * 64 + 8 * j);
 }
 
-// V rows of keys 4kg..4kg+3 of the block, dims 16dc..16dc+15 (for the LDS
-// transpose); invalid keys load row 0 (their probability is 0).
-__device__ __forceinline__ void gather_v(const uint16_t* V, int pos, int n_k, v4u (&v)[4][2]) {
+// V rows of one 32-key block, 16 bytes per lane and load: load i of lane l
+// holds key 4i + l/16, bytes 16 * (l % 16) of its row. Invalid keys load row
+// 0 (their probability is 0).
+__device__ __forceinline__ void gather_v(const uint16_t* V, int pos, int n_k, v4u (&v)[8]) {
   const int l = lane_id();
-  const int kg = l >> 3, dc = l & 7;
 #pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const int pe = __shfl(pos, 4 * kg + e, 64);
+  for (int i = 0; i < 8; ++i) {
+    const int pe = __shfl(pos, 4 * i + (l >> 4), 64);
     const int p = (unsigned)pe < (unsigned)n_k ? pe : 0;
-    const v4u* src = (const v4u*)(V + (int64_t)p * kD + 16 * dc);
-    v[e][0] = src[0];
-    v[e][1] = src[1];
+    v[i] = *(const v4u*)(V + (int64_t)p * kD + 8 * (l & 15));
   }
 }
 
-// V^T of one 32-key block into a per-wave LDS buffer: dim-major rows of 32
-// keys (4x4 register transposes, 8-byte writes). Lane (kg, dc) holds the V
-// rows of keys 4kg..4kg+3, dims 16dc..16dc+15.
-__device__ __forceinline__ void write_vt(const v4u (&Vr)[4][2], char* vlds) {
+// The block's V rows into LDS, row-major (key rows of kVRow bytes).
+__device__ __forceinline__ void store_v(const v4u (&v)[8], char* vlds) {
   const int l = lane_id();
-  const int kg = l >> 3, dc = l & 7;
 #pragma unroll
-  for (int x = 0; x < 8; ++x) {
-    uint32_t w[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) w[e] = Vr[e][x >> 2][x & 3];
-    const uint32_t lo01 = (w[0] & 0xffffu) | (w[1] << 16);
-    const uint32_t lo23 = (w[2] & 0xffffu) | (w[3] << 16);
-    const uint32_t hi01 = (w[0] >> 16) | (w[1] & 0xffff0000u);
-    const uint32_t hi23 = (w[2] >> 16) | (w[3] & 0xffff0000u);
-    const int d0 = 16 * dc + 2 * x;
-    *(v2u*)(vlds + d0 * kVStride + kg * 8) = v2u{lo01, lo23};
-    *(v2u*)(vlds + (d0 + 1) * kVStride + kg * 8) = v2u{hi01, hi23};
-  }
+  for (int i = 0; i < 8; ++i) *(v4u*)(vlds + (4 * i + (l >> 4)) * kVRow + 16 * (l & 15)) = v[i];
+}
+
+// The V^T operand of the PV product for dims 32mb.. and key slice js, read
+// transposed from the row-major V block with two ds_read_b64_tr_b16. The
+// transposing read gives lane j of each 16-lane group element j % 4 of the
+// 8-byte pieces addressed by lanes j / 4 + 4s of the group (s = 0..3), so a
+// lane addresses key row 4(G / 2) + j / 4 (+ the slice and half offsets) at
+// dims 16(G % 2) + 4(j % 4) (G = lane / 16). Lane (g, c) then holds dim c of
+// keys 16js + 4g + {0..3} and 16js + 8 + 4g + {0..3}: the key order of the P^T
+// operand.
+typedef short v4s __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ v8bf read_vt(const char* vblk, int lane_off, int mb, int js) {
+  const char* p = vblk + lane_off + 16 * js * kVRow + 64 * mb;
+  const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s*)p);
+  const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s*)(p + 8 * kVRow));
+  const v4u u = v4u{__builtin_bit_cast(v2u, lo)[0], __builtin_bit_cast(v2u, lo)[1], __builtin_bit_cast(v2u, hi)[0],
+                    __builtin_bit_cast(v2u, hi)[1]};
+  return __builtin_bit_cast(v8bf, u);
 }
 
 // Attend the wave's rows over keys ids[kb .. ke) of one sequence. The gathers
@@ -125,13 +127,15 @@ __device__ void attn_keys(const v8bf (&Q)[NB][8], const uint16_t* K, const uint1
   const int l = lane_id(), g = l >> 5, c = l & 31;
   auto pos_at = [&](int s0) { return s0 + c < ke ? ids[s0 + c] : -1; };
   v8bf Kc[8], Kn[8];
-  v4u Vn[4][2];
+  v4u Vn[8];
+  const int G = l >> 4, jj = l & 15;
+  const int vt_off = (4 * (G >> 1) + (jj >> 2)) * kVRow + (16 * (G & 1) + 4 * (jj & 3)) * 2;
   int pos = kb < ke ? pos_at(kb) : -1;
   int pos_n = kb + 32 < ke ? pos_at(kb + 32) : -1;
   if (kb < ke) {
     gather_k(K, pos, n_k, Kc);
     gather_v(V, pos, n_k, Vn);
-    write_vt(Vn, vlds);
+    store_v(Vn, vlds);
   }
   int buf = 0;
   for (int s0 = kb; s0 < ke; s0 += 32) {
@@ -216,19 +220,15 @@ __device__ void attn_keys(const v8bf (&Q)[NB][8], const uint16_t* K, const uint1
     // ---- O^T += V^T * P^T
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb) {
-      const char* rowp = vcur + (32 * mb + c) * kVStride;
 #pragma unroll
       for (int js = 0; js < 2; ++js) {
-        const v2u a0 = *(const v2u*)(rowp + (16 * js + 4 * g) * 2);
-        const v2u a1 = *(const v2u*)(rowp + (16 * js + 4 * g + 8) * 2);
-        const v4u au = v4u{a0[0], a0[1], a1[0], a1[1]};
-        const v8bf Va = __builtin_bit_cast(v8bf, au);
+        const v8bf Va = read_vt(vcur, vt_off, mb, js);
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) st.o[mb][nb] = mfma_bf16_32x32x16(Va, P[nb][js], st.o[mb][nb]);
       }
     }
     if (has_next) {
-      write_vt(Vn, vlds + (buf ^ 1) * kVLds);
+      store_v(Vn, vlds + (buf ^ 1) * kVLds);
 #pragma unroll
       for (int j = 0; j < 8; ++j) Kc[j] = Kn[j];
     }
