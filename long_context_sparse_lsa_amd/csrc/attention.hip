@@ -27,8 +27,11 @@
 namespace lsa {
 
 constexpr int kD = 128;
+constexpr int kKRow = 272;                   // bytes per K row in LDS: 256 + pad, conflict-free 16-byte reads
 constexpr int kVRow = 320;                   // bytes per V row in LDS: 256 + pad, conflict-free transposed reads
-constexpr int kVLds = 32 * kVRow;            // one 32-key block of V rows
+constexpr int kVOff = 32 * kKRow;            // V rows follow the K rows of a block
+constexpr int kBlkLds = kVOff + 32 * kVRow;  // one 32-key block of K and V rows
+constexpr int kWaveLds = 2 * kBlkLds;        // two blocks per wave
 constexpr float kSlack = 8.f;                // softmax reference slack, log2 units
 
 template <int NB>
@@ -66,35 +69,36 @@ __device__ __forceinline__ void load_q(const uint16_t* qrow, int h0, int H, v8bf
   }
 }
 
-// K rows of one 32-key block for the A operand (lane = key, 8 dims per
-// register group). A key outside [0, n_k) loads row 0 instead: its score is
-// set to -inf and its probability to 0 before use, so only finiteness
-// matters, and the loads need no masking.
-__device__ __forceinline__ void gather_k(const uint16_t* K, int pos, int n_k, v8bf (&k)[8]) {
-  const int g = lane_id() >> 5;
-  const int p = (unsigned)pos < (unsigned)n_k ? pos : 0;
-#pragma unroll
-  for (int j = 0; j < 8; ++j) k[j] = load_v8bf(K + (int64_t)p * kD + g * 64 + 8 * j);
-}
+// K and V rows of one 32-key block, staged through registers on their way
+// to LDS: load i of lane l holds bytes 16 * (l % 16) of the rows of key
+// 4i + l/16. A key outside [0, n_k) loads row 0 instead: its score is set to
+// -inf and its probability to 0 before use, so only finiteness matters and
+// the loads need no masking.
+struct KVStage {
+  v4u k[8], v[8];
+};
 
-// V rows of one 32-key block, 16 bytes per lane and load: load i of lane l
-// holds key 4i + l/16, bytes 16 * (l % 16) of its row. Invalid keys load row
-// 0 (their probability is 0).
-__device__ __forceinline__ void gather_v(const uint16_t* V, int pos, int n_k, v4u (&v)[8]) {
+__device__ __forceinline__ void gather_kv(const uint16_t* K, const uint16_t* V, int pos, int n_k,
+                                          KVStage& s) {
   const int l = lane_id();
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const int pe = __shfl(pos, 4 * i + (l >> 4), 64);
-    const int p = (unsigned)pe < (unsigned)n_k ? pe : 0;
-    v[i] = *(const v4u*)(V + (int64_t)p * kD + 8 * (l & 15));
+    const int64_t p = (unsigned)pe < (unsigned)n_k ? pe : 0;
+    s.k[i] = *(const v4u*)(K + p * kD + 8 * (l & 15));
+    s.v[i] = *(const v4u*)(V + p * kD + 8 * (l & 15));
   }
 }
 
-// The block's V rows into LDS, row-major (key rows of kVRow bytes).
-__device__ __forceinline__ void store_v(const v4u (&v)[8], char* vlds) {
+// The staged rows into one LDS block buffer (K rows, then V rows).
+__device__ __forceinline__ void store_kv(const KVStage& s, char* blk) {
   const int l = lane_id();
 #pragma unroll
-  for (int i = 0; i < 8; ++i) *(v4u*)(vlds + (4 * i + (l >> 4)) * kVRow + 16 * (l & 15)) = v[i];
+  for (int i = 0; i < 8; ++i) {
+    const int key = 4 * i + (l >> 4);
+    *(v4u*)(blk + key * kKRow + 16 * (l & 15)) = s.k[i];
+    *(v4u*)(blk + kVOff + key * kVRow + 16 * (l & 15)) = s.v[i];
+  }
 }
 
 // The V^T operand of the PV product for dims 32mb.. and key slice js, read
@@ -115,49 +119,72 @@ __device__ __forceinline__ v8bf read_vt(const char* vblk, int lane_off, int mb, 
   return __builtin_bit_cast(v8bf, u);
 }
 
-// Attend the wave's rows over keys ids[kb .. ke) of one sequence. The gathers
-// run one block ahead: while block i is computed, the K rows of block i + 1
-// are loaded into registers and its V rows are loaded and then transposed
-// into the second of two per-wave LDS buffers (vlds holds 2 * kVLds bytes),
-// so the gather latency hides under a whole block of work.
+// Attend the wave's rows over keys ids[kb .. ke) of one sequence, 32 keys
+// per block. The block's K and V rows sit in one of two per-wave LDS buffers
+// (kWaveLds bytes at lds). Loads run two blocks ahead: while block i is
+// computed from its buffer, the rows of block i + 2 are in flight in one
+// register stage and those of block i + 1 (in flight since the previous
+// block) go from the other stage into the second buffer at the end.
+template <int NB>
+__device__ __forceinline__ void attn_block(const v8bf (&Q)[NB][8], const char* blk, int pos, int n_k,
+                                           float sl2, int vt_off, AttnState<NB>& st);
+
 template <int NB>
 __device__ void attn_keys(const v8bf (&Q)[NB][8], const uint16_t* K, const uint16_t* V,
                           const int32_t* ids, int kb, int ke, int n_k, float sl2,
-                          AttnState<NB>& st, char* vlds) {
-  const int l = lane_id(), g = l >> 5, c = l & 31;
-  auto pos_at = [&](int s0) { return s0 + c < ke ? ids[s0 + c] : -1; };
-  v8bf Kc[8], Kn[8];
-  v4u Vn[8];
+                          AttnState<NB>& st, char* lds) {
+  const int l = lane_id(), c = l & 31;
   const int G = l >> 4, jj = l & 15;
-  const int vt_off = (4 * (G >> 1) + (jj >> 2)) * kVRow + (16 * (G & 1) + 4 * (jj & 3)) * 2;
-  int pos = kb < ke ? pos_at(kb) : -1;
-  int pos_n = kb + 32 < ke ? pos_at(kb + 32) : -1;
-  if (kb < ke) {
-    gather_k(K, pos, n_k, Kc);
-    gather_v(V, pos, n_k, Vn);
-    store_v(Vn, vlds);
+  const int vt_off = kVOff + (4 * (G >> 1) + (jj >> 2)) * kVRow + (16 * (G & 1) + 4 * (jj & 3)) * 2;
+  auto pos_at = [&](int s0) { return s0 + c < ke ? ids[s0 + c] : -1; };
+  if (kb >= ke) return;
+  KVStage sa, sb;
+  int p0 = pos_at(kb), p1 = pos_at(kb + 32), p2 = pos_at(kb + 64);
+  gather_kv(K, V, p0, n_k, sa);
+  store_kv(sa, lds);
+  if (kb + 32 < ke) gather_kv(K, V, p1, n_k, sb);
+  // two blocks per trip so that the stages and buffers swap roles statically
+  for (int s0 = kb; s0 < ke; s0 += 64) {
+    {
+      const int p3 = pos_at(s0 + 96);
+      if (s0 + 64 < ke) gather_kv(K, V, p2, n_k, sa);
+      attn_block<NB>(Q, lds, p0, n_k, sl2, vt_off, st);
+      if (s0 + 32 < ke) store_kv(sb, lds + kBlkLds);
+      p0 = p1;
+      p1 = p2;
+      p2 = p3;
+    }
+    if (s0 + 32 < ke) {
+      const int p3 = pos_at(s0 + 128);
+      if (s0 + 96 < ke) gather_kv(K, V, p2, n_k, sb);
+      attn_block<NB>(Q, lds + kBlkLds, p0, n_k, sl2, vt_off, st);
+      if (s0 + 64 < ke) store_kv(sa, lds);
+      p0 = p1;
+      p1 = p2;
+      p2 = p3;
+    }
   }
-  int buf = 0;
-  for (int s0 = kb; s0 < ke; s0 += 32) {
-    const bool has_next = s0 + 32 < ke;
-    int pos_nn = -1;
-    if (has_next) {
-      gather_k(K, pos_n, n_k, Kn);
-      gather_v(V, pos_n, n_k, Vn);
-      if (s0 + 64 < ke) pos_nn = pos_at(s0 + 64);
-    }
-    const bool valid = (unsigned)pos < (unsigned)n_k;
-    const uint32_t vmask = (uint32_t)__ballot(valid);
-    const char* vcur = vlds + buf * kVLds;
+}
 
-    // ---- S^T = K * Q^T
-    v16f S[NB];
+// One 32-key block: scores, softmax update, PV product. pos: this lane's key
+// position (lane % 32); K and V rows in LDS at blk.
+template <int NB>
+__device__ __forceinline__ void attn_block(const v8bf (&Q)[NB][8], const char* blk, int pos, int n_k,
+                                           float sl2, int vt_off, AttnState<NB>& st) {
+  const int l = lane_id(), g = l >> 5, c = l & 31;
+  const bool valid = (unsigned)pos < (unsigned)n_k;
+  const uint32_t vmask = (uint32_t)__ballot(valid);
+
+  // ---- S^T = K * Q^T (A operand: key row c, dims g*64 + 8j from LDS)
+  v16f S[NB];
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-      S[nb] = v16f{};
+  for (int nb = 0; nb < NB; ++nb) S[nb] = v16f{};
 #pragma unroll
-      for (int j = 0; j < 8; ++j) S[nb] = mfma_bf16_32x32x16(Kc[j], Q[nb][j], S[nb]);
-    }
+  for (int j = 0; j < 8; ++j) {
+    const v8bf Ka = *(const v8bf*)(blk + c * kKRow + g * 128 + 16 * j);
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) S[nb] = mfma_bf16_32x32x16(Ka, Q[nb][j], S[nb]);
+  }
 
     // ---- softmax numerators in base 2 against a per-head reference st.m:
     // p = 2^(S * sl2 - m). The reference moves up only when a block's max
@@ -222,29 +249,26 @@ __device__ void attn_keys(const v8bf (&Q)[NB][8], const uint16_t* K, const uint1
     for (int mb = 0; mb < 4; ++mb) {
 #pragma unroll
       for (int js = 0; js < 2; ++js) {
-        const v8bf Va = read_vt(vcur, vt_off, mb, js);
+        const v8bf Va = read_vt(blk, vt_off, mb, js);
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) st.o[mb][nb] = mfma_bf16_32x32x16(Va, P[nb][js], st.o[mb][nb]);
       }
     }
-    if (has_next) {
-      store_v(Vn, vlds + (buf ^ 1) * kVLds);
-#pragma unroll
-      for (int j = 0; j < 8; ++j) Kc[j] = Kn[j];
-    }
-    buf ^= 1;
-    pos = pos_n;
-    pos_n = pos_nn;
-  }
 }
 
 // ------------------------------------------------------------------ prefill
 template <int NB>
 __global__ __launch_bounds__(256) void attn_prefill_kernel(PrefillArgs a) {
-  __shared__ __attribute__((aligned(16))) char vlds_all[4 * 2 * kVLds];
+  __shared__ __attribute__((aligned(16))) char lds_all[4 * kWaveLds];
   const int wv = wave_id();
   const int HB = (a.H + 32 * NB - 1) / (32 * NB);
-  const int64_t gi = (int64_t)blockIdx.x * 4 + wv;
+  // Workgroups go to the 8 XCDs round-robin; remap so that each XCD walks a
+  // contiguous range of query rows. Rows that run together on one XCD then
+  // share their SI windows and sinks in that XCD's L2.
+  // (The grid is a multiple of 8 workgroups; the map is a bijection on it.)
+  const int64_t per = gridDim.x / 8, bx = blockIdx.x;
+  const int64_t tile = (bx % 8) * per + bx / 8;
+  const int64_t gi = tile * 4 + wv;
   if (gi >= (int64_t)a.B * a.L * HB) return;
   const int64_t gq = gi / HB;
   const int hb = (int)(gi % HB);
@@ -257,7 +281,7 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(PrefillArgs a) {
   const int n = min(max(a.n_sel[gq], 0), a.K_tot);
   const uint16_t* K = a.k + (int64_t)b * a.n_k * kD;
   const uint16_t* V = a.v + (int64_t)b * a.n_k * kD;
-  attn_keys<NB>(Q, K, V, a.idx + gq * a.K_tot, 0, n, a.n_k, a.sl2, st, vlds_all + wv * 2 * kVLds);
+  attn_keys<NB>(Q, K, V, a.idx + gq * a.K_tot, 0, n, a.n_k, a.sl2, st, lds_all + wv * kWaveLds);
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) st.l[nb] += shfl_xor_f(st.l[nb], 32);  // both key halves
 
@@ -285,7 +309,7 @@ hipError_t launch_attn_prefill(const PrefillArgs& a, hipStream_t st) {
   const int NB = a.H <= 32 ? 1 : 2;
   const int HB = (a.H + 32 * NB - 1) / (32 * NB);
   const int64_t groups = (int64_t)a.B * a.L * HB;
-  dim3 grid((unsigned)((groups + 3) / 4));
+  dim3 grid((unsigned)(((groups + 3) / 4 + 7) / 8 * 8));
   if (NB == 1) hipLaunchKernelGGL(attn_prefill_kernel<1>, grid, dim3(256), 0, st, a);
   else hipLaunchKernelGGL(attn_prefill_kernel<2>, grid, dim3(256), 0, st, a);
   return hipGetLastError();
@@ -296,7 +320,7 @@ hipError_t launch_attn_prefill(const PrefillArgs& a, hipStream_t st) {
 // R = n_q * H; o is unnormalised, m in base-2 units.
 template <int NB>
 __global__ __launch_bounds__(256) void attn_decode_partial(DecodeArgs a) {
-  __shared__ __attribute__((aligned(16))) char vlds_all[4 * 2 * kVLds];
+  __shared__ __attribute__((aligned(16))) char lds_all[4 * kWaveLds];
   const int wv = wave_id();
   const int HB = (a.H + 32 * NB - 1) / (32 * NB);
   const int gi = blockIdx.x * 4 + wv;
@@ -316,7 +340,7 @@ __global__ __launch_bounds__(256) void attn_decode_partial(DecodeArgs a) {
   const int kb = min(n, split * cs), ke = min(n, (split + 1) * cs);
   const uint16_t* K = a.k + (int64_t)b * a.n_k * kD;
   const uint16_t* V = a.v + (int64_t)b * a.n_k * kD;
-  attn_keys<NB>(Q, K, V, a.idx + ibase * a.K_tot, kb, ke, a.n_k, a.sl2, st, vlds_all + wv * 2 * kVLds);
+  attn_keys<NB>(Q, K, V, a.idx + ibase * a.K_tot, kb, ke, a.n_k, a.sl2, st, lds_all + wv * kWaveLds);
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) st.l[nb] += shfl_xor_f(st.l[nb], 32);  // both key halves
 
