@@ -12,9 +12,13 @@
 //   O^T += V^T * P^T: A = V^T from LDS (lane = dim),   B = P^T (lane = head)
 // The S^T accumulator gives lane l the head l%32 and 16 keys; those are
 // exactly the keys the P^T operand of the second product needs in that lane,
-// so softmax probabilities go from accumulator to operand in place. The V
-// tile is transposed through a per-wave LDS buffer (4x4 register transposes,
-// 8-byte LDS writes and reads). Online softmax runs in fp32 in base 2.
+// so softmax probabilities go from accumulator to operand in place. K and V
+// rows of a block are staged row-major in LDS; the V^T operand comes from
+// transposing LDS reads. Online softmax runs in fp32 in base 2.
+//
+// Prefill gives each wave one query row and 64 heads. Decode gives each
+// wave 32 heads of one query row so that two waves fit on a SIMD, and the
+// waves that read the same index share one gather of each K/V block.
 //
 // Decode splits the selected list into n_split contiguous parts (the one-GPU
 // form of the KV-cache parallel decode of the "③ KVP 解码切分示意" section) and
@@ -70,32 +74,39 @@ __device__ __forceinline__ void load_q(const uint16_t* qrow, int h0, int H, v8bf
 }
 
 // K and V rows of one 32-key block, staged through registers on their way
-// to LDS: load i of lane l holds bytes 16 * (l % 16) of the rows of key
-// 4i + l/16. A key outside [0, n_k) loads row 0 instead: its score is set to
-// -inf and its probability to 0 before use, so only finiteness matters and
-// the loads need no masking.
+// to LDS, gathered by a group of TW waves that share the block: thread gt
+// of the group (gt = 64 * wave-in-group + lane) loads, for i < 8 / TW, the
+// 16 bytes at 16 * (gt % 16) of the K row and of the V row of key
+// gt / 16 + 4 * TW * i. A key outside [0, n_k) loads row 0 instead: its
+// score is set to -inf and its probability to 0 before use, so only
+// finiteness matters and the loads need no masking.
+template <int TW>
 struct KVStage {
-  v4u k[8], v[8];
+  v4u k[8 / TW], v[8 / TW];
 };
 
-__device__ __forceinline__ void gather_kv(const uint16_t* K, const uint16_t* V, int pos, int n_k,
-                                          KVStage& s) {
+// pos: lane c (and c + 32) holds the cache position of key c of the block.
+template <int TW>
+__device__ __forceinline__ void gather_kv(const uint16_t* K, const uint16_t* V, int pos, int n_k, int gw,
+                                          KVStage<TW>& s) {
   const int l = lane_id();
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int pe = __shfl(pos, 4 * i + (l >> 4), 64);
-    const int64_t p = (unsigned)pe < (unsigned)n_k ? pe : 0;
-    s.k[i] = *(const v4u*)(K + p * kD + 8 * (l & 15));
-    s.v[i] = *(const v4u*)(V + p * kD + 8 * (l & 15));
+  for (int i = 0; i < 8 / TW; ++i) {
+    const int key = 4 * gw + (l >> 4) + 4 * TW * i;
+    const int pe = __shfl(pos, key, 64);
+    const int64_t off = ((unsigned)pe < (unsigned)n_k ? (int64_t)pe : 0) * kD + 8 * (l & 15);
+    s.k[i] = *(const v4u*)(K + off);
+    s.v[i] = *(const v4u*)(V + off);
   }
 }
 
-// The staged rows into one LDS block buffer (K rows, then V rows).
-__device__ __forceinline__ void store_kv(const KVStage& s, char* blk) {
+// The staged pieces into one LDS block buffer (K rows, then V rows).
+template <int TW>
+__device__ __forceinline__ void store_kv(const KVStage<TW>& s, char* blk, int gw) {
   const int l = lane_id();
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int key = 4 * i + (l >> 4);
+  for (int i = 0; i < 8 / TW; ++i) {
+    const int key = 4 * gw + (l >> 4) + 4 * TW * i;
     *(v4u*)(blk + key * kKRow + 16 * (l & 15)) = s.k[i];
     *(v4u*)(blk + kVOff + key * kVRow + 16 * (l & 15)) = s.v[i];
   }
@@ -119,49 +130,97 @@ __device__ __forceinline__ v8bf read_vt(const char* vblk, int lane_off, int mb, 
   return __builtin_bit_cast(v8bf, u);
 }
 
-// Attend the wave's rows over keys ids[kb .. ke) of one sequence, 32 keys
-// per block. The block's K and V rows sit in one of two per-wave LDS buffers
-// (kWaveLds bytes at lds). Loads run two blocks ahead: while block i is
-// computed from its buffer, the rows of block i + 2 are in flight in one
-// register stage and those of block i + 1 (in flight since the previous
-// block) go from the other stage into the second buffer at the end.
 template <int NB>
 __device__ __forceinline__ void attn_block(const v8bf (&Q)[NB][8], const char* blk, int pos, int n_k,
                                            float sl2, int vt_off, AttnState<NB>& st);
 
-template <int NB>
-__device__ void attn_keys(const v8bf (&Q)[NB][8], const uint16_t* K, const uint16_t* V,
-                          const int32_t* ids, int kb, int ke, int n_k, float sl2,
+// Attend the wave's rows over keys ids[sb .. se), 32 keys per block, with
+// the block's K and V rows in one of two LDS buffers (kBlkLds bytes each at
+// lds) shared by the TW waves of a group (SYNC: a workgroup barrier orders
+// the buffers; a single-wave group needs none, its LDS accesses execute in
+// order). Gathers run R blocks ahead through a ring of R register stages:
+// step i issues the loads of block i + R, computes block i and moves block
+// i + 1 from its stage into the other buffer. No load sits under a branch
+// and no loaded value is used before it has to be (masking is applied at
+// use), so the memory counter waits only for the stage being moved, not for
+// the loads still in flight. trips: the number of steps, a multiple of R and at least
+// the number of blocks; the same for all waves that meet at barriers.
+template <int NB, int TW, int R, bool SYNC>
+__device__ void attn_keys(const v8bf (&Q)[NB][8], bool active, const uint16_t* K, const uint16_t* V,
+                          const int32_t* ids, int sb, int se, int trips, int n_k, float sl2, int gw,
                           AttnState<NB>& st, char* lds) {
+  static_assert(R % 2 == 0, "block parity selects the LDS buffer");
   const int l = lane_id(), c = l & 31;
   const int G = l >> 4, jj = l & 15;
   const int vt_off = kVOff + (4 * (G >> 1) + (jj >> 2)) * kVRow + (16 * (G & 1) + 4 * (jj & 3)) * 2;
-  auto pos_at = [&](int s0) { return s0 + c < ke ? ids[s0 + c] : -1; };
-  if (kb >= ke) return;
-  KVStage sa, sb;
-  int p0 = pos_at(kb), p1 = pos_at(kb + 32), p2 = pos_at(kb + 64);
-  gather_kv(K, V, p0, n_k, sa);
-  store_kv(sa, lds);
-  if (kb + 32 < ke) gather_kv(K, V, p1, n_k, sb);
-  // two blocks per trip so that the stages and buffers swap roles statically
-  for (int s0 = kb; s0 < ke; s0 += 64) {
-    {
-      const int p3 = pos_at(s0 + 96);
-      if (s0 + 64 < ke) gather_kv(K, V, p2, n_k, sa);
-      attn_block<NB>(Q, lds, p0, n_k, sl2, vt_off, st);
-      if (s0 + 32 < ke) store_kv(sb, lds + kBlkLds);
-      p0 = p1;
-      p1 = p2;
-      p2 = p3;
+  const int ilast = max(se - 1, 0);
+  auto raw_at = [&](int s0) { return ids[min(max(s0 + c, 0), ilast)]; };
+  auto eff = [&](int s0, int raw) { return s0 + c < se ? raw : -1; };
+  // The memory counter is in order: waiting for a position also waits for
+  // every gather issued before it. Positions are therefore loaded P blocks
+  // ahead, far enough that this never waits for a stage before it is due.
+  constexpr int P = R > 2 ? 2 * R - 2 : R;
+  KVStage<TW> stg[R];
+  int pr[P + 1];  // raw positions of blocks i .. i + P
+#pragma unroll
+  for (int j = 0; j <= P; ++j) pr[j] = raw_at(sb + 32 * j);
+#pragma unroll
+  for (int j = 0; j < R; ++j) gather_kv<TW>(K, V, eff(sb + 32 * j, pr[j]), n_k, gw, stg[j]);
+  store_kv<TW>(stg[0], lds, gw);
+  for (int it = 0; it < trips; it += R) {
+#pragma unroll
+    for (int u = 0; u < R; ++u) {
+      const int s0 = sb + 32 * (it + u);
+      if constexpr (SYNC) __syncthreads();  // block it+u in its buffer for all; the other buffer free
+      const int pnew = raw_at(s0 + 32 * (P + 1));
+      gather_kv<TW>(K, V, eff(s0 + 32 * R, pr[R]), n_k, gw, stg[u]);
+      if (active && s0 < se) attn_block<NB>(Q, lds + (u & 1) * kBlkLds, eff(s0, pr[0]), n_k, sl2, vt_off, st);
+      store_kv<TW>(stg[(u + 1) % R], lds + ((u + 1) & 1) * kBlkLds, gw);
+#pragma unroll
+      for (int j = 0; j < P; ++j) pr[j] = pr[j + 1];
+      pr[P] = pnew;
     }
-    if (s0 + 32 < ke) {
-      const int p3 = pos_at(s0 + 128);
-      if (s0 + 96 < ke) gather_kv(K, V, p2, n_k, sb);
-      attn_block<NB>(Q, lds + kBlkLds, p0, n_k, sl2, vt_off, st);
-      if (s0 + 64 < ke) store_kv(sa, lds);
-      p0 = p1;
-      p1 = p2;
-      p2 = p3;
+  }
+}
+
+// The same pipeline with the positions already in LDS (pos: the chunk's
+// positions, -1 from entry cnt on, readable up to entry 32 * (trips + R)).
+// The block loop then issues no global load but the gathers, so the memory
+// counter holds nothing else and a stage waits only on its own loads. Used
+// where positions would otherwise chain their load latency into every step.
+template <int TW>
+__device__ __forceinline__ void gather_kv_lds(const uint16_t* K, const uint16_t* V, const int* pb, int n_k, int gw,
+                                              KVStage<TW>& s) {
+  const int l = lane_id();
+#pragma unroll
+  for (int i = 0; i < 8 / TW; ++i) {
+    const int pe = pb[4 * gw + (l >> 4) + 4 * TW * i];
+    const int64_t off = ((unsigned)pe < (unsigned)n_k ? (int64_t)pe : 0) * kD + 8 * (l & 15);
+    s.k[i] = *(const v4u*)(K + off);
+    s.v[i] = *(const v4u*)(V + off);
+  }
+}
+
+template <int NB, int TW, int R>
+__device__ void attn_keys_lds(const v8bf (&Q)[NB][8], bool active, const uint16_t* K, const uint16_t* V,
+                              const int* pos, int cnt, int trips, int n_k, float sl2, int gw, AttnState<NB>& st,
+                              char* lds) {
+  static_assert(R % 2 == 0, "block parity selects the LDS buffer");
+  const int l = lane_id(), c = l & 31;
+  const int G = l >> 4, jj = l & 15;
+  const int vt_off = kVOff + (4 * (G >> 1) + (jj >> 2)) * kVRow + (16 * (G & 1) + 4 * (jj & 3)) * 2;
+  KVStage<TW> stg[R];
+#pragma unroll
+  for (int j = 0; j < R; ++j) gather_kv_lds<TW>(K, V, pos + 32 * j, n_k, gw, stg[j]);
+  store_kv<TW>(stg[0], lds, gw);
+  for (int it = 0; it < trips; it += R) {
+#pragma unroll
+    for (int u = 0; u < R; ++u) {
+      const int bi = it + u;
+      __syncthreads();  // block bi in its buffer for all; the other buffer free
+      gather_kv_lds<TW>(K, V, pos + 32 * (bi + R), n_k, gw, stg[u]);
+      if (active && 32 * bi < cnt) attn_block<NB>(Q, lds + (u & 1) * kBlkLds, pos[32 * bi + c], n_k, sl2, vt_off, st);
+      store_kv<TW>(stg[(u + 1) % R], lds + ((u + 1) & 1) * kBlkLds, gw);
     }
   }
 }
@@ -281,7 +340,10 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(PrefillArgs a) {
   const int n = min(max(a.n_sel[gq], 0), a.K_tot);
   const uint16_t* K = a.k + (int64_t)b * a.n_k * kD;
   const uint16_t* V = a.v + (int64_t)b * a.n_k * kD;
-  attn_keys<NB>(Q, K, V, a.idx + gq * a.K_tot, 0, n, a.n_k, a.sl2, st, lds_all + wv * kWaveLds);
+  constexpr int kR = 2;
+  const int trips = ((n + 31) / 32 + kR - 1) / kR * kR;
+  attn_keys<NB, 1, kR, false>(Q, true, K, V, a.idx + gq * a.K_tot, 0, n, trips, a.n_k, a.sl2, 0, st,
+                             lds_all + wv * kWaveLds);
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) st.l[nb] += shfl_xor_f(st.l[nb], 32);  // both key halves
 
@@ -318,87 +380,212 @@ hipError_t launch_attn_prefill(const PrefillArgs& a, hipStream_t st) {
 // ------------------------------------------------------------------ decode
 // Partials: ws_m / ws_l [B, n_split, R], ws_o [B, n_split, R, 128] with
 // R = n_q * H; o is unnormalised, m in base-2 units.
-template <int NB>
-__global__ __launch_bounds__(256) void attn_decode_partial(DecodeArgs a) {
-  __shared__ __attribute__((aligned(16))) char lds_all[4 * kWaveLds];
-  const int wv = wave_id();
-  const int HB = (a.H + 32 * NB - 1) / (32 * NB);
-  const int gi = blockIdx.x * 4 + wv;
-  if (gi >= a.n_q * HB) return;
-  const int qr = gi / HB, hb = gi % HB;
-  const int split = blockIdx.y, b = blockIdx.z;
-  const int l = lane_id(), g = l >> 5, c = l & 31;
-  const int R = a.n_q * a.H;
-  v8bf Q[NB][8];
-  load_q<NB>(a.q + ((int64_t)b * a.n_q + qr) * a.H * kD, hb * 32 * NB, a.H, Q);
-  AttnState<NB> st;
-  attn_init(st);
-  const int irow = a.n_idx == 1 ? 0 : qr;
-  const int64_t ibase = (int64_t)b * a.n_idx + irow;
-  const int n = min(max(a.n_sel[ibase], 0), a.K_tot);
-  const int cs = (n + a.n_split - 1) / a.n_split;
-  const int kb = min(n, split * cs), ke = min(n, (split + 1) * cs);
-  const uint16_t* K = a.k + (int64_t)b * a.n_k * kD;
-  const uint16_t* V = a.v + (int64_t)b * a.n_k * kD;
-  attn_keys<NB>(Q, K, V, a.idx + ibase * a.K_tot, kb, ke, a.n_k, a.sl2, st, lds_all + wv * kWaveLds);
-#pragma unroll
-  for (int nb = 0; nb < NB; ++nb) st.l[nb] += shfl_xor_f(st.l[nb], 32);  // both key halves
+//
+// Decode runs 32 heads per wave (a row group: one query row x 32 heads), so
+// that a wave needs at most 256 registers and two waves share each SIMD:
+// one wave's MFMAs then overlap the other's softmax. A workgroup of W = TW *
+// KS waves takes one part of one index row; wave w has row group w % TW of
+// the workgroup's TW and key subrange w / TW of the part's KS. The TW waves
+// of a subrange need the same K/V rows, so they gather each 32-key block
+// together into one shared LDS buffer pair (one request per row instead of
+// one per wave). With KS > 1 the subrange states of a row group are combined
+// through LDS in a fixed binary tree before the part's partial is written.
 
-  const int64_t pbase = ((int64_t)b * a.n_split + split) * R;
+// (x0 + x1) or (x0 + x1) + (x2 + x3)
+template <int N>
+__device__ __forceinline__ float tree_sum(const float (&x)[N]) {
+  static_assert(N == 2 || N == 4, "two or four subranges");
+  if constexpr (N == 2) return x[0] + x[1];
+  else return (x[0] + x[1]) + (x[2] + x[3]);
+}
+
+template <int NB>
+__device__ __forceinline__ void store_partial(const AttnState<NB>& st, const DecodeArgs& a, int64_t rbase, int h0,
+                                              int mb_lo, int mb_hi, bool ml) {
+  const int l = lane_id(), g = l >> 5, c = l & 31;
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
-    const int h = hb * 32 * NB + 32 * nb + c;
+    const int h = h0 + 32 * nb + c;
     if (h >= a.H) continue;
-    const int64_t row = pbase + (int64_t)qr * a.H + h;
-    if (g == 0) {
+    const int64_t row = rbase + h;
+    if (ml && g == 0) {
       a.ws_m[row] = st.m[nb];
       a.ws_l[row] = st.l[nb];
     }
     float* orow = a.ws_o + row * kD;
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb)
+    for (int mb = 0; mb < 4; ++mb) {
+      if (mb < mb_lo || mb >= mb_hi) continue;
 #pragma unroll
       for (int i4 = 0; i4 < 4; ++i4) {
         const v16f& O = st.o[mb][nb];
-        *(v4f*)(orow + 32 * mb + 8 * i4 + 4 * g) =
-            v4f{O[4 * i4], O[4 * i4 + 1], O[4 * i4 + 2], O[4 * i4 + 3]};
+        *(v4f*)(orow + 32 * mb + 8 * i4 + 4 * g) = v4f{O[4 * i4], O[4 * i4 + 1], O[4 * i4 + 2], O[4 * i4 + 3]};
       }
+    }
   }
 }
 
-constexpr int kMaxSplit = 64;
+template <int TW, int KS>
+struct DecodeCfg {
+  static constexpr int W = TW * KS;                        // waves per workgroup
+  static constexpr int R = TW >= 8 ? 6 : TW >= 4 ? 4 : 2;  // register stages of 64 / TW VGPRs
+  static constexpr int kCap = KS >= 4 ? 512 : 2048;        // positions per chunk
+  static constexpr int kPosN = kCap + 64 * R;              // with the -1 tail the pipeline reads
+  static constexpr int kKvOnly = KS * 2 * kBlkLds;
+  static constexpr int kKv = kKvOnly + KS * kPosN * 4;
+  // subrange states: per wave, o as [mb][i][lane] and m, l as [lane]
+  static constexpr int kStO = 4 * 16 * 64 * 4;
+  static constexpr int kStW = kStO + 2 * 64 * 4;
+  static constexpr int kSt = KS > 1 ? W * kStW : 0;
+  static constexpr int kBytes = kKv > kSt ? kKv : kSt;
+  static_assert(kBytes <= 160 * 1024, "LDS");
+};
 
-// One block per (sequence, row); thread = output dim. Weighted sums over the
-// splits use a fixed 64-leaf binary tree (absent splits are exact zeros).
-__global__ __launch_bounds__(128) void attn_decode_merge(DecodeArgs a) {
+template <int TW, int KS>
+__global__ __launch_bounds__(64 * TW * KS) void attn_decode_partial(DecodeArgs a) {
+  using Cfg = DecodeCfg<TW, KS>;
+  constexpr int NB = 1;
+  __shared__ __attribute__((aligned(16))) char lds_all[Cfg::kBytes];
+  const int wv = wave_id(), gw = wv % TW, sr = wv / TW;
+  const int HB = (a.H + 31) / 32;
+  const int T = a.n_q * HB;
+  const int t = blockIdx.x * TW + gw;
+  const bool active = t < T;
+  const int qr = active ? t / HB : 0, hb = active ? t % HB : 0;
+  const int split = blockIdx.y, b = blockIdx.z;
+  const int l = lane_id();
   const int R = a.n_q * a.H;
-  const int64_t brow = blockIdx.x;
-  const int b = (int)(brow / R), r = (int)(brow % R);
-  const int d = threadIdx.x;
-  float M = -INFINITY;
-  for (int j = 0; j < a.n_split; ++j) M = fmaxf(M, a.ws_m[((int64_t)b * a.n_split + j) * R + r]);
-  float lv[kMaxSplit], ov[kMaxSplit];
+  v8bf Q[NB][8];
+  if (active) load_q<NB>(a.q + ((int64_t)b * a.n_q + qr) * a.H * kD, hb * 32, a.H, Q);
+  AttnState<NB> st;
+  attn_init(st);
+  // every row group of a workgroup reads the same index row
+  const int irow = a.n_idx == 1 ? 0 : (int)(blockIdx.x * TW) / HB;
+  const int64_t ibase = (int64_t)b * a.n_idx + irow;
+  const int n = min(max(a.n_sel[ibase], 0), a.K_tot);
+  const int cs = (n + a.n_split - 1) / a.n_split;
+  const int kb = min(n, split * cs), ke = min(n, (split + 1) * cs);
+  const int nblk = (ke - kb + 31) / 32;
+  const int bps = (nblk + KS - 1) / KS;
+  const int sb = min(ke, kb + 32 * bps * sr), se = min(ke, sb + 32 * bps);
+  const uint16_t* K = a.k + (int64_t)b * a.n_k * kD;
+  const uint16_t* V = a.v + (int64_t)b * a.n_k * kD;
+  // positions go to LDS a chunk at a time (one chunk for parts up to kCap
+  // keys); chunk and trip counts derive from bps alone, so every wave meets
+  // the same barriers
+  constexpr int kR = Cfg::R;
+  int* posg = (int*)(lds_all + Cfg::kKvOnly) + sr * Cfg::kPosN;
+  const int32_t* ids = a.idx + ibase * a.K_tot;
+  const int span = 32 * bps;
+  const int gt = 64 * gw + l;
+  for (int ch = 0; ch * Cfg::kCap < span; ++ch) {
+    const int cb = sb + ch * Cfg::kCap;
+    const int cnt = min(max(se - cb, 0), Cfg::kCap);
+    const int tr = (min(Cfg::kCap, span - ch * Cfg::kCap) / 32 + kR - 1) / kR * kR;
+    if (ch > 0) __syncthreads();  // the previous chunk's positions and buffers no longer read
+    for (int i = gt; i < Cfg::kPosN; i += 64 * TW) posg[i] = i < cnt ? ids[cb + i] : -1;
+    __syncthreads();
+    attn_keys_lds<NB, TW, kR>(Q, active, K, V, posg, cnt, tr, a.n_k, a.sl2, gw, st, lds_all + sr * 2 * kBlkLds);
+  }
+  st.l[0] += shfl_xor_f(st.l[0], 32);  // both key halves
+  const int64_t rbase = ((int64_t)b * a.n_split + split) * R + (int64_t)qr * a.H;
+  if constexpr (KS == 1) {
+    if (active) store_partial<NB>(st, a, rbase, hb * 32, 0, 4, true);
+  } else {
+    // combine the KS subrange states of each row group; wave sr of the row
+    // group then owns the dim blocks [sr * 4 / KS, (sr + 1) * 4 / KS)
+    __syncthreads();  // K/V buffers no longer read
+    float* so = (float*)(lds_all + wv * Cfg::kStW);
+    float* sm = (float*)(lds_all + wv * Cfg::kStW + Cfg::kStO);
+    sm[l] = st.m[0];
+    sm[64 + l] = st.l[0];
 #pragma unroll
-  for (int j = 0; j < kMaxSplit; ++j) {
-    lv[j] = 0.f;
-    ov[j] = 0.f;
-    if (j < a.n_split && M != -INFINITY) {
-      const int64_t row = ((int64_t)b * a.n_split + j) * R + r;
-      const float wj = exp2f(a.ws_m[row] - M);
-      lv[j] = wj * a.ws_l[row];
-      ov[j] = wj * a.ws_o[row * kD + d];
+    for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) so[(mb * 16 + i) * 64 + l] = st.o[mb][0][i];
+    __syncthreads();
+    float ms[KS], ws[KS], ls[KS];
+    float M = -INFINITY;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      const float* smw = (const float*)(lds_all + (s * TW + gw) * Cfg::kStW + Cfg::kStO);
+      ms[s] = smw[l];
+      ls[s] = smw[64 + l];
+      M = fmaxf(M, ms[s]);
     }
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      ws[s] = M == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ms[s] - M);
+      ls[s] *= ws[s];
+    }
+    st.m[0] = M;
+    st.l[0] = tree_sum<KS>(ls);
+    constexpr int MBW = 4 / KS;  // dim blocks per wave
+    const int mb_lo = sr * MBW;
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) {
+      if (mb < mb_lo || mb >= mb_lo + MBW) continue;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        float os[KS];
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+          const float* sow = (const float*)(lds_all + (s * TW + gw) * Cfg::kStW);
+          os[s] = ws[s] * sow[(mb * 16 + i) * 64 + l];
+        }
+        st.o[mb][0][i] = tree_sum<KS>(os);
+      }
+    }
+    if (active) store_partial<NB>(st, a, rbase, hb * 32, mb_lo, mb_lo + MBW, sr == 0);
+  }
+}
+
+// One row per 32 threads, 4 output dims per thread. Weighted sums over the
+// NS >= n_split leaves (absent parts are exact zeros) use a fixed binary
+// tree; for NS up to 64 the leaves beyond the next power of two above
+// n_split add exact zeros only, so every NS gives the same result.
+template <int NS>
+__global__ __launch_bounds__(256) void attn_decode_merge(DecodeArgs a) {
+  const int R = a.n_q * a.H;
+  const int64_t brow = (int64_t)blockIdx.x * 8 + (threadIdx.x >> 5);
+  if (brow >= (int64_t)a.B * R) return;
+  const int b = (int)(brow / R), r = (int)(brow % R);
+  const int d = 4 * (threadIdx.x & 31);
+  const int64_t row0 = (int64_t)b * a.n_split * R + r;
+  const float* pm = a.ws_m + row0;
+  const float* pl = a.ws_l + row0;
+  const float* po = a.ws_o + row0 * kD + d;
+  float mj[NS], lv[NS];
+  v4f ov[NS];
+#pragma unroll
+  for (int j = 0; j < NS; ++j) {
+    const bool in = j < a.n_split;
+    const int jr = in ? j * R : 0;
+    mj[j] = in ? pm[jr] : -INFINITY;
+    lv[j] = in ? pl[jr] : 0.f;
+    ov[j] = in ? *(const v4f*)(po + jr * kD) : v4f{};
+  }
+  float M = -INFINITY;
+#pragma unroll
+  for (int j = 0; j < NS; ++j) M = fmaxf(M, mj[j]);
+#pragma unroll
+  for (int j = 0; j < NS; ++j) {
+    const float wj = (j < a.n_split && M != -INFINITY) ? __builtin_amdgcn_exp2f(mj[j] - M) : 0.f;
+    lv[j] *= wj;
+    ov[j] *= wj;
   }
 #pragma unroll
-  for (int s = 1; s < kMaxSplit; s <<= 1)
+  for (int s = 1; s < NS; s <<= 1)
 #pragma unroll
-    for (int j = 0; j + s < kMaxSplit; j += 2 * s) {
+    for (int j = 0; j + s < NS; j += 2 * s) {
       lv[j] += lv[j + s];
       ov[j] += ov[j + s];
     }
   const float Lam = lv[0];
-  const float out = Lam > 0.f ? ov[0] / Lam : 0.f;
-  a.o[brow * kD + d] = (uint16_t)f32_to_bf16_bits(out);
+  const float inv = Lam > 0.f ? 1.f / Lam : 0.f;
+  const uint32_t w0 = pack_bf16x2(ov[0][0] * inv, ov[0][1] * inv);
+  const uint32_t w1 = pack_bf16x2(ov[0][2] * inv, ov[0][3] * inv);
+  *(v2u*)(a.o + brow * kD + d) = v2u{w0, w1};
   if (a.lse && d == 0) a.lse[brow] = Lam > 0.f ? (M + log2f(Lam)) * 0.69314718055994531f : -INFINITY;
 }
 
@@ -407,16 +594,40 @@ size_t decode_ws_bytes(int B, int n_q, int H, int n_split) {
   return rows * sizeof(float) * (2 + kD) + 256;
 }
 
+template <int TW, int KS>
+static void launch_partial_tk(const DecodeArgs& a, int T, hipStream_t st) {
+  dim3 grid((T + TW - 1) / TW, a.n_split, a.B);
+  hipLaunchKernelGGL((attn_decode_partial<TW, KS>), grid, dim3(64 * TW * KS), 0, st, a);
+}
+
+static hipError_t launch_partial(const DecodeArgs& a, hipStream_t st) {
+  const int HB = (a.H + 31) / 32;
+  const int T = a.n_q * HB;
+  // waves sharing K/V must read the same index row: with one index per
+  // query row, a workgroup stays within the head groups of one row
+  const int TW = a.n_idx == 1 ? (T >= 8 ? 8 : T >= 4 ? 4 : T >= 2 ? 2 : 1) : HB;
+  // subranges per part: 8 waves per workgroup (4 when one row group, to stay
+  // within LDS)
+  switch (TW) {
+    case 8: launch_partial_tk<8, 1>(a, T, st); break;
+    case 4: launch_partial_tk<4, 2>(a, T, st); break;
+    case 2: launch_partial_tk<2, 4>(a, T, st); break;
+    default: launch_partial_tk<1, 4>(a, T, st); break;
+  }
+  return hipGetLastError();
+}
+
 hipError_t launch_attn_decode(const DecodeArgs& a, hipStream_t st) {
-  const int NB = a.H <= 32 ? 1 : 2;
-  const int HB = (a.H + 32 * NB - 1) / (32 * NB);
-  const int groups = a.n_q * HB;
-  dim3 grid((groups + 3) / 4, a.n_split, a.B);
-  if (NB == 1) hipLaunchKernelGGL(attn_decode_partial<1>, grid, dim3(256), 0, st, a);
-  else hipLaunchKernelGGL(attn_decode_partial<2>, grid, dim3(256), 0, st, a);
-  hipError_t e = hipGetLastError();
+  hipError_t e = launch_partial(a, st);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(attn_decode_merge, dim3((unsigned)((int64_t)a.B * a.n_q * a.H)), dim3(kD), 0, st, a);
+  const dim3 grid((unsigned)(((int64_t)a.B * a.n_q * a.H + 7) / 8));
+  if (a.n_split <= 1) hipLaunchKernelGGL(attn_decode_merge<1>, grid, dim3(256), 0, st, a);
+  else if (a.n_split <= 2) hipLaunchKernelGGL(attn_decode_merge<2>, grid, dim3(256), 0, st, a);
+  else if (a.n_split <= 4) hipLaunchKernelGGL(attn_decode_merge<4>, grid, dim3(256), 0, st, a);
+  else if (a.n_split <= 8) hipLaunchKernelGGL(attn_decode_merge<8>, grid, dim3(256), 0, st, a);
+  else if (a.n_split <= 16) hipLaunchKernelGGL(attn_decode_merge<16>, grid, dim3(256), 0, st, a);
+  else if (a.n_split <= 32) hipLaunchKernelGGL(attn_decode_merge<32>, grid, dim3(256), 0, st, a);
+  else hipLaunchKernelGGL(attn_decode_merge<64>, grid, dim3(256), 0, st, a);
   return hipGetLastError();
 }
 

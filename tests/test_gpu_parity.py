@@ -279,7 +279,8 @@ def test_prefill_attention(H):
 
 
 @pytest.mark.parametrize("H,n_q,n_idx,n_split", [(64, 4, 1, 8), (64, 4, 4, 3), (16, 2, 1, 5), (128, 1, 1, 1),
-                                                 (64, 1, 1, 64)])
+                                                 (64, 1, 1, 64), (32, 4, 1, 2), (32, 1, 1, 8), (128, 2, 2, 16),
+                                                 (64, 3, 1, 4), (16, 8, 8, 1)])
 def test_decode_attention(H, n_q, n_idx, n_split):
     say(f"decode attention H={H} n_q={n_q} n_idx={n_idx} n_split={n_split}")
     B, n_k, K_tot = 3, 5000, 700
