@@ -31,7 +31,7 @@ CFLAGS = [
 # accumulators in ordinary VGPRs, which their VALU epilogues read directly
 # (no copies between accumulation and vector registers in the loops).
 _VGPR_FORM = ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]
-FILE_FLAGS = {"index_prefill.hip": _VGPR_FORM, "attention.hip": _VGPR_FORM}
+FILE_FLAGS = {"index_prefill.hip": _VGPR_FORM, "index_decode.hip": _VGPR_FORM, "attention.hip": _VGPR_FORM}
 
 
 def sources():

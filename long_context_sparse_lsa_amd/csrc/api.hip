@@ -48,13 +48,10 @@ int32_t hip_status(hipError_t e) { return e == hipSuccess ? LSA_OK : LSA_HIP; }
 
 int k_cap_of(int k) { return std::max(4, (k + 3) / 4 * 4); }
 
-int chunks_of(int64_t nc) { return select_chunks(nc); }
+int chunks_of(int64_t nc, int k_cap) { return select_chunks(nc, k_cap); }
 
 // Stage two of a multi-chunk selection holds every chunk's survivors at once.
-bool survivors_ok(int64_t max_nc, int k_cap) {
-  const int ch = chunks_of(max_nc);
-  return ch <= 1 || (int64_t)ch * k_cap <= kSelMaxSurvivors;
-}
+bool survivors_ok(int64_t max_nc, int k_cap) { return select_fits(max_nc, k_cap); }
 
 // Rows per pass of the fused (score + select) prefill path: the score buffer
 // of one pass is at most kFusedScoreBytes.
@@ -144,14 +141,14 @@ extern "C" int32_t lsa_select_topk(const int32_t* scores, const int8_t* q_idx, c
   int R = 0, nb_pass = 1;
   int rows_pass = B * n_q;
   if (scores != nullptr) {
-    const size_t per_row = select_ws_bytes(1, chunks_of(max_nc), k_cap);
+    const size_t per_row = select_ws_bytes(1, chunks_of(max_nc, k_cap), k_cap);
     if (per_row > 0)
       rows_pass = (int)std::max<size_t>(1, std::min<size_t>(rows_pass, kFusedScoreBytes / per_row));
-    need = select_ws_bytes(rows_pass, chunks_of(max_nc), k_cap);
+    need = select_ws_bytes(rows_pass, chunks_of(max_nc, k_cap), k_cap);
   } else {
     fused_pass(B, n_q, n_k, R, nb_pass);
     const size_t rows = (size_t)R * nb_pass;
-    need = align_up(rows * n_k * sizeof(int32_t)) + select_ws_bytes((int)rows, chunks_of(max_nc), k_cap);
+    need = align_up(rows * n_k * sizeof(int32_t)) + select_ws_bytes((int)rows, chunks_of(max_nc, k_cap), k_cap);
   }
   need = align_up(std::max<size_t>(need, 1));
   if (ws_needed) *ws_needed = need;
@@ -277,8 +274,8 @@ extern "C" int32_t lsa_hier_select(const int8_t* q_idx, const int8_t* k_idx, con
   const size_t sz_blocks = align_up((size_t)B * n_blk_recall * sizeof(int32_t));
   const size_t sz_nblk = align_up((size_t)B * sizeof(int32_t));
   const size_t sz_fine = align_up((size_t)B * n_virt * sizeof(int32_t));
-  const size_t sz_sel = align_up(std::max(select_ws_bytes(B, chunks_of(n_elig), kc_coarse),
-                                          select_ws_bytes(B, chunks_of(n_virt), kc_fine)));
+  const size_t sz_sel = align_up(std::max(select_ws_bytes(B, chunks_of(n_elig, kc_coarse), kc_coarse),
+                                          select_ws_bytes(B, chunks_of(n_virt, kc_fine), kc_fine)));
   const size_t need = trivial ? kAlign : sz_coarse + sz_blocks + sz_nblk + sz_fine + sz_sel;
   if (ws_needed) *ws_needed = need;
   if (ws == nullptr) return ws_needed ? LSA_OK : LSA_WORKSPACE;  // size query
@@ -301,8 +298,8 @@ extern "C" int32_t lsa_hier_select(const int8_t* q_idx, const int8_t* k_idx, con
     sa.idx = idx;
     sa.n_sel = n_sel;
     sa.out_ld = K_tot;
-    select_plan(sa, 1);
     sa.k_cap = kc_fine;
+    select_plan(sa, 1);
     return hip_status(launch_select(sa, st));
   }
 
@@ -352,8 +349,8 @@ extern "C" int32_t lsa_hier_select(const int8_t* q_idx, const int8_t* k_idx, con
   sc.idx = blocks;
   sc.n_sel = nblk;
   sc.out_ld = n_blk_recall;
-  select_plan(sc, n_elig);
   sc.k_cap = kc_coarse;
+  select_plan(sc, n_elig);
   select_bind_ws(sc, sel_ws, B);
   s = hip_status(launch_select(sc, st));
   if (s != LSA_OK) return s;
@@ -392,8 +389,8 @@ extern "C" int32_t lsa_hier_select(const int8_t* q_idx, const int8_t* k_idx, con
   sf.idx = idx;
   sf.n_sel = n_sel;
   sf.out_ld = K_tot;
-  select_plan(sf, n_virt);
   sf.k_cap = kc_fine;
+  select_plan(sf, n_virt);
   select_bind_ws(sf, sel_ws, B);
   return hip_status(launch_select(sf, st));
 }

@@ -1,0 +1,233 @@
+// Indexer scoring for a few query rows per sequence (decode and the two HI
+// stages) on int8 MFMA (gfx950).
+//
+// S[t, s] = sum_h w[h] * max(0, q_I[t, h, :] . k_I[s, :]), exact in int32
+// (LongCat-2.0 release article, section "LongCat 稀疏注意力"; the arithmetic
+// is fixed by this library as int8 q/k, integer head weights, int32 result).
+//
+// With one query row per sequence the scan reads every key once and does
+// little arithmetic per byte, so it is bound by HBM streaming. Each wave owns
+// a long contiguous key range, loads its query rows (the MFMA A operand) once,
+// and streams 32-key tiles straight into registers through a ring of kDepth
+// tiles: the loads of tile t + kDepth are issued as soon as tile t has gone
+// through the MFMAs, so kDepth tiles are in flight per wave at all times.
+// No load is conditional: keys past the range re-read the range's last key,
+// which only touches lines already in cache. In the HI fine stage (keys
+// addressed through a block table) the wave first copies its slice of the
+// table to LDS, so key addresses never wait on a global load.
+//
+// Layout of the 32x32x32 int8 MFMA: lane l supplies row / key l % 32 and
+// half l / 32 of the d_I bytes (A and B use the same byte-to-slot map, so
+// the product is exact); the accumulator gives lane l key column l % 32 and
+// rows 8 * (i / 4) + 4 * (l / 32) + i % 4 of register i. A query owns H_I
+// consecutive rows, so its head sum is a per-lane sum plus one exchange
+// between lane halves. Weights are folded into A when that is exact (every
+// weight >= 0 and every product w[h] * q fits int8, checked per wave), else
+// applied in the epilogue from LDS; both give the same integers.
+#include <algorithm>
+
+#include "lsa_device.h"
+#include "lsa_internal.h"
+
+namespace lsa {
+
+namespace {
+
+constexpr int kWaves = 4;
+constexpr int kDepth = 4;          // key tiles in flight per wave
+constexpr int kMaxBlkIds = 136;    // block-table entries per wave in LDS
+constexpr int kMaxKeysPerWave = 4096;
+
+template <int MB, int KS>
+__device__ __forceinline__ void tile_mfma(const v4i (&A)[MB][KS], const v4i (&Bk)[KS], v16i (&acc)[MB]) {
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) acc[mb] = v16i{};
+#pragma unroll
+  for (int j = 0; j < KS; ++j)
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) acc[mb] = mfma_i8_32x32x32(A[mb][j], Bk[j], acc[mb]);
+}
+
+// Lane-partial score of query qi (its M-blocks [qi * MQ, (qi + 1) * MQ)).
+template <int MB, int MQ, bool FOLD>
+__device__ __forceinline__ int query_sum(const v16i (&acc)[MB], int qi, const int* wl) {
+  int s = 0;
+#pragma unroll
+  for (int m = 0; m < MQ; ++m) {
+    const int mb = qi * MQ + m;
+    if constexpr (FOLD) {
+#pragma unroll
+      for (int i = 0; i < 16; i += 2) s = s + max(acc[mb][i], 0) + max(acc[mb][i + 1], 0);
+    } else {
+      const int g = lane_id() >> 5;
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4) {
+        const v4i w4 = *(const v4i*)(wl + 32 * mb + 8 * i4 + 4 * g);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) s += __mul24(max(acc[mb][4 * i4 + e], 0), w4[e]);
+      }
+    }
+  }
+  return s;
+}
+
+template <int HI, int DI, bool FOLD>
+__device__ __forceinline__ void scan_keys(const ScoreArgs& a, const v4i (&A)[HI >= 64 ? HI / 32 : 2][DI / 32],
+                                          const int* wl, const int* blw, int bfirst, int b, int q0, int v0,
+                                          int v1) {
+  constexpr int MB = HI >= 64 ? HI / 32 : 2;
+  constexpr int NQ = 32 * MB / HI;  // query rows per wave: 1 or 2
+  constexpr int MQ = MB / NQ;       // M-blocks per query
+  constexpr int KS = DI / 32;
+  const int l = lane_id(), g = l >> 5, c = l & 31;
+  const bool direct = a.blocks == nullptr;
+  const int8_t* kb = a.k + (int64_t)b * a.k_bstride;
+  int32_t* sc = a.scores + (int64_t)b * a.s_bstride;
+
+  auto pos_of = [&](int v) -> int {
+    if (direct) return v;
+    const int bi = blw[v / a.blk - bfirst];
+    return bi < 0 ? -1 : bi * a.blk + v % a.blk;
+  };
+  auto load = [&](int t, v4i (&Bt)[KS]) {
+    const int p = pos_of(min(v0 + 32 * t + c, v1 - 1));
+    const int pp = (unsigned)p < (unsigned)a.n_k ? p : 0;
+    const v4i* src = (const v4i*)(kb + (int64_t)pp * DI + g * (DI / 2));
+#pragma unroll
+    for (int j = 0; j < KS; ++j) Bt[j] = src[j];
+  };
+  auto store = [&](int qi, int v, int p, int val) {
+    const int gq = q0 + qi;
+    if (gq >= a.n_q || v >= v1) return;
+    const bool vis = p >= a.pos_lo && p <= a.mask_off + gq;
+    if (vis) sc[(int64_t)gq * a.ld + v] = val;
+    else if (a.fill_masked) sc[(int64_t)gq * a.ld + v] = kMasked;
+  };
+
+  const int T = (v1 - v0 + 31) / 32;
+  v4i ring[kDepth][KS];
+#pragma unroll
+  for (int u = 0; u < kDepth; ++u) load(u, ring[u]);
+  for (int t0 = 0; t0 < T; t0 += kDepth) {
+#pragma unroll
+    for (int u = 0; u < kDepth; ++u) {
+      const int t = t0 + u;
+      if (t < T) {
+        v16i acc[MB];
+        tile_mfma<MB, KS>(A, ring[u], acc);
+        const int v = v0 + 32 * t + c;
+        const int p = v < v1 ? pos_of(v) : -1;
+        if constexpr (NQ == 1) {
+          int s = query_sum<MB, MQ, FOLD>(acc, 0, wl);
+          s += shfl_xor_i(s, 32);
+          if (g == 0) store(0, v, p, s);
+        } else {
+          const int s0 = query_sum<MB, MQ, FOLD>(acc, 0, wl);
+          const int s1 = query_sum<MB, MQ, FOLD>(acc, 1, wl);
+          // lane half g finishes query g
+          const int mine = (g ? s1 : s0) + shfl_xor_i(g ? s0 : s1, 32);
+          store(g, v, p, mine);
+        }
+      }
+      load(t + kDepth, ring[u]);
+    }
+  }
+}
+
+template <int HI, int DI>
+__global__ __launch_bounds__(64 * kWaves) void index_decode_kernel(ScoreArgs a, int kpw, int fold_ok) {
+  constexpr int MB = HI >= 64 ? HI / 32 : 2;
+  constexpr int NQ = 32 * MB / HI;
+  constexpr int KS = DI / 32;
+  __shared__ __attribute__((aligned(16))) int wl[128];
+  __shared__ int bl[kWaves][kMaxBlkIds];
+  const int l = lane_id(), c = l & 31, g = l >> 5, wv = wave_id();
+  for (int h = threadIdx.x; h < 128; h += 64 * kWaves) wl[h] = h < HI ? a.w.w[h] : 0;
+  __syncthreads();
+  const int b = blockIdx.z;
+  const int q0 = blockIdx.x * NQ;
+  const int nq_tile = min(NQ, a.n_q - q0);
+  const int v0 = (blockIdx.y * kWaves + wv) * kpw;
+  const int v1 = min(v0 + kpw, a.n_keys);
+  if (v0 >= v1) return;
+  const bool direct = a.blocks == nullptr;
+  if (direct && (v0 > a.mask_off + q0 + nq_tile - 1 || v1 <= a.pos_lo)) {
+    // nothing in this range is visible to any row of the tile
+    if (a.fill_masked) {
+      int32_t* sc = a.scores + (int64_t)b * a.s_bstride;
+      for (int qi = 0; qi < nq_tile; ++qi)
+        for (int v = v0 + l; v < v1; v += 64) sc[(int64_t)(q0 + qi) * a.ld + v] = kMasked;
+    }
+    return;
+  }
+  // this wave's slice of the block table (HI fine stage)
+  int* blw = bl[wv];
+  const int bfirst = direct ? 0 : v0 / a.blk;
+  if (!direct) {
+    const int nb = (v1 - 1) / a.blk - bfirst + 1;
+    for (int i = l; i < nb; i += 64) blw[i] = a.blocks[(int64_t)b * a.nbr + bfirst + i];
+  }
+
+  // A operand: this wave's query rows, MB M-blocks x KS 16-byte pieces
+  v4i A[MB][KS];
+  const int8_t* qb = a.q + (int64_t)b * a.q_bstride;
+  bool ok = fold_ok != 0;
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) {
+    const int r = 32 * mb + c;
+    const int gq = q0 + r / HI, h = r % HI;
+    const v4i* src = (const v4i*)(qb + ((int64_t)gq * HI + h) * DI + g * (DI / 2));
+#pragma unroll
+    for (int j = 0; j < KS; ++j) {
+      A[mb][j] = gq < a.n_q ? src[j] : v4i{0, 0, 0, 0};
+      ok = ok && bytes_scale_fit(A[mb][j], wl[h]);
+    }
+  }
+  if (__all(ok)) {
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int j = 0; j < KS; ++j) A[mb][j] = scale_bytes(A[mb][j], wl[(32 * mb + c) % HI]);
+    scan_keys<HI, DI, true>(a, A, wl, blw, bfirst, b, q0, v0, v1);
+  } else {
+    scan_keys<HI, DI, false>(a, A, wl, blw, bfirst, b, q0, v0, v1);
+  }
+}
+
+template <int HI, int DI>
+hipError_t launch_t(const ScoreArgs& a, hipStream_t st) {
+  constexpr int MB = HI >= 64 ? HI / 32 : 2;
+  constexpr int NQ = 32 * MB / HI;
+  const int qtiles = (a.n_q + NQ - 1) / NQ;
+  // one wave per wave slot of the GPU (256 CUs x 2 waves per SIMD x 4), so
+  // that every wave streams from start to end without a second round; each
+  // wave takes a multiple of 32 * kDepth keys
+  const int64_t total = (int64_t)a.B * qtiles * a.n_keys;
+  int64_t kpw = (total + 2047) / 2048;
+  kpw = (kpw + 32 * kDepth - 1) / (32 * kDepth) * (32 * kDepth);
+  kpw = std::min<int64_t>(std::max<int64_t>(kpw, 32 * kDepth), kMaxKeysPerWave);
+  const int64_t per_wg = kpw * kWaves;
+  dim3 grid((unsigned)qtiles, (unsigned)((a.n_keys + per_wg - 1) / per_wg), (unsigned)a.B);
+  int fold_ok = 1;
+  for (int h = 0; h < a.H_I; ++h) fold_ok &= a.w.w[h] >= 0;
+  hipLaunchKernelGGL((index_decode_kernel<HI, DI>), grid, dim3(64 * kWaves), 0, st, a, (int)kpw, fold_ok);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+bool index_decode_supported(const ScoreArgs& a) {
+  // a wave's keys span at most kMaxKeysPerWave / blk + 2 table entries
+  const bool table_ok = a.blocks == nullptr || (a.blk >= 32 && kMaxKeysPerWave / a.blk + 2 <= kMaxBlkIds);
+  return (a.H_I == 32 || a.H_I == 64 || a.H_I == 128) && (a.d_I == 64 || a.d_I == 128) && table_ok;
+}
+
+hipError_t launch_index_decode(const ScoreArgs& a, hipStream_t st) {
+#define LSA_CASE(h, d) \
+  if (a.H_I == h && a.d_I == d) return launch_t<h, d>(a, st);
+  LSA_CASE(32, 64) LSA_CASE(32, 128) LSA_CASE(64, 64) LSA_CASE(64, 128) LSA_CASE(128, 64) LSA_CASE(128, 128)
+#undef LSA_CASE
+  return hipErrorInvalidValue;
+}
+
+}  // namespace lsa

@@ -54,35 +54,6 @@ struct TileGeom {
   static constexpr int kPerThread = kPieces / kThreads;
 };
 
-// True iff w times each of the 16 int8 values of v stays in [-128, 127].
-__device__ __forceinline__ bool bytes_scale_fit(v4i v, int w) {
-  bool ok = true;
-#pragma unroll
-  for (int e = 0; e < 4; ++e)
-#pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      const int x = (int)(int8_t)((uint32_t)v[e] >> (8 * b)) * w;
-      ok = ok && x >= -128 && x <= 127;
-    }
-  return ok;
-}
-
-// The 16 int8 values of v times w (each product known to fit int8).
-__device__ __forceinline__ v4i scale_bytes(v4i v, int w) {
-  v4i r;
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    uint32_t o = 0;
-#pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      const int x = (int)(int8_t)((uint32_t)v[e] >> (8 * b)) * w;
-      o |= ((uint32_t)x & 0xffu) << (8 * b);
-    }
-    r[e] = (int)o;
-  }
-  return r;
-}
-
 // Lane-partial head sum of one 32-key block (this lane's rows, key l % 32).
 // Unfolded, the weights of this lane's rows come from LDS (wl holds w[h];
 // rows 8*(i/4) + 4*g + i%4 of block mb are four consecutive heads).

@@ -165,6 +165,7 @@ static hipError_t launch_t(const ScoreArgs& a, hipStream_t st) {
 
 hipError_t launch_index_score(const ScoreArgs& a, hipStream_t st) {
   if (index_prefill_supported(a)) return launch_index_prefill(a, st);
+  if (index_decode_supported(a)) return launch_index_decode(a, st);
 #define LSA_CASE(h, d) \
   if (a.H_I == h && a.d_I == d) return launch_t<h, d>(a, st);
   LSA_CASE(4, 64) LSA_CASE(4, 128) LSA_CASE(8, 64) LSA_CASE(8, 128)

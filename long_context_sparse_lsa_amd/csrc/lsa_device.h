@@ -65,4 +65,33 @@ __device__ __forceinline__ int wave_sum(int v) {
   return v;
 }
 
+// True iff w times each of the 16 int8 values of v stays in [-128, 127].
+__device__ __forceinline__ bool bytes_scale_fit(v4i v, int w) {
+  bool ok = true;
+#pragma unroll
+  for (int e = 0; e < 4; ++e)
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      const int x = (int)(int8_t)((uint32_t)v[e] >> (8 * b)) * w;
+      ok = ok && x >= -128 && x <= 127;
+    }
+  return ok;
+}
+
+// The 16 int8 values of v times w (each product known to fit int8).
+__device__ __forceinline__ v4i scale_bytes(v4i v, int w) {
+  v4i r;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    uint32_t o = 0;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      const int x = (int)(int8_t)((uint32_t)v[e] >> (8 * b)) * w;
+      o |= ((uint32_t)x & 0xffu) << (8 * b);
+    }
+    r[e] = (int)o;
+  }
+  return r;
+}
+
 }  // namespace lsa

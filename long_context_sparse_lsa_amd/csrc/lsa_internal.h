@@ -36,6 +36,10 @@ hipError_t launch_index_score(const ScoreArgs& a, hipStream_t st);
 // H_I in {32, 64}, n_q >= 8.
 bool index_prefill_supported(const ScoreArgs& a);
 hipError_t launch_index_prefill(const ScoreArgs& a, hipStream_t st);
+// Few-row variant (long per-wave key ranges streamed through registers);
+// direct keys or a block table with blk >= 32, H_I in {32, 64, 128}.
+bool index_decode_supported(const ScoreArgs& a);
+hipError_t launch_index_decode(const ScoreArgs& a, hipStream_t st);
 
 // Selection launch.
 enum SelMode { SEL_FLAT = 0, SEL_RAW = 1, SEL_INDIRECT = 2 };
@@ -68,9 +72,12 @@ struct SelectArgs {
   int chunk_e;     // candidates per thread of a chunk (select_plan)
   int k_cap;
 };
-// Chunk geometry for rows of at most max_nc candidates: the chunk count of
-// the longest row, and a plan that sets max_chunks and chunk_e together.
-int select_chunks(int64_t max_nc);
+// Chunk geometry for rows of at most max_nc candidates keeping k_cap each:
+// the chunk count of the longest row (workspace sizing), whether the
+// stage-two input of such rows fits kSelMaxSurvivors, and a plan that sets
+// max_chunks and chunk_e together.
+int select_chunks(int64_t max_nc, int k_cap);
+bool select_fits(int64_t max_nc, int k_cap);
 void select_plan(SelectArgs& a, int64_t max_nc);
 // Largest stage-two input (max_chunks * k_cap) the selection supports.
 constexpr int64_t kSelMaxSurvivors = 32 * 1024;

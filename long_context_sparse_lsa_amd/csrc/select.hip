@@ -23,6 +23,8 @@
 // top min(k, valid) of every chunk (a superset of the row's top-k inside that
 // chunk), stage B selects the row's top-k from the concatenated survivors,
 // which are still in ascending position order.
+#include <algorithm>
+
 #include "lsa_device.h"
 #include "lsa_internal.h"
 
@@ -30,14 +32,20 @@ namespace lsa {
 
 namespace {
 
-constexpr int SEL_NT = 1024;
-constexpr int SEL_NW = SEL_NT / 64;
+constexpr int SEL_NT = 1024;  // threads of a stage-B workgroup (and the widest stage A)
 
+constexpr int kBins1 = 2048;  // first radix digit: up to 11 bits
+constexpr int kList = 4096;   // keys of the first pass's threshold bin kept in LDS
+
+template <int NT>
 struct SelShared {
-  uint32_t hist[256];
-  int scan_w[SEL_NW];
-  uint32_t red_w[2][SEL_NW];
-  int bcast[4];
+  static constexpr int NW = NT / 64;
+  alignas(16) uint32_t hist1[kBins1];  // first pass
+  alignas(16) uint32_t hist[3][256];   // later pass p counts into hist[p % 3]
+  uint32_t list[kList];
+  int list_n;
+  uint32_t scan_w[NW];   // per-wave totals of the compaction scan
+  uint32_t st_w[3][NW];  // per-wave count, min, max of the chunk
 };
 
 struct RowGeom {
@@ -78,19 +86,20 @@ __device__ __forceinline__ int pos_of(const SelectArgs& a, int r, int v) {
   return bi * a.blk + v % a.blk;
 }
 
-// Exclusive prefix sum over the block in thread order; *total gets the sum.
-__device__ __forceinline__ int block_excl_scan(int v, SelShared& sh, int* total) {
-  const int incl = wave_incl_scan(v);
+// Exclusive prefix sum over the block in thread order (mod 2^32); *total
+// gets the sum. One barrier: sh.scan_w is written once per workgroup.
+template <int NT>
+__device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, SelShared<NT>& sh, uint32_t* total) {
+  const uint32_t incl = (uint32_t)wave_incl_scan((int)v);
   if (lane_id() == 63) sh.scan_w[wave_id()] = incl;
   __syncthreads();
-  int off = 0, tot = 0;
+  uint32_t off = 0, tot = 0;
 #pragma unroll
-  for (int w = 0; w < SEL_NW; ++w) {
-    const int x = sh.scan_w[w];
-    off += (w < wave_id()) ? x : 0;
+  for (int w = 0; w < SelShared<NT>::NW; ++w) {
+    const uint32_t x = sh.scan_w[w];
+    off += (w < wave_id()) ? x : 0u;
     tot += x;
   }
-  __syncthreads();
   *total = tot;
   return off + incl - v;
 }
@@ -106,64 +115,123 @@ __device__ __forceinline__ uint32_t wave_min_u(uint32_t v) {
   return v;
 }
 
+// The bin of the k_rem-th largest key from per-bin counts, found by every
+// wave on its own (no broadcast barrier): lane l owns B / 64 consecutive
+// bins, a suffix sum over lanes gives the keys above each lane's bins, and
+// the one lane whose bins hold the k_rem-th largest scans them. Returns the
+// bin, the keys in bins above it and the keys in it, wave-uniform.
+template <int B>
+__device__ __forceinline__ void find_bin(const uint32_t* hist, int k_rem, uint32_t& d, int& above, int& eq) {
+  constexpr int PL = B / 64;  // bins per lane
+  const int l = lane_id();
+  const v4i* hp = (const v4i*)(hist + PL * l);
+  int sl = 0;
+#pragma unroll
+  for (int i = 0; i < PL / 4; ++i) {
+    const v4i h4 = hp[i];
+    sl += h4[0] + h4[1] + h4[2] + h4[3];
+  }
+  int v = sl;  // inclusive suffix sum over lanes
+#pragma unroll
+  for (int dd = 1; dd < 64; dd <<= 1) {
+    const int t = __shfl_down(v, dd, 64);
+    if (l + dd < 64) v += t;
+  }
+  int cum = v - sl;  // keys in bins above this lane's bins
+  int my_bin = 0, my_above = 0, my_eq = 0;
+  const bool mine = cum < k_rem && k_rem <= cum + sl;
+  if (mine) {
+    for (int i = PL - 1; i >= 0; --i) {
+      const int h = (int)hist[PL * l + i];
+      if (cum < k_rem && k_rem <= cum + h) {
+        my_bin = PL * l + i;
+        my_above = cum;
+        my_eq = h;
+        break;
+      }
+      cum += h;
+    }
+  }
+  const uint64_t who = __ballot(mine);
+  const int src = __ffsll((unsigned long long)who) - 1;
+  d = (uint32_t)__shfl(my_bin, src, 64);
+  above = __shfl(my_above, src, 64);
+  eq = __shfl(my_eq, src, 64);
+}
+
 // Threshold of the k-th largest nonzero key of the chunk (0 < k < #nonzero).
 // On return an entry u is kept iff (u >> shift) > (T >> shift), or
 // (u >> shift) == (T >> shift) and it is among the first r_eq such entries.
-template <int E>
+// The first pass counts every key by a digit of up to 11 bits starting at
+// the highest bit in which the chunk's keys differ. The keys of the bin that
+// holds the threshold (usually a few hundred) are then copied to an LDS list
+// when they fit, and further 8-bit passes count only those. Later pass p
+// counts into hist[p % 3] (hist[0] and hist[1] start cleared); after its
+// barrier every wave finds the digit itself and clears hist[(p + 2) % 3],
+// which no wave reads any more and none writes before the next barrier.
+template <int E, int NT>
 __device__ void radix_select(const uint32_t (&u)[E], uint32_t kmin, uint32_t kmax, int k,
-                             SelShared& sh, uint32_t& T, int& shift_out, int& r_eq) {
+                             SelShared<NT>& sh, uint32_t& T, int& shift_out, int& r_eq) {
   if (kmin == kmax) {  // every candidate has the same key: take the first k
     T = kmax;
     shift_out = 0;
     r_eq = k;
     return;
   }
+  const int tid = threadIdx.x;
   int hb = 31 - __clz(kmin ^ kmax);  // highest differing bit
   uint32_t mask = hb == 31 ? 0u : ~((2u << hb) - 1u);
   uint32_t prefix = kmax & mask;
   int k_rem = k;
-  const int tid = threadIdx.x;
-  while (true) {
-    const int lo = max(0, hb - 7);
-    const uint32_t dmask = (2u << (hb - lo)) - 1u;  // digit of hb - lo + 1 bits
-    if (tid < 256) sh.hist[tid] = 0;
-    __syncthreads();
+  // pass 1 over all keys (all nonzero keys share the bits above hb)
+  int lo = max(0, hb - 10);
+  uint32_t dmask = (2u << (hb - lo)) - 1u;
+#pragma unroll
+  for (int e = 0; e < E; ++e)
+    if (u[e] != 0u) atomicAdd(&sh.hist1[(u[e] >> lo) & dmask], 1u);
+  __syncthreads();
+  uint32_t d;
+  int above, eq;
+  find_bin<kBins1>(sh.hist1, k_rem, d, above, eq);
+  k_rem -= above;
+  prefix |= d << lo;
+  mask |= dmask << lo;
+  if (eq == k_rem || lo == 0) {
+    T = prefix;
+    shift_out = lo;
+    r_eq = k_rem;
+    return;
+  }
+  const bool listed = eq <= kList;
+  if (listed) {
 #pragma unroll
     for (int e = 0; e < E; ++e)
-      if (u[e] != 0u && (u[e] & mask) == prefix) atomicAdd(&sh.hist[(u[e] >> lo) & dmask], 1u);
+      if (u[e] != 0u && (u[e] & mask) == prefix) sh.list[atomicAdd(&sh.list_n, 1)] = u[e];
     __syncthreads();
-    if (wave_id() == 0) {
-      // lane l owns bins 4l .. 4l+3; find the bin holding the k_rem-th largest
-      const int l = lane_id();
-      int h[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) h[e] = (int)sh.hist[4 * l + e];
-      const int s = h[0] + h[1] + h[2] + h[3];
-      int v = s;  // inclusive suffix sum over lanes
-#pragma unroll
-      for (int d = 1; d < 64; d <<= 1) {
-        const int t = __shfl_down(v, d, 64);
-        if (l + d < 64) v += t;
+  }
+  hb = lo - 1;
+  for (int p = 0;; ++p) {
+    uint32_t* hist = sh.hist[p % 3];
+    lo = max(0, hb - 7);
+    dmask = (2u << (hb - lo)) - 1u;
+    if (listed) {
+      for (int i = tid; i < eq; i += NT) {
+        const uint32_t x = sh.list[i];
+        if ((x & mask) == prefix) atomicAdd(&hist[(x >> lo) & dmask], 1u);
       }
-      int cum = v - s;  // keys in bins above this lane's bins
+    } else {
 #pragma unroll
-      for (int e = 3; e >= 0; --e) {
-        if (cum < k_rem && k_rem <= cum + h[e]) {
-          sh.bcast[0] = 4 * l + e;
-          sh.bcast[1] = cum;
-          sh.bcast[2] = h[e];
-        }
-        cum += h[e];
-      }
+      for (int e = 0; e < E; ++e)
+        if (u[e] != 0u && (u[e] & mask) == prefix) atomicAdd(&hist[(u[e] >> lo) & dmask], 1u);
     }
     __syncthreads();
-    const uint32_t d = (uint32_t)sh.bcast[0];
-    const int above = sh.bcast[1], eq = sh.bcast[2];
-    __syncthreads();  // bcast / hist are rewritten by the next pass
-    k_rem -= above;
+    if (tid < 256) sh.hist[(p + 2) % 3][tid] = 0u;
+    int above2, eq2;
+    find_bin<256>(hist, k_rem, d, above2, eq2);
+    k_rem -= above2;
     prefix |= d << lo;
     mask |= dmask << lo;
-    if (eq == k_rem || lo == 0) {
+    if (eq2 == k_rem || lo == 0) {
       T = prefix;
       shift_out = lo;
       r_eq = k_rem;
@@ -174,58 +242,68 @@ __device__ void radix_select(const uint32_t (&u)[E], uint32_t kmin, uint32_t kma
 }
 
 // Stable compaction over the chunk; emit(out_pos, e) for each kept entry e
-// of this thread, in candidate order. Returns the number kept.
-template <int E, class Emit>
-__device__ int compact(const uint32_t (&u)[E], uint32_t T, int shift, int r_eq, SelShared& sh, Emit emit) {
+// of this thread, in candidate order. Returns the number kept. Each thread
+// builds bit masks of its entries above and equal to the threshold; one
+// scan of the packed counts (above << 16 | equal; each at most 32768) gives
+// both prefixes, and an entry equal to the threshold is kept while fewer
+// than r_eq equal entries precede it. Only the kept entries are visited.
+template <int E, int NT, class Emit>
+__device__ int compact(const uint32_t (&u)[E], uint32_t T, int shift, int r_eq, SelShared<NT>& sh, Emit emit) {
+  static_assert(E <= 32, "one mask bit per entry");
   const uint32_t Ts = T >> shift;
-  int n_eq = 0;
-#pragma unroll
-  for (int e = 0; e < E; ++e) n_eq += (u[e] != 0u && (u[e] >> shift) == Ts);
-  int eq_tot;
-  int eq_rank = block_excl_scan(n_eq, sh, &eq_tot);
-  uint32_t keep = 0;  // bit e: entry e kept (E <= 32)
+  uint32_t gt = 0u, em = 0u;
 #pragma unroll
   for (int e = 0; e < E; ++e) {
-    const bool valid = u[e] != 0u;
     const uint32_t us = u[e] >> shift;
-    const bool eq = valid && us == Ts;
-    const bool sel = (valid && us > Ts) || (eq && eq_rank < r_eq);
-    eq_rank += eq;
-    keep |= (uint32_t)sel << e;
+    const bool valid = u[e] != 0u;
+    gt |= (uint32_t)(valid && us > Ts) << e;
+    em |= (uint32_t)(valid && us == Ts) << e;
   }
-  int tot;
-  int o = block_excl_scan(__popc(keep), sh, &tot);
-#pragma unroll
-  for (int e = 0; e < E; ++e)
-    if ((keep >> e) & 1u) emit(o++, e);
-  return tot;
+  uint32_t tot;
+  const uint32_t ex = block_excl_scan<NT>(((uint32_t)__popc(gt) << 16) | (uint32_t)__popc(em), sh, &tot);
+  const int eq_before = (int)(ex & 0xffffu);
+  int o = (int)(ex >> 16) + min(eq_before, r_eq);
+  uint32_t keep = gt;
+  for (int take = r_eq - eq_before; take > 0 && em != 0u; --take) {
+    keep |= em & (0u - em);  // lowest remaining equal entry
+    em &= em - 1u;
+  }
+  while (keep != 0u) {
+    const int e = __ffs(keep) - 1;
+    keep &= keep - 1u;
+    emit(o++, e);
+  }
+  return (int)(tot >> 16) + min((int)(tot & 0xffffu), r_eq);
 }
 
+template <int NT>
 __device__ void write_trivial(const SelectArgs& a, int r, int t) {
   int32_t* out = a.idx + (int64_t)r * a.out_ld;
-  for (int i = threadIdx.x; i < a.out_ld; i += SEL_NT) out[i] = i <= t ? i : -1;
+  for (int i = threadIdx.x; i < a.out_ld; i += NT) out[i] = i <= t ? i : -1;
   if (threadIdx.x == 0) a.n_sel[r] = t + 1;
 }
 
 // Sinks, window and padding around `count` kept positions already written.
+template <int NT>
 __device__ void finalize(const SelectArgs& a, int r, const RowGeom& gm, int count) {
   int32_t* out = a.idx + (int64_t)r * a.out_ld;
   if (a.mode == SEL_RAW) {
-    for (int i = count + threadIdx.x; i < a.out_ld; i += SEL_NT) out[i] = -1;
+    for (int i = count + threadIdx.x; i < a.out_ld; i += NT) out[i] = -1;
     if (threadIdx.x == 0) a.n_sel[r] = count;
     return;
   }
   const int ns = a.n_sink, W = a.n_window;
-  for (int i = threadIdx.x; i < ns; i += SEL_NT) out[i] = i;
+  for (int i = threadIdx.x; i < ns; i += NT) out[i] = i;
   const int w0 = ns + count;
-  for (int i = threadIdx.x; i < W; i += SEL_NT) out[w0 + i] = gm.t - W + 1 + i;
-  for (int i = w0 + W + threadIdx.x; i < a.out_ld; i += SEL_NT) out[i] = -1;
+  for (int i = threadIdx.x; i < W; i += NT) out[w0 + i] = gm.t - W + 1 + i;
+  for (int i = w0 + W + threadIdx.x; i < a.out_ld; i += NT) out[i] = -1;
   if (threadIdx.x == 0) a.n_sel[r] = w0 + W;
 }
 
-// Chunk statistics: number of nonzero keys, their min and max.
-template <int E>
-__device__ void chunk_stats(const uint32_t (&u)[E], SelShared& sh, int& n_valid, uint32_t& kmin,
+// Chunk statistics: number of nonzero keys, their min and max. Also clears
+// the radix counts and the list (published by the same barrier).
+template <int E, int NT>
+__device__ void chunk_stats(const uint32_t (&u)[E], SelShared<NT>& sh, int& n_valid, uint32_t& kmin,
                             uint32_t& kmax) {
   int cnt = 0;
   uint32_t mn = 0xffffffffu, mx = 0u;
@@ -237,20 +315,29 @@ __device__ void chunk_stats(const uint32_t (&u)[E], SelShared& sh, int& n_valid,
       mx = max(mx, u[e]);
     }
   }
+  cnt = wave_sum(cnt);
   mn = wave_min_u(mn);
   mx = wave_max_u(mx);
   if (lane_id() == 0) {
-    sh.red_w[0][wave_id()] = mn;
-    sh.red_w[1][wave_id()] = mx;
+    sh.st_w[0][wave_id()] = (uint32_t)cnt;
+    sh.st_w[1][wave_id()] = mn;
+    sh.st_w[2][wave_id()] = mx;
   }
-  int tot;
-  block_excl_scan(cnt, sh, &tot);  // its barriers also publish red_w
+  for (int i = threadIdx.x; i < kBins1; i += NT) sh.hist1[i] = 0u;
+  if (threadIdx.x < 256) {
+    sh.hist[0][threadIdx.x] = 0u;
+    sh.hist[1][threadIdx.x] = 0u;
+  }
+  if (threadIdx.x == 0) sh.list_n = 0;
+  __syncthreads();
+  int tot = 0;
   mn = 0xffffffffu;
   mx = 0u;
 #pragma unroll
-  for (int w = 0; w < SEL_NW; ++w) {
-    mn = min(mn, sh.red_w[0][w]);
-    mx = max(mx, sh.red_w[1][w]);
+  for (int w = 0; w < SelShared<NT>::NW; ++w) {
+    tot += (int)sh.st_w[0][w];
+    mn = min(mn, sh.st_w[1][w]);
+    mx = max(mx, sh.st_w[2][w]);
   }
   n_valid = tot;
   kmin = mn;
@@ -293,14 +380,14 @@ __device__ __forceinline__ bool plan_trivial(int k, int n_valid, uint32_t& T, in
   return false;
 }
 
-template <int E>
-__global__ __launch_bounds__(SEL_NT) void select_stage_a(SelectArgs a) {
-  __shared__ SelShared sh;
-  constexpr int CH = SEL_NT * E;
+template <int E, int NT, int MINW>
+__global__ __launch_bounds__(NT, MINW) void select_stage_a(SelectArgs a) {
+  __shared__ SelShared<NT> sh;
+  constexpr int CH = NT * E;
   const int r = blockIdx.x, j = blockIdx.y;
   const RowGeom gm = row_geom(a, r);
   if (gm.trivial) {
-    if (j == 0) write_trivial(a, r, gm.t);
+    if (j == 0) write_trivial<NT>(a, r, gm.t);
     return;
   }
   const int n_chunks = max(1, (gm.nc + CH - 1) / CH);
@@ -312,23 +399,24 @@ __global__ __launch_bounds__(SEL_NT) void select_stage_a(SelectArgs a) {
   load_keys<E>(row, v0, n, u);
   int n_valid;
   uint32_t kmin, kmax, T;
-  chunk_stats<E>(u, sh, n_valid, kmin, kmax);
+  chunk_stats<E, NT>(u, sh, n_valid, kmin, kmax);
   int shift, r_eq;
-  if (!plan_trivial(gm.k, n_valid, T, shift, r_eq)) radix_select<E>(u, kmin, kmax, gm.k, sh, T, shift, r_eq);
+  if (!plan_trivial(gm.k, n_valid, T, shift, r_eq)) radix_select<E, NT>(u, kmin, kmax, gm.k, sh, T, shift, r_eq);
   const int i0 = threadIdx.x * E;
   if (n_chunks == 1) {
     int32_t* out = a.idx + (int64_t)r * a.out_ld + (a.mode == SEL_RAW ? 0 : a.n_sink);
-    const int cnt = compact<E>(u, T, shift, r_eq, sh, [&](int o, int e) { out[o] = pos_of(a, r, v0 + i0 + e); });
-    finalize(a, r, gm, cnt);
+    const int cnt =
+        compact<E, NT>(u, T, shift, r_eq, sh, [&](int o, int e) { out[o] = pos_of(a, r, v0 + i0 + e); });
+    finalize<NT>(a, r, gm, cnt);
   } else {
     const int64_t base = ((int64_t)r * a.max_chunks + j) * a.k_cap;
     int32_t* ws_s = a.ws_score + base;
     int32_t* ws_p = a.ws_pos + base;
-    const int cnt = compact<E>(u, T, shift, r_eq, sh, [&](int o, int e) {
-      ws_s[o] = (int32_t)(u[e] ^ 0x80000000u);
+    const int cnt = compact<E, NT>(u, T, shift, r_eq, sh, [&](int o, int e) {
+      ws_s[o] = row[v0 + i0 + e];  // the score itself (still in cache)
       ws_p[o] = pos_of(a, r, v0 + i0 + e);
     });
-    for (int i = cnt + threadIdx.x; i < a.k_cap; i += SEL_NT) ws_s[i] = kMasked;
+    for (int i = cnt + threadIdx.x; i < a.k_cap; i += NT) ws_s[i] = kMasked;
   }
 }
 
@@ -336,7 +424,7 @@ __global__ __launch_bounds__(SEL_NT) void select_stage_a(SelectArgs a) {
 // entries, padded with INT32_MIN) of one row.
 template <int E>
 __global__ __launch_bounds__(SEL_NT) void select_stage_b(SelectArgs a, int CH) {
-  __shared__ SelShared sh;
+  __shared__ SelShared<SEL_NT> sh;
   const int r = blockIdx.x;
   const RowGeom gm = row_geom(a, r);
   if (gm.trivial) return;
@@ -350,26 +438,41 @@ __global__ __launch_bounds__(SEL_NT) void select_stage_b(SelectArgs a, int CH) {
   load_keys<E>(ws_s, 0, n, u);
   int n_valid;
   uint32_t kmin, kmax, T;
-  chunk_stats<E>(u, sh, n_valid, kmin, kmax);
+  chunk_stats<E, SEL_NT>(u, sh, n_valid, kmin, kmax);
   int shift, r_eq;
-  if (!plan_trivial(gm.k, n_valid, T, shift, r_eq)) radix_select<E>(u, kmin, kmax, gm.k, sh, T, shift, r_eq);
+  if (!plan_trivial(gm.k, n_valid, T, shift, r_eq))
+    radix_select<E, SEL_NT>(u, kmin, kmax, gm.k, sh, T, shift, r_eq);
   const int i0 = threadIdx.x * E;
   int32_t* out = a.idx + (int64_t)r * a.out_ld + (a.mode == SEL_RAW ? 0 : a.n_sink);
-  const int cnt = compact<E>(u, T, shift, r_eq, sh, [&](int o, int e) { out[o] = ws_p[i0 + e]; });
-  finalize(a, r, gm, cnt);
+  const int cnt = compact<E, SEL_NT>(u, T, shift, r_eq, sh, [&](int o, int e) { out[o] = ws_p[i0 + e]; });
+  finalize<SEL_NT>(a, r, gm, cnt);
 }
 
-int chunk_e(int64_t max_nc) {
-  if (max_nc <= SEL_NT * 4) return 4;
-  if (max_nc <= SEL_NT * 16) return 16;
-  return 32;
+// Chunk geometry: E candidates per thread of a 1024-thread workgroup.
+struct SelGeo {
+  int e, chunks;
+};
+
+SelGeo sel_geo(int64_t max_nc) {
+  const int e = max_nc <= (int64_t)SEL_NT * 4 ? 4 : max_nc <= (int64_t)SEL_NT * 16 ? 16 : 32;
+  const int64_t ch = (int64_t)SEL_NT * e;
+  return SelGeo{e, (int)(max_nc <= ch ? 1 : (max_nc + ch - 1) / ch)};
 }
+
+// Stage A runs two workgroups per CU (registers capped at 64 per lane) when
+// there are enough chunks to fill the GPU twice over, so that one
+// workgroup's load latency and barriers overlap the other's work; with fewer
+// chunks it keeps the full register budget, one workgroup per CU.
+constexpr int kTwoPerCuChunks = 2 * 256 * 2;
 
 template <int E>
 hipError_t launch_e(const SelectArgs& a, hipStream_t st) {
   constexpr int CH = SEL_NT * E;
   dim3 ga(a.n_rows, max(a.max_chunks, 1));
-  hipLaunchKernelGGL((select_stage_a<E>), ga, dim3(SEL_NT), 0, st, a);
+  if ((int64_t)a.n_rows * max(a.max_chunks, 1) >= kTwoPerCuChunks)
+    hipLaunchKernelGGL((select_stage_a<E, SEL_NT, 8>), ga, dim3(SEL_NT), 0, st, a);
+  else
+    hipLaunchKernelGGL((select_stage_a<E, SEL_NT, 1>), ga, dim3(SEL_NT), 0, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.max_chunks <= 1) return e;
   // survivors of one row: max_chunks * k_cap
@@ -382,14 +485,17 @@ hipError_t launch_e(const SelectArgs& a, hipStream_t st) {
 
 }  // namespace
 
-int select_chunks(int64_t max_nc) {
-  const int64_t ch = (int64_t)SEL_NT * chunk_e(max_nc);
-  return (int)(max_nc <= ch ? 1 : (max_nc + ch - 1) / ch);
+int select_chunks(int64_t max_nc, int k_cap) { return sel_geo(max_nc).chunks; }
+
+bool select_fits(int64_t max_nc, int k_cap) {
+  const int c = sel_geo(max_nc).chunks;
+  return c <= 1 || (int64_t)c * k_cap <= kSelMaxSurvivors;
 }
 
 void select_plan(SelectArgs& a, int64_t max_nc) {
-  a.chunk_e = chunk_e(max_nc);
-  a.max_chunks = select_chunks(max_nc);
+  const SelGeo g = sel_geo(max_nc);
+  a.chunk_e = g.e;
+  a.max_chunks = g.chunks;
 }
 
 size_t select_ws_bytes(int n_rows, int max_chunks, int k_cap) {
@@ -406,14 +512,13 @@ void select_bind_ws(SelectArgs& a, void* ws, int n_rows) {
   a.ws_pos = a.ws_score + (size_t)n_rows * a.max_chunks * a.k_cap;
 }
 
-// max_chunks must equal select_chunks(max candidates per row) and the stage-B
+// The geometry must come from select_plan (k_cap set first), and the stage-B
 // survivor count max_chunks * k_cap must fit 32 * 1024 entries.
 hipError_t launch_select(const SelectArgs& a, hipStream_t st) {
   if (a.n_rows <= 0) return hipSuccess;
   if (a.max_chunks > 1 && (int64_t)a.max_chunks * a.k_cap > kSelMaxSurvivors) return hipErrorInvalidValue;
-  const int E = a.chunk_e;
-  if (E == 4) return launch_e<4>(a, st);
-  if (E == 16) return launch_e<16>(a, st);
+  if (a.chunk_e == 4) return launch_e<4>(a, st);
+  if (a.chunk_e == 16) return launch_e<16>(a, st);
   return launch_e<32>(a, st);
 }
 
