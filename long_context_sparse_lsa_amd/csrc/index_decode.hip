@@ -118,15 +118,13 @@ __device__ __forceinline__ void scan_keys(const ScoreArgs& a, const v4i (&A)[HI 
         const int v = v0 + 32 * t + c;
         const int p = v < v1 ? pos_of(v) : -1;
         if constexpr (NQ == 1) {
-          int s = query_sum<MB, MQ, FOLD>(acc, 0, wl);
-          s += shfl_xor_i(s, 32);
+          const int s = xor32_sum(query_sum<MB, MQ, FOLD>(acc, 0, wl));
           if (g == 0) store(0, v, p, s);
         } else {
           const int s0 = query_sum<MB, MQ, FOLD>(acc, 0, wl);
           const int s1 = query_sum<MB, MQ, FOLD>(acc, 1, wl);
           // lane half g finishes query g
-          const int mine = (g ? s1 : s0) + shfl_xor_i(g ? s0 : s1, 32);
-          store(g, v, p, mine);
+          store(g, v, p, pair_sum32(s0, s1));
         }
       }
       load(t + kDepth, ring[u]);

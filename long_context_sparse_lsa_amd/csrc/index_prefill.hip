@@ -148,14 +148,15 @@ __device__ __forceinline__ void score_chunk(const ScoreArgs& a, const v4i (&A)[k
         read_b<DI, KS>(tile, nb, Bk);
 #pragma unroll
         for (int qp = 0; qp < kQW; qp += 2) {
-          v16i acc[MB];
-          block_mfma<MB, KS>(A[qp], Bk, acc);
-          const int s0 = head_sum<MB, FOLD>(acc, wl);
-          block_mfma<MB, KS>(A[qp + 1], Bk, acc);
-          const int s1 = head_sum<MB, FOLD>(acc, wl);
-          // half g keeps query qp + g's own partial and receives the other half's
-          const int recv = shfl_xor_i(g ? s0 : s1, 32);
-          sc[(int64_t)(row0 + qp + g) * a.ld + v0 + 32 * nb + c] = (g ? s1 : s0) + recv;
+          // both queries' MFMAs first: the first epilogue then runs while
+          // the second query's products finish
+          v16i acc0[MB], acc1[MB];
+          block_mfma<MB, KS>(A[qp], Bk, acc0);
+          block_mfma<MB, KS>(A[qp + 1], Bk, acc1);
+          const int s0 = head_sum<MB, FOLD>(acc0, wl);
+          const int s1 = head_sum<MB, FOLD>(acc1, wl);
+          // lane half g ends with query qp + g's full sum
+          sc[(int64_t)(row0 + qp + g) * a.ld + v0 + 32 * nb + c] = pair_sum32(s0, s1);
         }
       }
     } else {
@@ -178,8 +179,7 @@ __device__ __forceinline__ void score_chunk(const ScoreArgs& a, const v4i (&A)[k
             const int s0 = head_sum<MB, FOLD>(acc, wl);
             block_mfma<MB, KS>(A[qp + 1], Bk, acc);
             const int s1 = head_sum<MB, FOLD>(acc, wl);
-            const int recv = shfl_xor_i(g ? s0 : s1, 32);
-            full = (g ? s1 : s0) + recv;
+            full = pair_sum32(s0, s1);
           }
           if (row < a.n_q && v < v_end) {
             int32_t* dst = sc + (int64_t)row * a.ld + v;

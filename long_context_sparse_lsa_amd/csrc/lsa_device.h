@@ -36,6 +36,16 @@ __device__ __forceinline__ int shfl_xor_i(int v, int m) { return __shfl_xor(v, m
 __device__ __forceinline__ float shfl_xor_f(float v, int m) { return __shfl_xor(v, m, 64); }
 
 // float -> bfloat16 bits, round to nearest even (inputs here are finite).
+// Lane-half exchange without LDS (v_permlane32_swap_b32): lanes 0-31 get
+// lo[l] + lo[l + 32] and lanes 32-63 get hi[l - 32] + hi[l], i.e. lane half
+// g holds the full 64-lane pair sum of its own operand.
+__device__ __forceinline__ int pair_sum32(int lo, int hi) {
+  const auto r = __builtin_amdgcn_permlane32_swap((unsigned)lo, (unsigned)hi, false, false);
+  return (int)r[0] + (int)r[1];
+}
+// v[l] + v[l ^ 32] in every lane.
+__device__ __forceinline__ int xor32_sum(int v) { return pair_sum32(v, v); }
+
 __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
   uint32_t u = __float_as_uint(f);
   uint32_t r = u + 0x7fffu + ((u >> 16) & 1u);

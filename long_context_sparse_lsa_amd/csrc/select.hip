@@ -162,8 +162,8 @@ __device__ __forceinline__ void find_bin(const uint32_t* hist, int k_rem, uint32
 // Threshold of the k-th largest nonzero key of the chunk (0 < k < #nonzero).
 // On return an entry u is kept iff (u >> shift) > (T >> shift), or
 // (u >> shift) == (T >> shift) and it is among the first r_eq such entries.
-// The first pass counts every key by a digit of up to 11 bits starting at
-// the highest bit in which the chunk's keys differ. The keys of the bin that
+// The first pass counts every key by a digit of up to 11 bits (8 for small
+// chunks) starting at the highest bit in which the chunk's keys differ. The keys of the bin that
 // holds the threshold (usually a few hundred) are then copied to an LDS list
 // when they fit, and further 8-bit passes count only those. Later pass p
 // counts into hist[p % 3] (hist[0] and hist[1] start cleared); after its
@@ -183,8 +183,11 @@ __device__ void radix_select(const uint32_t (&u)[E], uint32_t kmin, uint32_t kma
   uint32_t mask = hb == 31 ? 0u : ~((2u << hb) - 1u);
   uint32_t prefix = kmax & mask;
   int k_rem = k;
-  // pass 1 over all keys (all nonzero keys share the bits above hb)
-  int lo = max(0, hb - 10);
+  // pass 1 over all keys (all nonzero keys share the bits above hb); small
+  // chunks take an 8-bit digit, whose counts are cheaper to search
+  constexpr int B1 = E >= 16 ? kBins1 : 256;
+  constexpr int W1 = B1 == 256 ? 8 : 11;
+  int lo = max(0, hb - (W1 - 1));
   uint32_t dmask = (2u << (hb - lo)) - 1u;
 #pragma unroll
   for (int e = 0; e < E; ++e)
@@ -192,7 +195,7 @@ __device__ void radix_select(const uint32_t (&u)[E], uint32_t kmin, uint32_t kma
   __syncthreads();
   uint32_t d;
   int above, eq;
-  find_bin<kBins1>(sh.hist1, k_rem, d, above, eq);
+  find_bin<B1>(sh.hist1, k_rem, d, above, eq);
   k_rem -= above;
   prefix |= d << lo;
   mask |= dmask << lo;
