@@ -7,12 +7,16 @@ to 2048 keys; 64 query heads on one bf16 KV head of dim 128. One step =
 fused indexer scoring + top-k selection for every row (lsa_select_topk),
 then sparse attention for every row and layer (lsa_sparse_attn_prefill).
 Decode workloads (--config c3 / c4) time one decode step: selection for
-the target row of every sequence, then split-KV attention with the merge.
+the target row of every sequence, then split-KV attention with the merge;
+the step is captured once as a HIP graph and the timed steps replay it
+(per-call parts come from an eager pass of the same steps).
 
 Inputs are synthetic and seeded, and resident in HBM before timing starts.
-Prints ONE JSON line: throughput, per-call times measured with HIP events on
-the stream the kernels run on, the roofline of the dominant call, and the
-CPU oracle timed on a bounded sample of the same workload.
+Prints ONE JSON line: throughput over the timed steps, per-call times from
+HIP events on the stream the calls run on, per-kernel launch times from the
+library's own event timing over the same number of further steps, the
+roofline of the kernel with the most time per step, and the CPU oracle timed
+on a bounded sample of the same workload.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--config c2]
 """
@@ -38,6 +42,8 @@ def parse():
     p.add_argument("--config", default="c2", choices=["c1", "c2", "c3", "c4", "c5"])
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=10.0, help="time budget of the oracle sample")
+    p.add_argument("--copy-probe", action="store_true",
+                   help="end with three plain 1 GiB device copies (HBM counter calibration)")
     return p.parse_args()
 
 
@@ -84,12 +90,77 @@ def cpu_threads():
     return len(os.sched_getaffinity(0))
 
 
-def roofline(bound, name, kernels, work, ms, peak, unit):
-    """work: ops (unit T*/s) or bytes (unit GB/s) of one call; ms: mean call time."""
+KERNELS = ("index_prefill_kernel", "index_decode_kernel", "index_score_kernel", "select_stage_a",
+           "select_stage_b", "attn_prefill_kernel", "attn_decode_partial", "attn_decode_merge")
+
+
+def kernel_times(L, torch, step, steps, park=False):
+    """Per-kernel launch durations over `steps` more steps, from the HIP events
+    the library records on the launch stream around each of its kernel
+    launches: {name: (mean ms per launch, launches per step)}. park: first
+    hold the GPU on a spin kernel so that the host queues every launch before
+    the GPU reaches it (short launches would otherwise include host latency
+    between their two events)."""
+    L.lsa_kernel_timing(True)
+    try:
+        if park:
+            torch.cuda._sleep(50_000_000)
+        for _ in range(steps):
+            step()
+        torch.cuda.synchronize()
+        out = {}
+        for name in KERNELS:
+            ms, n = L.lsa_kernel_time(name)
+            if n:
+                out[name] = (ms, n / steps)
+    finally:
+        L.lsa_kernel_timing(False)
+    return out
+
+
+def roofline(bound, name, work_per_step, kt, peak, unit):
+    """Roofline of one kernel: work_per_step ops (unit T*/s) or bytes (GB/s)
+    done by its launches in one step, over their event-measured duration."""
+    ms, per_step = kt[name]
+    work = work_per_step / per_step  # per launch (mean)
     achieved = work / (ms * 1e-3) / (1e9 if unit == "GB/s" else 1e12)
-    return {"bound": bound, "kernel": name, "kernels": kernels, "achieved": round(achieved, 2), "peak": peak,
-            "unit": unit, "frac": round(achieved / peak, 4), "traffic": None,
-            "work_per_call": work, "ms_per_call": round(ms, 4)}
+    return {"bound": bound, "kernel": name, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
+            "frac": round(achieved / peak, 4), "traffic": None,
+            "work_per_launch": work, "ms_per_launch": round(ms, 4), "launches_per_step": per_step}
+
+
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.txt")
+
+
+def measured_traffic(workload, kernel):
+    """HBM bytes per launch (FETCH_SIZE + WRITE_SIZE, copy-calibrated) of the
+    kernel on this workload from profiles/hbm_traffic.txt, or None when the
+    file lacks it or was taken on other kernel sources."""
+    from long_context_sparse_lsa_amd.profile_summary import sources_hash
+    try:
+        lines = open(TRAFFIC_FILE).read().splitlines()
+    except OSError:
+        return None
+    head = [ln for ln in lines if ln.startswith("sources:")]
+    if not head or head[0].split()[1] != sources_hash():
+        return None
+    for ln in lines:
+        f = ln.split()
+        if len(f) >= 4 and f[0] == workload and f[1] == kernel:
+            kv = dict(x.split("=") for x in f[2:])
+            return int(kv["fetch_bytes"]) + int(kv["write_bytes"])
+    return None
+
+
+def dominant(kt, candidates):
+    """The candidate kernel with the most time per step."""
+    have = [k for k in candidates if k in kt]
+    return max(have, key=lambda k: kt[k][0] * kt[k][1])
+
+
+def kernel_parts(kt):
+    return {k: {"ms_per_launch": round(ms, 4), "launches_per_step": n, "ms_per_step": round(ms * n, 4)}
+            for k, (ms, n) in kt.items()}
 
 
 def prefill_cpu_baseline(wl, q_idx, k_idx, w, q, k, v, seconds):
@@ -150,13 +221,15 @@ def run_prefill(args, wl, torch):
     gathered = 2.0 * wl.D * 2 * n_sel_sum
     sel_tops = i8_ops / (sel_ms * 1e-3) / 1e12
     attn_tflops = attn_flop / (attn_ms * 1e-3) / 1e12
-    if sel_ms >= attn_ms * wl.n_layers:  # the call that takes most of the step
-        roof = roofline("mfma", "lsa_select_topk",
-                        "index_prefill_kernel (int8 MFMA scores) + select_stage_a/b (top-k)",
-                        i8_ops, sel_ms, PEAK_I8_TOPS, "TOP/s")
-    else:
-        roof = roofline("mfma", "lsa_sparse_attn_prefill", "attn_prefill_kernel (bf16 MFMA on gathered K/V)",
-                        attn_flop, attn_ms, PEAK_BF16_TFLOPS, "TFLOP/s")
+    kt = kernel_times(L, torch, lambda: step(plain), args.steps)
+    # algorithmic work of each kernel in one step
+    work = {"index_prefill_kernel": ("mfma", i8_ops, PEAK_I8_TOPS, "TOP/s"),
+            "select_stage_a": ("hbm", 4.0 * pairs, PEAK_HBM_GBS, "GB/s"),  # the scores it reads
+            "attn_prefill_kernel": ("mfma", attn_flop * wl.n_layers, PEAK_BF16_TFLOPS, "TFLOP/s")}
+    name = dominant(kt, work)
+    bound, wk, peak, unit = work[name]
+    roof = roofline(bound, name, wk, kt, peak, unit)
+    roof["traffic"] = measured_traffic(wl.name, name)
     out = {
         "metric": "LSA prefill tokens/s",
         "value": round(wl.L / (ms_step * 1e-3), 1),
@@ -171,7 +244,8 @@ def run_prefill(args, wl, torch):
         "parts": {"select_ms": round(sel_ms, 4), "select_int8_tops": round(sel_tops, 1),
                   "scored_pairs": pairs,
                   "attn_ms_per_layer": round(attn_ms, 4), "attn_bf16_tflops": round(attn_tflops, 1),
-                  "attn_gather_gbs": round(gathered / (attn_ms * 1e-3) / 1e9, 1)},
+                  "attn_gather_gbs": round(gathered / (attn_ms * 1e-3) / 1e9, 1),
+                  "kernels": kernel_parts(kt)},
         "roofline": roof,
     }
     if not args.no_cpu_baseline:
@@ -234,13 +308,26 @@ def run_decode(args, wl, torch):
     for _ in range(args.warmup):
         step(plain)
     torch.cuda.synchronize()
+    # per-call parts from one eager pass of the steps
     t0 = time.perf_counter()
     for _ in range(args.steps):
         step(timer)
     torch.cuda.synchronize()
-    us_step = (time.perf_counter() - t0) * 1e6 / args.steps
+    us_eager = (time.perf_counter() - t0) * 1e6 / args.steps
     sel_ms, _ = timer.ms("select")
     attn_ms, _ = timer.ms("attn")
+    # the timed steps: one decode step captured once as a HIP graph and
+    # replayed, as a serving loop runs a fixed-shape step
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step(plain)
+    graph.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        graph.replay()
+    torch.cuda.synchronize()
+    us_step = (time.perf_counter() - t0) * 1e6 / args.steps
     K_tot = wl.K_tot
     kv_bytes = wl.B * K_tot * wl.D * 2 * 2
     qo_bytes = 2 * wl.B * wl.n_q * wl.H * wl.D * 2
@@ -250,13 +337,17 @@ def run_decode(args, wl, torch):
     else:
         idx_bytes = wl.B * N * wl.d_I
     step_bytes = idx_bytes + kv_bytes + qo_bytes
-    if sel_ms >= attn_ms:
-        roof = roofline("hbm", "lsa_hier_select" if wl.blk else "lsa_select_topk",
-                        "index_score_kernel (indexer key scan) + select_stage_a/b", idx_bytes, sel_ms,
-                        PEAK_HBM_GBS, "GB/s")
-    else:
-        roof = roofline("hbm", "lsa_sparse_attn_decode", "attn_decode_partial + attn_decode_merge",
-                        kv_bytes + qo_bytes, attn_ms, PEAK_HBM_GBS, "GB/s")
+    kt = kernel_times(L, torch, lambda: step(plain), args.steps, park=True)
+    # algorithmic bytes of each kernel in one step: the indexer keys it scans,
+    # the scores the selection reads, the K/V rows and q the attention reads
+    n_scored = (N // wl.blk + wl.n_blk_recall * wl.blk) if wl.blk else N
+    work = {"index_decode_kernel": ("hbm", idx_bytes, PEAK_HBM_GBS, "GB/s"),
+            "select_stage_a": ("hbm", 4.0 * wl.B * n_scored, PEAK_HBM_GBS, "GB/s"),
+            "attn_decode_partial": ("hbm", kv_bytes + qo_bytes // 2, PEAK_HBM_GBS, "GB/s")}
+    name = dominant(kt, work)
+    bound, wk, peak, unit = work[name]
+    roof = roofline(bound, name, wk, kt, peak, unit)
+    roof["traffic"] = measured_traffic(wl.name, name)
     out = {
         "metric": "LSA decode us/step",
         "value": round(us_step, 2), "unit": "us/step",
@@ -265,10 +356,13 @@ def run_decode(args, wl, torch):
         "higher_is_better": False, "scaling": "weak", "vs_baseline": None,
         "dtype": "int8+bf16", "data": "synthetic (seeded int8 U[-16,15] indexer, bf16 N(0,1) q and caches)",
         "config": {"workload": wl.name, "global_batch": wl.B, "context": N, "n_q": wl.n_q, "H": wl.H,
-                   "K_tot": K_tot, "n_split": wl.n_split, "hier_blk": wl.blk, "parallelism": "none"},
-        "parts": {"select_us": round(sel_ms * 1e3, 2), "attn_us": round(attn_ms * 1e3, 2),
+                   "K_tot": K_tot, "n_split": wl.n_split, "hier_blk": wl.blk, "launch": "hip_graph_replay",
+                   "parallelism": "none"},
+        "parts": {"eager_us_per_step": round(us_eager, 2),
+                  "select_us": round(sel_ms * 1e3, 2), "attn_us": round(attn_ms * 1e3, 2),
                   "step_bytes": step_bytes,
-                  "step_hbm_frac": round(step_bytes / (us_step * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)},
+                  "step_hbm_frac": round(step_bytes / (us_step * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
+                  "kernels": kernel_parts(kt)},
         "roofline": roof,
     }
     if not args.no_cpu_baseline:
@@ -296,6 +390,13 @@ def main():
     L.load()
     wl = configs.BY_ID[args.config]
     out = run_prefill(args, wl, torch) if wl.kind == "prefill" else run_decode(args, wl, torch)
+    if args.copy_probe:
+        a = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        del a, b
     print(json.dumps(out), flush=True)
 
 

@@ -141,6 +141,22 @@ int32_t lsa_sparse_attn_decode(const lsa_bf16* q, const lsa_bf16* k_cache,
                                int32_t n_split, float scale, lsa_bf16* o, float* lse,
                                void* ws, size_t ws_bytes, size_t* ws_needed, void* stream);
 
+/* Kernel timing, a measurement aid (not part of the method). While on, every
+ * kernel launch of the library is bracketed by two HIP events recorded on
+ * the launch stream; a launch costs two event records more.
+ *   lsa_kernel_timing(on): waits for the events still pending, clears all
+ *     records, then starts (on != 0) or stops (on == 0) recording.
+ *   lsa_kernel_time(name, ms_mean, launches): mean duration in ms and count
+ *     of the recorded launches of kernel `name` (waits for their events).
+ *     Names: "index_prefill_kernel", "index_decode_kernel",
+ *     "index_score_kernel", "select_stage_a", "select_stage_b",
+ *     "attn_prefill_kernel", "attn_decode_partial", "attn_decode_merge",
+ *     "block_summary_kernel". An unknown name reports 0 launches.
+ * Errors: LSA_INVALID_ARG for NULL pointers, LSA_HIP for a failed event call.
+ * Not for concurrent use from several host threads while launches run. */
+int32_t lsa_kernel_timing(int32_t on);
+int32_t lsa_kernel_time(const char* name, float* ms_mean, int32_t* launches);
+
 #ifdef __cplusplus
 }
 #endif

@@ -45,6 +45,8 @@ SIGNATURES = {
     "lsa_hier_select": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, SelectCfg, _P, _P, _P, _Z, _ZP, _P]),
     "lsa_sparse_attn_prefill": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _P, _P, _P]),
     "lsa_sparse_attn_decode": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _F, _P, _P, _P, _Z, _ZP, _P]),
+    "lsa_kernel_timing": (_I, [_I]),
+    "lsa_kernel_time": (_I, [ctypes.c_char_p, ctypes.POINTER(_F), ctypes.POINTER(_I)]),
 }
 
 _lib = None
@@ -245,3 +247,16 @@ def lsa_sparse_attn_decode(q, k_cache, v_cache, idx, n_sel, n_split=8, scale=Non
     _check("lsa_sparse_attn_decode", lib.lsa_sparse_attn_decode(*args, _ptr(o), _ptr(lse), _ptr(ws), ws.numel(),
                                                                 None, _stream()))
     return (o, lse) if want_lse else o
+
+
+def lsa_kernel_timing(on):
+    """Start (True) or stop (False) per-launch HIP event timing in the
+    library; either way the earlier records are cleared."""
+    _check("lsa_kernel_timing", load().lsa_kernel_timing(1 if on else 0))
+
+
+def lsa_kernel_time(name):
+    """(mean ms, launches) of kernel `name` since timing was switched on."""
+    ms, n = _F(), _I()
+    _check("lsa_kernel_time", load().lsa_kernel_time(name.encode(), ctypes.byref(ms), ctypes.byref(n)))
+    return float(ms.value), int(n.value)

@@ -372,6 +372,7 @@ hipError_t launch_attn_prefill(const PrefillArgs& a, hipStream_t st) {
   const int HB = (a.H + 32 * NB - 1) / (32 * NB);
   const int64_t groups = (int64_t)a.B * a.L * HB;
   dim3 grid((unsigned)(((groups + 3) / 4 + 7) / 8 * 8));
+  KernelTimer kt("attn_prefill_kernel", st);
   if (NB == 1) hipLaunchKernelGGL(attn_prefill_kernel<1>, grid, dim3(256), 0, st, a);
   else hipLaunchKernelGGL(attn_prefill_kernel<2>, grid, dim3(256), 0, st, a);
   return hipGetLastError();
@@ -597,6 +598,7 @@ size_t decode_ws_bytes(int B, int n_q, int H, int n_split) {
 template <int TW, int KS>
 static void launch_partial_tk(const DecodeArgs& a, int T, hipStream_t st) {
   dim3 grid((T + TW - 1) / TW, a.n_split, a.B);
+  KernelTimer kt("attn_decode_partial", st);
   hipLaunchKernelGGL((attn_decode_partial<TW, KS>), grid, dim3(64 * TW * KS), 0, st, a);
 }
 
@@ -621,6 +623,7 @@ hipError_t launch_attn_decode(const DecodeArgs& a, hipStream_t st) {
   hipError_t e = launch_partial(a, st);
   if (e != hipSuccess) return e;
   const dim3 grid((unsigned)(((int64_t)a.B * a.n_q * a.H + 7) / 8));
+  KernelTimer kt("attn_decode_merge", st);
   if (a.n_split <= 1) hipLaunchKernelGGL(attn_decode_merge<1>, grid, dim3(256), 0, st, a);
   else if (a.n_split <= 2) hipLaunchKernelGGL(attn_decode_merge<2>, grid, dim3(256), 0, st, a);
   else if (a.n_split <= 4) hipLaunchKernelGGL(attn_decode_merge<4>, grid, dim3(256), 0, st, a);

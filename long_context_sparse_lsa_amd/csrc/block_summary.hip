@@ -58,6 +58,7 @@ hipError_t launch_block_summary(const int8_t* k, int B, int n_k, int d_I, int bl
                                 hipStream_t st) {
   const int nb = (n_k + blk - 1) / blk;
   const int64_t threads = (int64_t)B * nb * (d_I / 16);
+  KernelTimer kt("block_summary_kernel", st);
   hipLaunchKernelGGL(block_summary_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0,
                      st, k, B, n_k, d_I, blk, kb);
   return hipGetLastError();

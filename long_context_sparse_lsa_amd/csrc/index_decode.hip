@@ -208,6 +208,7 @@ hipError_t launch_t(const ScoreArgs& a, hipStream_t st) {
   dim3 grid((unsigned)qtiles, (unsigned)((a.n_keys + per_wg - 1) / per_wg), (unsigned)a.B);
   int fold_ok = 1;
   for (int h = 0; h < a.H_I; ++h) fold_ok &= a.w.w[h] >= 0;
+  KernelTimer kt("index_decode_kernel", st);
   hipLaunchKernelGGL((index_decode_kernel<HI, DI>), grid, dim3(64 * kWaves), 0, st, a, (int)kpw, fold_ok);
   return hipGetLastError();
 }

@@ -265,6 +265,7 @@ __global__ __launch_bounds__(kThreads, 2) void index_prefill_kernel(ScoreArgs a,
 template <int HI, int DI>
 hipError_t launch_t(const ScoreArgs& a, int fold_ok, hipStream_t st) {
   dim3 grid((a.n_keys + kChunkKeys - 1) / kChunkKeys, (a.n_q + kQT - 1) / kQT, a.B);
+  KernelTimer kt("index_prefill_kernel", st);
   hipLaunchKernelGGL((index_prefill_kernel<HI, DI>), grid, dim3(kThreads), 0, st, a, fold_ok);
   return hipGetLastError();
 }

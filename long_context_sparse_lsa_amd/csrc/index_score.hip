@@ -159,6 +159,7 @@ static hipError_t launch_t(const ScoreArgs& a, hipStream_t st) {
   const int QT = n_tiles >= 16 ? 4 : 1;
   const int KC = QT == 4 ? 256 : 512;
   dim3 grid((n_tiles + QT - 1) / QT, (a.n_keys + KC - 1) / KC, a.B);
+  KernelTimer kt("index_score_kernel", st);
   hipLaunchKernelGGL((index_score_kernel<HI, DI>), grid, dim3(256), 0, st, a, QT, KC);
   return hipGetLastError();
 }

@@ -113,4 +113,19 @@ hipError_t launch_attn_decode(const DecodeArgs& a, hipStream_t st);
 hipError_t launch_block_summary(const int8_t* k, int B, int n_k, int d_I, int blk, int8_t* kb,
                                 hipStream_t st);
 
+// Brackets one kernel launch with HIP events on its stream while kernel
+// timing (lsa_kernel_timing) is on; name is the kernel's base name.
+class KernelTimer {
+ public:
+  KernelTimer(const char* name, hipStream_t st);
+  ~KernelTimer();
+  KernelTimer(const KernelTimer&) = delete;
+  KernelTimer& operator=(const KernelTimer&) = delete;
+
+ private:
+  const char* name_;
+  hipStream_t st_;
+  void* a_;
+};
+
 }  // namespace lsa

@@ -472,14 +472,18 @@ template <int E>
 hipError_t launch_e(const SelectArgs& a, hipStream_t st) {
   constexpr int CH = SEL_NT * E;
   dim3 ga(a.n_rows, max(a.max_chunks, 1));
-  if ((int64_t)a.n_rows * max(a.max_chunks, 1) >= kTwoPerCuChunks)
-    hipLaunchKernelGGL((select_stage_a<E, SEL_NT, 8>), ga, dim3(SEL_NT), 0, st, a);
-  else
-    hipLaunchKernelGGL((select_stage_a<E, SEL_NT, 1>), ga, dim3(SEL_NT), 0, st, a);
+  {
+    KernelTimer kt("select_stage_a", st);
+    if ((int64_t)a.n_rows * max(a.max_chunks, 1) >= kTwoPerCuChunks)
+      hipLaunchKernelGGL((select_stage_a<E, SEL_NT, 8>), ga, dim3(SEL_NT), 0, st, a);
+    else
+      hipLaunchKernelGGL((select_stage_a<E, SEL_NT, 1>), ga, dim3(SEL_NT), 0, st, a);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.max_chunks <= 1) return e;
   // survivors of one row: max_chunks * k_cap
   const int64_t nb = (int64_t)a.max_chunks * a.k_cap;
+  KernelTimer kt("select_stage_b", st);
   if (nb <= SEL_NT * 4) hipLaunchKernelGGL((select_stage_b<4>), dim3(a.n_rows), dim3(SEL_NT), 0, st, a, CH);
   else if (nb <= SEL_NT * 16) hipLaunchKernelGGL((select_stage_b<16>), dim3(a.n_rows), dim3(SEL_NT), 0, st, a, CH);
   else hipLaunchKernelGGL((select_stage_b<32>), dim3(a.n_rows), dim3(SEL_NT), 0, st, a, CH);

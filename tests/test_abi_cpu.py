@@ -150,3 +150,15 @@ def test_attention_checks():
     bad[12] = 65        # n_split
     assert lib.lsa_sparse_attn_decode(*bad, f, None, None, 0, ctypes.byref(need), None) == L.LSA_UNSUPPORTED
     assert lib.lsa_sparse_attn_decode(*dargs, f, None, f, 100, None, None) == L.LSA_WORKSPACE
+
+
+def test_kernel_timing_without_launches():
+    """Timing on/off and reads touch no GPU while nothing was recorded."""
+    lib = L.load()
+    ms, n = ctypes.c_float(1.0), ctypes.c_int32(7)
+    assert lib.lsa_kernel_time(None, ctypes.byref(ms), ctypes.byref(n)) == L.LSA_INVALID_ARG
+    assert lib.lsa_kernel_time(b"attn_prefill_kernel", None, ctypes.byref(n)) == L.LSA_INVALID_ARG
+    assert lib.lsa_kernel_timing(0) == L.LSA_OK
+    assert lib.lsa_kernel_time(b"attn_prefill_kernel", ctypes.byref(ms), ctypes.byref(n)) == L.LSA_OK
+    assert n.value == 0 and ms.value == 0.0
+    assert lib.lsa_kernel_timing(0) == L.LSA_OK

@@ -349,3 +349,51 @@ def test_c1_end_to_end_and_cli_reuse():
             ref, _ = O.attend(qf[t], kf, vf, sel, wl.scale)
             err.add(of[t], ref)
         err.check()
+
+
+def test_kernel_timing_records_launches():
+    """The event timing aid counts each kernel launch and reports positive
+    durations; switching it off clears the records."""
+    wl = configs.C1
+    q_idx, k_idx, w = synth.indexer_inputs(wl, DEV)
+    q, k, v = synth.attention_inputs(wl, 0, DEV)
+    L.lsa_kernel_timing(True)
+    try:
+        idx, n_sel = L.lsa_select_topk(q_idx, k_idx, w, wl.n_sink, wl.n_window, wl.k_dyn, q_off=0)
+        for _ in range(3):
+            L.lsa_sparse_attn_prefill(q, k, v, idx, n_sel)
+        ms, n = L.lsa_kernel_time("attn_prefill_kernel")
+        assert n == 3 and ms > 0.0
+        ms, n = L.lsa_kernel_time("select_stage_a")
+        assert n >= 1 and ms > 0.0
+        assert L.lsa_kernel_time("no_such_kernel") == (0.0, 0)
+    finally:
+        L.lsa_kernel_timing(False)
+    assert L.lsa_kernel_time("attn_prefill_kernel")[1] == 0
+
+
+def test_decode_step_graph_replays_match_eager():
+    """A decode step (selection + split-KV attention) captured as a HIP
+    graph gives the eager result on every replay, with eager work and
+    synchronisations of the program between the replays."""
+    wl = configs.C3.scaled(B=3, L=20000)
+    q_idx, k_idx, w = synth.indexer_inputs(wl, DEV)
+    q, kc, vc = synth.attention_inputs(wl, 0, DEV)
+    q1 = q_idx[:, None].contiguous()
+
+    def step():
+        idx, n_sel = L.lsa_select_topk(q1, k_idx, w, wl.n_sink, wl.n_window, wl.k_dyn, q_off=wl.L - 1)
+        return idx, L.lsa_sparse_attn_decode(q, kc, vc, idx, n_sel, n_split=wl.n_split)
+
+    idx_e, o_e = step()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        idx_g, o_g = step()
+    for rep in range(4):
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(idx_g, idx_e), f"replay {rep}: idx"
+        assert torch.equal(o_g, o_e), f"replay {rep}: o"
+        step()   # eager work between replays
+        torch.cuda.synchronize()
