@@ -234,15 +234,36 @@ __device__ __forceinline__ void attn_block(const v8bf (&Q)[NB][8], const char* b
   const bool valid = (unsigned)pos < (unsigned)n_k;
   const uint32_t vmask = (uint32_t)__ballot(valid);
 
-  // ---- S^T = K * Q^T (A operand: key row c, dims g*64 + 8j from LDS)
+  // ---- S^T = K * Q^T (A operand: key row c, dims g*64 + 8j from LDS). With
+  // 64 heads per wave (one wave per SIMD, registers to spare) every operand
+  // read of the block is issued before the products that consume it, so LDS
+  // latency is paid once per block rather than once per fragment.
   v16f S[NB];
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) S[nb] = v16f{};
+  constexpr bool kAhead = NB == 2;
+  v8bf Ka[8];
+  if constexpr (kAhead) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) Ka[j] = *(const v8bf*)(blk + c * kKRow + g * 128 + 16 * j);
+  }
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
-    const v8bf Ka = *(const v8bf*)(blk + c * kKRow + g * 128 + 16 * j);
+    if constexpr (!kAhead) Ka[j] = *(const v8bf*)(blk + c * kKRow + g * 128 + 16 * j);
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) S[nb] = mfma_bf16_32x32x16(Ka, Q[nb][j], S[nb]);
+    for (int nb = 0; nb < NB; ++nb) S[nb] = mfma_bf16_32x32x16(Ka[j], Q[nb][j], S[nb]);
+  }
+  if constexpr (kAhead) {
+    // keep the eight K reads ahead of the sixteen products in the schedule
+    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);
+  }
+  v8bf Va[4][2];
+  if constexpr (kAhead) {
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+      for (int js = 0; js < 2; ++js) Va[mb][js] = read_vt(blk, vt_off, mb, js);
   }
 
     // ---- softmax numerators in base 2 against a per-head reference st.m:
@@ -268,7 +289,7 @@ __device__ __forceinline__ void attn_block(const v8bf (&Q)[NB][8], const char* b
       float m = S[nb][0];
 #pragma unroll
       for (int i = 1; i < 16; ++i) m = fmaxf(m, S[nb][i]);
-      mx[nb] = fmaxf(m, shfl_xor_f(m, 32)) * sl2;
+      mx[nb] = xor32_max(m) * sl2;
       need = need || mx[nb] > st.m[nb] + kSlack;
     }
     if (__any(need)) {
@@ -308,9 +329,9 @@ __device__ __forceinline__ void attn_block(const v8bf (&Q)[NB][8], const char* b
     for (int mb = 0; mb < 4; ++mb) {
 #pragma unroll
       for (int js = 0; js < 2; ++js) {
-        const v8bf Va = read_vt(blk, vt_off, mb, js);
+        if constexpr (!kAhead) Va[mb][js] = read_vt(blk, vt_off, mb, js);
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb) st.o[mb][nb] = mfma_bf16_32x32x16(Va, P[nb][js], st.o[mb][nb]);
+        for (int nb = 0; nb < NB; ++nb) st.o[mb][nb] = mfma_bf16_32x32x16(Va[mb][js], P[nb][js], st.o[mb][nb]);
       }
     }
 }
@@ -367,12 +388,72 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(PrefillArgs a) {
   }
 }
 
+// Prefill with 32 heads per wave (two waves per SIMD): the TW waves of a
+// query row (H = 32 * TW) share one gather of each K/V block in LDS, and a
+// workgroup of 4 waves takes 4 / TW rows. Barriers run over the whole
+// workgroup, so its rows step through max(n_sel) blocks together.
+template <int TW>
+__global__ __launch_bounds__(256) void attn_prefill_shared(PrefillArgs a) {
+  constexpr int RW = 4 / TW;
+  __shared__ __attribute__((aligned(16))) char lds_all[RW * 2 * kBlkLds];
+  const int wv = wave_id(), gw = wv % TW, sr = wv / TW;
+  const int64_t per = gridDim.x / 8, bx = blockIdx.x;
+  const int64_t tile = (bx % 8) * per + bx / 8;
+  const int64_t rows = (int64_t)a.B * a.L;
+  const int64_t gq0 = tile * RW;
+  if (gq0 >= rows) return;  // the same for every wave of the workgroup
+  const bool active = gq0 + sr < rows;
+  const int64_t gq = active ? gq0 + sr : rows - 1;  // a missing row repeats the last, stores nothing
+  const int b = (int)(gq / a.L);
+  const int l = lane_id(), g = l >> 5, c = l & 31;
+  v8bf Q[1][8];
+  load_q<1>(a.q + gq * a.H * kD, gw * 32, a.H, Q);
+  AttnState<1> st;
+  attn_init(st);
+  const int n = min(max(a.n_sel[gq], 0), a.K_tot);
+  int nmax = 0;
+#pragma unroll
+  for (int r = 0; r < RW; ++r) nmax = max(nmax, min(max(a.n_sel[min(gq0 + r, rows - 1)], 0), a.K_tot));
+  const uint16_t* K = a.k + (int64_t)b * a.n_k * kD;
+  const uint16_t* V = a.v + (int64_t)b * a.n_k * kD;
+  constexpr int kR = 2;
+  const int trips = ((nmax + 31) / 32 + kR - 1) / kR * kR;
+  attn_keys<1, TW, kR, true>(Q, true, K, V, a.idx + gq * a.K_tot, 0, n, trips, a.n_k, a.sl2, gw, st,
+                             lds_all + sr * 2 * kBlkLds);
+  st.l[0] += shfl_xor_f(st.l[0], 32);  // both key halves
+  const int h = gw * 32 + c;
+  if (!active || h >= a.H) return;
+  const float inv = st.l[0] > 0.f ? 1.f / st.l[0] : 0.f;
+  uint16_t* orow = a.o + (gq * a.H + h) * kD;
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+    for (int i4 = 0; i4 < 4; ++i4) {
+      const v16f& O = st.o[mb][0];
+      const uint32_t w0 = pack_bf16x2(O[4 * i4] * inv, O[4 * i4 + 1] * inv);
+      const uint32_t w1 = pack_bf16x2(O[4 * i4 + 2] * inv, O[4 * i4 + 3] * inv);
+      *(v2u*)(orow + 32 * mb + 8 * i4 + 4 * g) = v2u{w0, w1};
+    }
+  if (a.lse && g == 0)
+    a.lse[gq * a.H + h] = st.l[0] > 0.f ? (st.m[0] + log2f(st.l[0])) * 0.69314718055994531f : -INFINITY;
+}
+
+constexpr bool kPrefillShared = true;
+
 hipError_t launch_attn_prefill(const PrefillArgs& a, hipStream_t st) {
   const int NB = a.H <= 32 ? 1 : 2;
   const int HB = (a.H + 32 * NB - 1) / (32 * NB);
   const int64_t groups = (int64_t)a.B * a.L * HB;
   dim3 grid((unsigned)(((groups + 3) / 4 + 7) / 8 * 8));
   KernelTimer kt("attn_prefill_kernel", st);
+  if (kPrefillShared && (a.H == 64 || a.H == 128)) {
+    const int TW = a.H / 32, RW = 4 / TW;
+    const int64_t wgs = ((int64_t)a.B * a.L + RW - 1) / RW;
+    const dim3 g2((unsigned)((wgs + 7) / 8 * 8));
+    if (TW == 2) hipLaunchKernelGGL(attn_prefill_shared<2>, g2, dim3(256), 0, st, a);
+    else hipLaunchKernelGGL(attn_prefill_shared<4>, g2, dim3(256), 0, st, a);
+    return hipGetLastError();
+  }
   if (NB == 1) hipLaunchKernelGGL(attn_prefill_kernel<1>, grid, dim3(256), 0, st, a);
   else hipLaunchKernelGGL(attn_prefill_kernel<2>, grid, dim3(256), 0, st, a);
   return hipGetLastError();

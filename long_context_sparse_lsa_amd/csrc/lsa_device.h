@@ -43,6 +43,12 @@ __device__ __forceinline__ int pair_sum32(int lo, int hi) {
   const auto r = __builtin_amdgcn_permlane32_swap((unsigned)lo, (unsigned)hi, false, false);
   return (int)r[0] + (int)r[1];
 }
+// max(v[l], v[l ^ 32]) in every lane (float), through the same lane swap.
+__device__ __forceinline__ float xor32_max(float v) {
+  const unsigned u = __builtin_bit_cast(unsigned, v);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return fmaxf(__builtin_bit_cast(float, (unsigned)r[0]), __builtin_bit_cast(float, (unsigned)r[1]));
+}
 // v[l] + v[l ^ 32] in every lane.
 __device__ __forceinline__ int xor32_sum(int v) { return pair_sum32(v, v); }
 
