@@ -688,12 +688,16 @@ static hipError_t launch_partial(const DecodeArgs& a, hipStream_t st) {
   const int T = a.n_q * HB;
   // waves sharing K/V must read the same index row: with one index per
   // query row, a workgroup stays within the head groups of one row
-  const int TW = a.n_idx == 1 ? (T >= 8 ? 8 : T >= 4 ? 4 : T >= 2 ? 2 : 1) : HB;
+  const int TW = a.n_idx == 1 ? (T >= 4 ? 4 : T >= 2 ? 2 : 1) : HB;
   // subranges per part: 8 waves per workgroup (4 when one row group, to stay
-  // within LDS)
+  // within LDS); with eight or more head groups, workgroups of four waves
+  // (one per SIMD) without subranges
   switch (TW) {
     case 8: launch_partial_tk<8, 1>(a, T, st); break;
-    case 4: launch_partial_tk<4, 2>(a, T, st); break;
+    case 4:
+      if (T >= 8) launch_partial_tk<4, 1>(a, T, st);
+      else launch_partial_tk<4, 2>(a, T, st);
+      break;
     case 2: launch_partial_tk<2, 4>(a, T, st); break;
     default: launch_partial_tk<1, 4>(a, T, st); break;
   }

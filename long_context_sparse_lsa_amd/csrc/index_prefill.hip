@@ -7,10 +7,12 @@
 //
 // GEMM view: M = (query, head) rows, N = keys, K = d_I. A workgroup of 4 waves
 // (one per SIMD) owns 16 consecutive queries, 4 per wave, and walks a chunk
-// of keys in tiles of 128 keys that are staged once in LDS (double-buffered)
-// and read by all four waves. A wave keeps its 4 queries' rows (4 * H_I rows)
-// in registers as the A operand for the whole chunk, so every 16-byte LDS
-// read of the key operand feeds 4 * H_I / 32 MFMAs.
+// of 4096 to 16384 keys in tiles of 128 keys that are staged once in LDS
+// (double-buffered) and read by all four waves. A wave keeps its 4 queries'
+// rows (4 * H_I rows) in registers as the A operand for the whole chunk, so
+// every 16-byte LDS read of the key operand feeds 4 * H_I / 32 MFMAs, and the
+// A operand is loaded once per chunk (the longest chunk that still leaves
+// several rounds of workgroups).
 //
 // Per 32-key block a wave runs, for each of its 4 queries, H_I/32 * d_I/32
 // MFMAs and a ReLU / head-sum epilogue on the VALU. The MFMA pipe and the
@@ -43,7 +45,9 @@ constexpr int kWaves = 4;
 constexpr int kQW = 4;                   // queries per wave
 constexpr int kQT = kWaves * kQW;        // queries per workgroup
 constexpr int kThreads = 64 * kWaves;
-constexpr int kChunkKeys = 4096;         // keys per workgroup
+constexpr int kMinChunkKeys = 4096;      // keys per workgroup: 4096, 8192 or 16384
+constexpr int kMaxChunkKeys = 16384;
+constexpr int kFullGrid = 2048;           // workgroups of four rounds over the chip
 constexpr int kBlocks = kTileKeys / 32;  // 32-key blocks per tile
 
 template <int DI>
@@ -197,17 +201,26 @@ __device__ __forceinline__ void score_chunk(const ScoreArgs& a, const v4i (&A)[k
   }
 }
 
+// Grid: gridDim.x * gridDim.y = chunks * query tiles, walked chunk-major:
+// consecutive workgroups (which the dispatcher deals to the 8 XCDs in turn)
+// take consecutive query tiles of one key chunk, so every XCD gets the same
+// mix of chunks and the chunk's keys are shared in each XCD's L2.
 template <int HI, int DI>
-__global__ __launch_bounds__(kThreads, 2) void index_prefill_kernel(ScoreArgs a, int fold_ok) {
+__global__ __launch_bounds__(kThreads, 2) void index_prefill_kernel(ScoreArgs a, int fold_ok, int chunk_keys) {
   using G = TileGeom<DI>;
   constexpr int MB = HI / 32, KS = DI / 32;
   __shared__ __attribute__((aligned(16))) char lds[2 * G::kBytes];
   __shared__ __attribute__((aligned(16))) int wl[HI];
-  const int chunk = blockIdx.x, qt = blockIdx.y, b = blockIdx.z;
+  const int lin = blockIdx.y * gridDim.x + blockIdx.x;
+  const int n_qt = (a.n_q + kQT - 1) / kQT;
+  const int chunk = lin / n_qt, qt = lin % n_qt, b = blockIdx.z;
   const int q0 = qt * kQT;
-  const int v_begin = chunk * kChunkKeys;
-  const int v_end = min(v_begin + kChunkKeys, a.n_keys);
+  const int v_begin = chunk * chunk_keys;
   const int last_row = min(q0 + kQT, a.n_q) - 1;
+  // without masked fill, keys past the last one visible to the workgroup's
+  // rows are never stored and are not scored
+  const int v_end = min(min(v_begin + chunk_keys, a.n_keys),
+                        a.fill_masked ? a.n_keys : a.mask_off + last_row + 1);
   int32_t* sc = a.scores + (int64_t)b * a.s_bstride;
   const int l = lane_id(), g = l >> 5, c = l & 31;
 
@@ -264,9 +277,16 @@ __global__ __launch_bounds__(kThreads, 2) void index_prefill_kernel(ScoreArgs a,
 
 template <int HI, int DI>
 hipError_t launch_t(const ScoreArgs& a, int fold_ok, hipStream_t st) {
-  dim3 grid((a.n_keys + kChunkKeys - 1) / kChunkKeys, (a.n_q + kQT - 1) / kQT, a.B);
+  // longer chunks load each query's A operand fewer times; they are taken
+  // while the grid still fills the chip for several rounds
+  const int64_t n_qt = (a.n_q + kQT - 1) / kQT;
+  int ck = kMinChunkKeys;
+  while (ck < kMaxChunkKeys && (int64_t)((a.n_keys + 2 * ck - 1) / (2 * ck)) * n_qt * a.B >= kFullGrid) ck *= 2;
+  const int64_t n_chunks = (a.n_keys + ck - 1) / ck;
+  if (n_chunks * n_qt > INT32_MAX) return hipErrorInvalidValue;
+  dim3 grid((unsigned)n_chunks, (unsigned)n_qt, a.B);
   KernelTimer kt("index_prefill_kernel", st);
-  hipLaunchKernelGGL((index_prefill_kernel<HI, DI>), grid, dim3(kThreads), 0, st, a, fold_ok);
+  hipLaunchKernelGGL((index_prefill_kernel<HI, DI>), grid, dim3(kThreads), 0, st, a, fold_ok, ck);
   return hipGetLastError();
 }
 
