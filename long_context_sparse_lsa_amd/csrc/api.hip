@@ -55,7 +55,7 @@ bool survivors_ok(int64_t max_nc, int k_cap) { return select_fits(max_nc, k_cap)
 
 // Rows per pass of the fused (score + select) prefill path: the score buffer
 // of one pass is at most kFusedScoreBytes.
-constexpr size_t kFusedScoreBytes = (size_t)1024 << 20;
+constexpr size_t kFusedScoreBytes = (size_t)2048 << 20;
 // Returns the rows of one query range (R) and the sequences per pass (nb):
 // a long prefill is cut into row ranges of one sequence (nb = 1), a short
 // decode batch puts many whole sequences into one pass.

@@ -50,13 +50,24 @@ constexpr int kMaxChunkKeys = 16384;
 constexpr int kFullGrid = 2048;           // workgroups of four rounds over the chip
 constexpr int kBlocks = kTileKeys / 32;  // 32-key blocks per tile
 
+// A key tile in LDS: rows of DI bytes, unpadded, written by direct
+// global -> LDS loads (each 64-lane load fills 1 KB, lane i at byte 16 i).
+// Within a row the 16-byte parts are permuted so that the same part of 8
+// consecutive keys lands in 8 distinct 16-byte bank groups: the key-operand
+// reads (lane c reads key c) are then free of bank conflicts.
 template <int DI>
 struct TileGeom {
-  static constexpr int kRow = DI + 16;                 // padded LDS row: conflict-free b128 reads
-  static constexpr int kBytes = kTileKeys * kRow;      // one stage
-  static constexpr int kPieces = kTileKeys * DI / 16;  // 16-byte pieces per tile
-  static constexpr int kPerThread = kPieces / kThreads;
+  static constexpr int kParts = DI / 16;                   // 16-byte parts of a row
+  static constexpr int kRowsPerLine = 8 / kParts;          // rows per 128 bytes
+  static constexpr int kBytes = kTileKeys * DI;            // one stage
+  static constexpr int kPerWave = kTileKeys * DI / 1024 / kWaves;  // 1 KB loads per wave
 };
+
+template <int DI>
+__device__ __forceinline__ int tile_off(int key, int part) {
+  using G = TileGeom<DI>;
+  return key * DI + 16 * (part ^ ((key / G::kRowsPerLine) & (G::kParts - 1)));
+}
 
 // Lane-partial head sum of one 32-key block (this lane's rows, key l % 32).
 // Unfolded, the weights of this lane's rows come from LDS (wl holds w[h];
@@ -98,7 +109,7 @@ __device__ __forceinline__ void read_b(const char* tile, int nb, v4i (&Bk)[KS]) 
   using G = TileGeom<DI>;
   const int l = lane_id(), g = l >> 5, c = l & 31;
 #pragma unroll
-  for (int j = 0; j < KS; ++j) Bk[j] = *(const v4i*)(tile + (32 * nb + c) * G::kRow + g * (DI / 2) + 16 * j);
+  for (int j = 0; j < KS; ++j) Bk[j] = *(const v4i*)(tile + tile_off<DI>(32 * nb + c, g * (G::kParts / 2) + j));
 }
 
 // Scores of this wave's queries row0 .. row0+3 against keys [v_begin, v_end).
@@ -108,38 +119,37 @@ __device__ __forceinline__ void score_chunk(const ScoreArgs& a, const v4i (&A)[k
                                             int v_end, int row0, int32_t* sc) {
   using G = TileGeom<DI>;
   constexpr int MB = HI / 32, KS = DI / 32;
-  const int tid = threadIdx.x;
   const int l = lane_id(), g = l >> 5, c = l & 31;
   const int vis_lo_wave = a.mask_off + row0;  // last key visible to every query of the wave
   const bool rows_ok = row0 + kQW <= a.n_q;
 
-  // global -> register prefetch of one tile
-  v4i pf[G::kPerThread];
-  auto fetch = [&](int v0) {
+  // direct global -> LDS loads of one tile into a stage: load u of wave w
+  // fills rows [8 (w * kPerWave + u), +8) (DI = 128) of the stage
+  // Buffer loads: lane offsets are fixed (the part permutation of a lane does
+  // not depend on the load, every load starting at a multiple of 8 rows), the
+  // tile position goes in the scalar offset, and rows past the batch's keys
+  // read as zero (range-checked by the buffer; such keys are never stored).
+  const int wbase = __builtin_amdgcn_readfirstlane(wave_id() * G::kPerWave);
+  const int lane_key = l / G::kParts;
+  const int lane_off = lane_key * DI + 16 * ((l % G::kParts) ^ ((lane_key / G::kRowsPerLine) & (G::kParts - 1)));
+  const __amdgpu_buffer_rsrc_t kres =
+      __builtin_amdgcn_make_buffer_rsrc((void*)kb, (short)0, (int)((int64_t)a.n_k * DI), 0x00020000);
+  auto fetch = [&](int v0, char* stage) {
 #pragma unroll
-    for (int u = 0; u < G::kPerThread; ++u) {
-      const int id = tid + u * kThreads;
-      const int key = id / (DI / 16), part = id % (DI / 16);
-      const int v = min(v0 + key, v_end - 1);  // clamped: keys past v_end are never stored
-      pf[u] = *(const v4i*)(kb + (int64_t)v * DI + part * 16);
-    }
-  };
-  auto stash = [&](char* stage) {
-#pragma unroll
-    for (int u = 0; u < G::kPerThread; ++u) {
-      const int id = tid + u * kThreads;
-      const int key = id / (DI / 16), part = id % (DI / 16);
-      *(v4i*)(stage + key * G::kRow + part * 16) = pf[u];
+    for (int u = 0; u < G::kPerWave; ++u) {
+      const int n = wbase + u;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(kres, (__attribute__((address_space(3))) void*)(stage + n * 1024), 16,
+                                               lane_off, (v0 + n * (64 / G::kParts)) * DI, 0, 0);
     }
   };
 
-  fetch(v_begin);
-  stash(lds);
+  fetch(v_begin, lds);
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   int stage = 0;
   for (int v0 = v_begin; v0 < v_end; v0 += kTileKeys) {
     const bool more = v0 + kTileKeys < v_end;
-    if (more) fetch(v0 + kTileKeys);
+    if (more) fetch(v0 + kTileKeys, lds + (stage ^ 1) * G::kBytes);
     const char* tile = lds + stage * G::kBytes;
     // every key of the tile visible to every query of the wave
     const bool fast = rows_ok && v0 >= a.pos_lo && v0 + kTileKeys <= v_end && v0 + kTileKeys - 1 <= vis_lo_wave;
@@ -193,11 +203,11 @@ __device__ __forceinline__ void score_chunk(const ScoreArgs& a, const v4i (&A)[k
         }
       }
     }
-    if (more) {
-      stash(lds + (stage ^ 1) * G::kBytes);
-      stage ^= 1;
-    }
+    // this wave's loads of the next tile have landed; the barrier publishes
+    // every wave's and frees the current stage for the tile after
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
+    stage ^= 1;
   }
 }
 
@@ -213,7 +223,9 @@ __global__ __launch_bounds__(kThreads, 2) void index_prefill_kernel(ScoreArgs a,
   __shared__ __attribute__((aligned(16))) int wl[HI];
   const int lin = blockIdx.y * gridDim.x + blockIdx.x;
   const int n_qt = (a.n_q + kQT - 1) / kQT;
-  const int chunk = lin / n_qt, qt = lin % n_qt, b = blockIdx.z;
+  // query tiles in descending order: under a causal mask the later rows
+  // have the most visible keys, and the longest workgroups start first
+  const int chunk = lin / n_qt, qt = n_qt - 1 - lin % n_qt, b = blockIdx.z;
   const int q0 = qt * kQT;
   const int v_begin = chunk * chunk_keys;
   const int last_row = min(q0 + kQT, a.n_q) - 1;
