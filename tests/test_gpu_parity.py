@@ -123,6 +123,37 @@ def test_select_given_scores_ties_and_chunks(cfg, n_k, hi):
             check_idx(In[b, i], Nn[b, i], ref, K_tot, f"b{b} i{i}")
 
 
+@pytest.mark.parametrize("n_k", [20000, 70000])
+def test_select_structured_rows(n_k):
+    """Structured rows: every 8th candidate scores low (or only those score
+    high), and a row whose threshold value is shared by thousands of ties.
+    Selection must stay exact on one chunk and across chunks."""
+    say(f"select structured rows n_k={n_k}")
+    n_sink, W, kd = 4, 512, 1532
+    n_q = 3
+    g = torch.Generator(device=DEV)
+    g.manual_seed(79)
+    pos = torch.arange(n_k, device=DEV)
+    high = torch.randint(1 << 20, 1 << 24, (n_k,), dtype=torch.int32, generator=g, device=DEV)
+    low = torch.randint(0, 1000, (n_k,), dtype=torch.int32, generator=g, device=DEV)
+    # row 0: every candidate whose offset from the first one is a multiple of 8 scores low
+    r0 = torch.where((pos - n_sink) % 8 == 0, low, high)
+    # row 1: kd - 10 large scores, then 6000 ties at one value, the rest low
+    r1 = low.clone()
+    r1[torch.randperm(n_k - W - n_sink, generator=g, device=DEV)[:kd - 10] + n_sink] = 1 << 23
+    tie = torch.randperm(n_k - W - n_sink, generator=g, device=DEV)[:6000] + n_sink
+    r1[tie] = torch.where(r1[tie] == (1 << 23), r1[tie], torch.full_like(r1[tie], 5000))
+    # row 2: only the sampled candidates score high
+    r2 = torch.where((pos - n_sink) % 8 == 0, high, low)
+    scores = torch.stack([r0, r1, r2])[None].contiguous()
+    q_off = n_k - n_q
+    idx, n_sel = L.lsa_select_topk(scores=scores, n_sink=n_sink, n_window=W, k_dyn=kd, q_off=q_off)
+    Sn, In, Nn = np_(scores), np_(idx), np_(n_sel)
+    for i in range(n_q):
+        ref = O.select_flat(Sn[0, i], q_off + i, n_sink, W, kd)
+        check_idx(In[0, i], Nn[0, i], ref, n_sink + W + kd, f"row {i}")
+
+
 def test_select_given_scores_short_rows():
     say("select short rows")
     n = 300
