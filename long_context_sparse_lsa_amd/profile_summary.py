@@ -40,10 +40,18 @@ def sources_hash():
     return h.hexdigest()[:16]
 
 
+# kernel symbols reported under another timing name (the library times its
+# 32-head-wave prefill attention kernel as "attn_prefill_kernel")
+ALIASES = {"attn_prefill_shared": "attn_prefill_kernel"}
+
+
 def base_name(full):
     for k in KERNELS:
         if k in full:
             return k
+    for k, v in ALIASES.items():
+        if k in full:
+            return v
     return None
 
 
