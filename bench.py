@@ -328,6 +328,22 @@ def run_decode(args, wl, torch):
         graph.replay()
     torch.cuda.synchronize()
     us_step = (time.perf_counter() - t0) * 1e6 / args.steps
+    # the same replays with the last-level cache (256 MB MALL) flushed before
+    # each one by reading 512 MB, untimed: a step that follows other work (a
+    # read leaves clean lines, so the step pays no write-back of the flush)
+    flush = torch.zeros(64 << 20, dtype=torch.int64, device=dev)
+    flush.sum()
+    cold = []
+    for _ in range(args.steps):
+        flush.sum()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        graph.replay()
+        e1.record()
+        cold.append((e0, e1))
+    torch.cuda.synchronize()
+    us_cold = sum(a.elapsed_time(b) for a, b in cold) * 1e3 / len(cold)
+    del flush
     K_tot = wl.K_tot
     kv_bytes = wl.B * K_tot * wl.D * 2 * 2
     qo_bytes = 2 * wl.B * wl.n_q * wl.H * wl.D * 2
@@ -358,7 +374,7 @@ def run_decode(args, wl, torch):
         "config": {"workload": wl.name, "global_batch": wl.B, "context": N, "n_q": wl.n_q, "H": wl.H,
                    "K_tot": K_tot, "n_split": wl.n_split, "hier_blk": wl.blk, "launch": "hip_graph_replay",
                    "parallelism": "none"},
-        "parts": {"eager_us_per_step": round(us_eager, 2),
+        "parts": {"eager_us_per_step": round(us_eager, 2), "cold_cache_us_per_step": round(us_cold, 2),
                   "select_us": round(sel_ms * 1e3, 2), "attn_us": round(attn_ms * 1e3, 2),
                   "step_bytes": step_bytes,
                   "step_hbm_frac": round(step_bytes / (us_step * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
