@@ -7,7 +7,7 @@
 //
 // GEMM view: M = (query, head) rows, N = keys, K = d_I. A workgroup of 4 waves
 // (one per SIMD) owns 16 consecutive queries, 4 per wave, and walks a chunk
-// of 4096 to 16384 keys in tiles of 128 keys that are staged once in LDS
+// of 4096 to 16384 keys in tiles of 256 keys that are staged once in LDS
 // (double-buffered) and read by all four waves. A wave keeps its 4 queries'
 // rows (4 * H_I rows) in registers as the A operand for the whole chunk, so
 // every 16-byte LDS read of the key operand feeds 4 * H_I / 32 MFMAs, and the
@@ -40,7 +40,7 @@ namespace lsa {
 
 namespace {
 
-constexpr int kTileKeys = 128;  // keys per LDS tile
+constexpr int kTileKeys = 256;  // keys per LDS tile
 constexpr int kWaves = 4;
 constexpr int kQW = 4;                   // queries per wave
 constexpr int kQT = kWaves * kQW;        // queries per workgroup
@@ -163,10 +163,15 @@ __device__ __forceinline__ void score_chunk(const ScoreArgs& a, const v4i (&A)[k
 #pragma unroll
         for (int qp = 0; qp < kQW; qp += 2) {
           // both queries' MFMAs first: the first epilogue then runs while
-          // the second query's products finish
+          // the second query's products finish. The epilogue runs at a
+          // raised wave priority: the SIMD's other wave, issuing products,
+          // needs an issue slot only once per MFMA, and the VALU work is no
+          // longer held back by it (measured: about 3% faster)
           v16i acc0[MB], acc1[MB];
+          __builtin_amdgcn_s_setprio(0);
           block_mfma<MB, KS>(A[qp], Bk, acc0);
           block_mfma<MB, KS>(A[qp + 1], Bk, acc1);
+          __builtin_amdgcn_s_setprio(2);
           const int s0 = head_sum<MB, FOLD>(acc0, wl);
           const int s1 = head_sum<MB, FOLD>(acc1, wl);
           // lane half g ends with query qp + g's full sum
