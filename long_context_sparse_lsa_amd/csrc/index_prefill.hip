@@ -151,38 +151,45 @@ __device__ __forceinline__ void score_chunk(const ScoreArgs& a, const v4i (&A)[k
     const bool more = v0 + kTileKeys < v_end;
     if (more) fetch(v0 + kTileKeys, lds + (stage ^ 1) * G::kBytes);
     const char* tile = lds + stage * G::kBytes;
+    // per block: each query's MFMAs and epilogue in turn, one 64-lane store
+    // per pair of queries; the other wave on the SIMD fills the MFMA pipe
+    auto fast_block = [&](int nb) {
+      v4i Bk[KS];
+      read_b<DI, KS>(tile, nb, Bk);
+#pragma unroll
+      for (int qp = 0; qp < kQW; qp += 2) {
+        // both queries' MFMAs first: the first epilogue then runs while
+        // the second query's products finish. The epilogue runs at a
+        // raised wave priority: the SIMD's other wave, issuing products,
+        // needs an issue slot only once per MFMA, and the VALU work is no
+        // longer held back by it (measured: about 3% faster)
+        v16i acc0[MB], acc1[MB];
+        __builtin_amdgcn_s_setprio(0);
+        block_mfma<MB, KS>(A[qp], Bk, acc0);
+        block_mfma<MB, KS>(A[qp + 1], Bk, acc1);
+        __builtin_amdgcn_s_setprio(2);
+        const int s0 = head_sum<MB, FOLD>(acc0, wl);
+        const int s1 = head_sum<MB, FOLD>(acc1, wl);
+        // lane half g ends with query qp + g's full sum
+        sc[(int64_t)(row0 + qp + g) * a.ld + v0 + 32 * nb + c] = pair_sum32(s0, s1);
+      }
+    };
     // every key of the tile visible to every query of the wave
     const bool fast = rows_ok && v0 >= a.pos_lo && v0 + kTileKeys <= v_end && v0 + kTileKeys - 1 <= vis_lo_wave;
     if (fast) {
-      // per block: each query's MFMAs and epilogue in turn, one 64-lane store
-      // per pair of queries; the other wave on the SIMD fills the MFMA pipe
 #pragma unroll
-      for (int nb = 0; nb < kBlocks; ++nb) {
-        v4i Bk[KS];
-        read_b<DI, KS>(tile, nb, Bk);
-#pragma unroll
-        for (int qp = 0; qp < kQW; qp += 2) {
-          // both queries' MFMAs first: the first epilogue then runs while
-          // the second query's products finish. The epilogue runs at a
-          // raised wave priority: the SIMD's other wave, issuing products,
-          // needs an issue slot only once per MFMA, and the VALU work is no
-          // longer held back by it (measured: about 3% faster)
-          v16i acc0[MB], acc1[MB];
-          __builtin_amdgcn_s_setprio(0);
-          block_mfma<MB, KS>(A[qp], Bk, acc0);
-          block_mfma<MB, KS>(A[qp + 1], Bk, acc1);
-          __builtin_amdgcn_s_setprio(2);
-          const int s0 = head_sum<MB, FOLD>(acc0, wl);
-          const int s1 = head_sum<MB, FOLD>(acc1, wl);
-          // lane half g ends with query qp + g's full sum
-          sc[(int64_t)(row0 + qp + g) * a.ld + v0 + 32 * nb + c] = pair_sum32(s0, s1);
-        }
-      }
+      for (int nb = 0; nb < kBlocks; ++nb) fast_block(nb);
     } else {
 #pragma unroll 1
       for (int nb = 0; nb < kBlocks; ++nb) {
         const int p0 = v0 + 32 * nb;  // first key of the block
         if (p0 >= v_end) break;
+        // a block of the tile that every query of the wave sees whole (the
+        // blocks before the diagonal) takes the fast form
+        if (rows_ok && p0 >= a.pos_lo && p0 + 32 <= v_end && p0 + 31 <= vis_lo_wave) {
+          fast_block(nb);
+          continue;
+        }
         const int v = p0 + c;
         v4i Bk[KS];
         read_b<DI, KS>(tile, nb, Bk);
