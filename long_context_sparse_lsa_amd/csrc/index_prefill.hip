@@ -115,8 +115,8 @@ __device__ __forceinline__ void read_b(const char* tile, int nb, v4i (&Bk)[KS]) 
 // Scores of this wave's queries row0 .. row0+3 against keys [v_begin, v_end).
 template <int HI, int DI, bool FOLD>
 __device__ __forceinline__ void score_chunk(const ScoreArgs& a, const v4i (&A)[kQW][HI / 32][DI / 32],
-                                            const int* wl, const int8_t* kb, char* lds, int v_begin,
-                                            int v_end, int row0, int32_t* sc) {
+                                            const int* wl, const int8_t* kb, char* lds0, char* lds1,
+                                            int v_begin, int v_end, int row0, int32_t* sc) {
   using G = TileGeom<DI>;
   constexpr int MB = HI / 32, KS = DI / 32;
   const int l = lane_id(), g = l >> 5, c = l & 31;
@@ -143,14 +143,13 @@ __device__ __forceinline__ void score_chunk(const ScoreArgs& a, const v4i (&A)[k
     }
   };
 
-  fetch(v_begin, lds);
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  int stage = 0;
-  for (int v0 = v_begin; v0 < v_end; v0 += kTileKeys) {
+  // One tile from stage `tile` while the next one loads into `next`. The two
+  // stages are separate LDS arrays, and the loop below names each one
+  // explicitly, so the compiler can tell the next tile's loads apart from
+  // this tile's reads and does not wait for them before reading.
+  auto step = [&](int v0, const char* tile, char* next) {
     const bool more = v0 + kTileKeys < v_end;
-    if (more) fetch(v0 + kTileKeys, lds + (stage ^ 1) * G::kBytes);
-    const char* tile = lds + stage * G::kBytes;
+    if (more) fetch(v0 + kTileKeys, next);
     // per block: each query's MFMAs and epilogue in turn, one 64-lane store
     // per pair of queries; the other wave on the SIMD fills the MFMA pipe
     auto fast_block = [&](int nb) {
@@ -219,7 +218,13 @@ __device__ __forceinline__ void score_chunk(const ScoreArgs& a, const v4i (&A)[k
     // every wave's and frees the current stage for the tile after
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    stage ^= 1;
+  };
+  fetch(v_begin, lds0);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  for (int v0 = v_begin; v0 < v_end; v0 += 2 * kTileKeys) {
+    step(v0, lds0, lds1);
+    if (v0 + kTileKeys < v_end) step(v0 + kTileKeys, lds1, lds0);
   }
 }
 
@@ -231,7 +236,8 @@ template <int HI, int DI>
 __global__ __launch_bounds__(kThreads, 2) void index_prefill_kernel(ScoreArgs a, int fold_ok, int chunk_keys) {
   using G = TileGeom<DI>;
   constexpr int MB = HI / 32, KS = DI / 32;
-  __shared__ __attribute__((aligned(16))) char lds[2 * G::kBytes];
+  __shared__ __attribute__((aligned(16))) char lds0[G::kBytes];
+  __shared__ __attribute__((aligned(16))) char lds1[G::kBytes];
   __shared__ __attribute__((aligned(16))) int wl[HI];
   const int lin = blockIdx.y * gridDim.x + blockIdx.x;
   const int n_qt = (a.n_q + kQT - 1) / kQT;
@@ -293,9 +299,9 @@ __global__ __launch_bounds__(kThreads, 2) void index_prefill_kernel(ScoreArgs a,
 #pragma unroll
         for (int j = 0; j < KS; ++j) A[q][mb][j] = scale_bytes(A[q][mb][j], wh);
     }
-    score_chunk<HI, DI, true>(a, A, wl, kb, lds, v_begin, v_end, row0, sc);
+    score_chunk<HI, DI, true>(a, A, wl, kb, lds0, lds1, v_begin, v_end, row0, sc);
   } else {
-    score_chunk<HI, DI, false>(a, A, wl, kb, lds, v_begin, v_end, row0, sc);
+    score_chunk<HI, DI, false>(a, A, wl, kb, lds0, lds1, v_begin, v_end, row0, sc);
   }
 }
 
