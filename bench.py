@@ -79,6 +79,22 @@ class EventTimer:
         return sum(a.elapsed_time(b) for a, b in ev) / max(1, len(ev)), len(ev)
 
 
+def copy_gbs(torch, nbytes=1 << 30, reps=5):
+    """Read + write GB/s of a plain 1 GiB device-to-device copy (event-timed)."""
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    del src, dst
+    return 2.0 * nbytes / (ms * 1e-3) / 1e9
+
+
 def cpu_threads():
     try:
         from threadpoolctl import threadpool_info
@@ -406,6 +422,13 @@ def main():
     L.load()
     wl = configs.BY_ID[args.config]
     out = run_prefill(args, wl, torch) if wl.kind == "prefill" else run_decode(args, wl, torch)
+    roof = out["roofline"]
+    if roof["bound"] == "hbm":
+        # the bandwidth a plain device copy reaches on this GPU in this run: the
+        # attainable ceiling next to the 8 TB/s figure
+        cg = copy_gbs(torch)
+        roof["copy_gbs"] = round(cg, 1)
+        roof["frac_of_copy"] = round(roof["achieved"] / cg, 4)
     if args.copy_probe:
         a = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
         b = torch.empty_like(a)
