@@ -445,6 +445,6 @@ extern "C" int32_t lsa_sparse_attn_decode(const lsa_bf16* q, const lsa_bf16* k_c
   a.lse = lse;
   a.ws_m = (float*)ws;
   a.ws_l = a.ws_m + rows;
-  a.ws_o = (float*)((char*)ws + align_up(rows * 2 * sizeof(float)));
+  a.ws_o = (_Float16*)((char*)ws + align_up(rows * 2 * sizeof(float)));
   return hip_status(launch_attn_decode(a, (hipStream_t)stream));
 }

@@ -460,8 +460,9 @@ hipError_t launch_attn_prefill(const PrefillArgs& a, hipStream_t st) {
 }
 
 // ------------------------------------------------------------------ decode
-// Partials: ws_m / ws_l [B, n_split, R], ws_o [B, n_split, R, 128] with
-// R = n_q * H; o is unnormalised, m in base-2 units.
+// Partials: ws_m / ws_l [B, n_split, R] fp32, ws_o [B, n_split, R, 128] fp16
+// with R = n_q * H; o is the part's output normalised by its own l, m in
+// base-2 units.
 //
 // Decode runs 32 heads per wave (a row group: one query row x 32 heads), so
 // that a wave needs at most 256 registers and two waves share each SIMD:
@@ -494,14 +495,21 @@ __device__ __forceinline__ void store_partial(const AttnState<NB>& st, const Dec
       a.ws_m[row] = st.m[nb];
       a.ws_l[row] = st.l[nb];
     }
-    float* orow = a.ws_o + row * kD;
+    // the part's output normalised by its own sum (so each value is a convex
+    // combination of V entries), in fp16 rounded to nearest (11 significant
+    // bits: a quarter of a bf16 output's rounding); the merge weighs it by
+    // l * 2^(m - M)
+    const float inv = st.l[nb] > 0.f ? 1.f / st.l[nb] : 0.f;
+    _Float16* orow = a.ws_o + row * kD;
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb) {
       if (mb < mb_lo || mb >= mb_hi) continue;
 #pragma unroll
       for (int i4 = 0; i4 < 4; ++i4) {
         const v16f& O = st.o[mb][nb];
-        *(v4f*)(orow + 32 * mb + 8 * i4 + 4 * g) = v4f{O[4 * i4], O[4 * i4 + 1], O[4 * i4 + 2], O[4 * i4 + 3]};
+        *(v4h*)(orow + 32 * mb + 8 * i4 + 4 * g) =
+            v4h{(_Float16)(O[4 * i4] * inv), (_Float16)(O[4 * i4 + 1] * inv), (_Float16)(O[4 * i4 + 2] * inv),
+                (_Float16)(O[4 * i4 + 3] * inv)};
       }
     }
   }
@@ -636,7 +644,7 @@ __global__ __launch_bounds__(256) void attn_decode_merge(DecodeArgs a) {
   const int64_t row0 = (int64_t)b * a.n_split * R + r;
   const float* pm = a.ws_m + row0;
   const float* pl = a.ws_l + row0;
-  const float* po = a.ws_o + row0 * kD + d;
+  const _Float16* po = a.ws_o + row0 * kD + d;
   float mj[NS], lv[NS];
   v4f ov[NS];
 #pragma unroll
@@ -645,7 +653,8 @@ __global__ __launch_bounds__(256) void attn_decode_merge(DecodeArgs a) {
     const int jr = in ? j * R : 0;
     mj[j] = in ? pm[jr] : -INFINITY;
     lv[j] = in ? pl[jr] : 0.f;
-    ov[j] = in ? *(const v4f*)(po + jr * kD) : v4f{};
+    const v4h w = in ? *(const v4h*)(po + (int64_t)jr * kD) : v4h{};
+    ov[j] = v4f{(float)w[0], (float)w[1], (float)w[2], (float)w[3]};
   }
   float M = -INFINITY;
 #pragma unroll
@@ -654,7 +663,7 @@ __global__ __launch_bounds__(256) void attn_decode_merge(DecodeArgs a) {
   for (int j = 0; j < NS; ++j) {
     const float wj = (j < a.n_split && M != -INFINITY) ? __builtin_amdgcn_exp2f(mj[j] - M) : 0.f;
     lv[j] *= wj;
-    ov[j] *= wj;
+    ov[j] *= lv[j];  // the part's normalised output weighed by l * 2^(m - M)
   }
 #pragma unroll
   for (int s = 1; s < NS; s <<= 1)
@@ -673,7 +682,7 @@ __global__ __launch_bounds__(256) void attn_decode_merge(DecodeArgs a) {
 
 size_t decode_ws_bytes(int B, int n_q, int H, int n_split) {
   const size_t rows = (size_t)B * n_split * n_q * H;
-  return rows * sizeof(float) * (2 + kD) + 256;
+  return rows * (2 * sizeof(float) + kD * sizeof(uint16_t)) + 256;
 }
 
 template <int TW, int KS>

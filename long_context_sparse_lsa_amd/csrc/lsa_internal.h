@@ -104,7 +104,8 @@ struct DecodeArgs {
   float sl2;
   uint16_t* o;
   float* lse;
-  float *ws_m, *ws_l, *ws_o;
+  float *ws_m, *ws_l;
+  _Float16* ws_o;
 };
 size_t decode_ws_bytes(int B, int n_q, int H, int n_split);
 hipError_t launch_attn_decode(const DecodeArgs& a, hipStream_t st);
