@@ -188,6 +188,8 @@ __device__ void attn_keys(const v8bf (&Q)[NB][8], bool active, const uint16_t* K
 // The block loop then issues no global load but the gathers, so the memory
 // counter holds nothing else and a stage waits only on its own loads. Used
 // where positions would otherwise chain their load latency into every step.
+// trips_used: the key span of the chunk's longest subrange (the same for all
+// waves of the workgroup); steps past its last block are not run.
 template <int TW>
 __device__ __forceinline__ void gather_kv_lds(const uint16_t* K, const uint16_t* V, const int* pb, int n_k, int gw,
                                               KVStage<TW>& s) {
@@ -203,8 +205,8 @@ __device__ __forceinline__ void gather_kv_lds(const uint16_t* K, const uint16_t*
 
 template <int NB, int TW, int R>
 __device__ void attn_keys_lds(const v8bf (&Q)[NB][8], bool active, const uint16_t* K, const uint16_t* V,
-                              const int* pos, int cnt, int trips, int n_k, float sl2, int gw, AttnState<NB>& st,
-                              char* lds) {
+                              const int* pos, int cnt, int trips, int trips_used, int n_k, float sl2, int gw,
+                              AttnState<NB>& st, char* lds) {
   static_assert(R % 2 == 0, "block parity selects the LDS buffer");
   const int l = lane_id(), c = l & 31;
   const int G = l >> 4, jj = l & 15;
@@ -213,10 +215,12 @@ __device__ void attn_keys_lds(const v8bf (&Q)[NB][8], bool active, const uint16_
 #pragma unroll
   for (int j = 0; j < R; ++j) gather_kv_lds<TW>(K, V, pos + 32 * j, n_k, gw, stg[j]);
   store_kv<TW>(stg[0], lds, gw);
+  const int nsteps = (trips_used + 31) / 32;  // the blocks of the chunk's longest subrange
   for (int it = 0; it < trips; it += R) {
 #pragma unroll
     for (int u = 0; u < R; ++u) {
       const int bi = it + u;
+      if (bi >= nsteps) break;  // the same for every wave of the workgroup
       __syncthreads();  // block bi in its buffer for all; the other buffer free
       gather_kv_lds<TW>(K, V, pos + 32 * (bi + R), n_k, gw, stg[u]);
       if (active && 32 * bi < cnt) attn_block<NB>(Q, lds + (u & 1) * kBlkLds, pos[32 * bi + c], n_k, sl2, vt_off, st);
@@ -575,7 +579,8 @@ __global__ __launch_bounds__(64 * TW * KS) void attn_decode_partial(DecodeArgs a
     if (ch > 0) __syncthreads();  // the previous chunk's positions and buffers no longer read
     for (int i = gt; i < Cfg::kPosN; i += 64 * TW) posg[i] = i < cnt ? ids[cb + i] : -1;
     __syncthreads();
-    attn_keys_lds<NB, TW, kR>(Q, active, K, V, posg, cnt, tr, a.n_k, a.sl2, gw, st, lds_all + sr * 2 * kBlkLds);
+    attn_keys_lds<NB, TW, kR>(Q, active, K, V, posg, cnt, tr, min(Cfg::kCap, span - ch * Cfg::kCap), a.n_k, a.sl2,
+                              gw, st, lds_all + sr * 2 * kBlkLds);
   }
   st.l[0] += shfl_xor_f(st.l[0], 32);  // both key halves
   const int64_t rbase = ((int64_t)b * a.n_split + split) * R + (int64_t)qr * a.H;
