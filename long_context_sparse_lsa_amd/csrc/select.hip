@@ -485,6 +485,7 @@ hipError_t launch_e(const SelectArgs& a, hipStream_t st) {
   const int64_t nb = (int64_t)a.max_chunks * a.k_cap;
   KernelTimer kt("select_stage_b", st);
   if (nb <= SEL_NT * 4) hipLaunchKernelGGL((select_stage_b<4>), dim3(a.n_rows), dim3(SEL_NT), 0, st, a, CH);
+  else if (nb <= SEL_NT * 8) hipLaunchKernelGGL((select_stage_b<8>), dim3(a.n_rows), dim3(SEL_NT), 0, st, a, CH);
   else if (nb <= SEL_NT * 16) hipLaunchKernelGGL((select_stage_b<16>), dim3(a.n_rows), dim3(SEL_NT), 0, st, a, CH);
   else hipLaunchKernelGGL((select_stage_b<32>), dim3(a.n_rows), dim3(SEL_NT), 0, st, a, CH);
   return hipGetLastError();
