@@ -34,7 +34,7 @@ namespace {
 
 constexpr int SEL_NT = 1024;  // threads of a stage-B workgroup (and the widest stage A)
 
-constexpr int kBins1 = 2048;  // first radix digit: up to 11 bits
+constexpr int kBins1 = 256;   // first radix digit: 8 bits
 constexpr int kList = 4096;   // keys of the first pass's threshold bin kept in LDS
 
 template <int NT>
@@ -162,9 +162,11 @@ __device__ __forceinline__ void find_bin(const uint32_t* hist, int k_rem, uint32
 // Threshold of the k-th largest nonzero key of the chunk (0 < k < #nonzero).
 // On return an entry u is kept iff (u >> shift) > (T >> shift), or
 // (u >> shift) == (T >> shift) and it is among the first r_eq such entries.
-// The first pass counts every key by a digit of up to 11 bits (8 for small
-// chunks) starting at the highest bit in which the chunk's keys differ. The keys of the bin that
-// holds the threshold (usually a few hundred) are then copied to an LDS list
+// The first pass counts every key by an 8-bit digit starting at the highest
+// bit in which the chunk's keys differ (an 11-bit digit leaves fewer keys in
+// the threshold bin but costs more to search: measured slower at every chunk
+// size here). The keys of the bin that holds the threshold are then copied
+// to an LDS list
 // when they fit, and further 8-bit passes count only those. Later pass p
 // counts into hist[p % 3] (hist[0] and hist[1] start cleared); after its
 // barrier every wave finds the digit itself and clears hist[(p + 2) % 3],
@@ -185,9 +187,8 @@ __device__ void radix_select(const uint32_t (&u)[E], uint32_t kmin, uint32_t kma
   int k_rem = k;
   // pass 1 over all keys (all nonzero keys share the bits above hb); small
   // chunks take an 8-bit digit, whose counts are cheaper to search
-  constexpr int B1 = E >= 16 ? kBins1 : 256;
-  constexpr int W1 = B1 == 256 ? 8 : 11;
-  int lo = max(0, hb - (W1 - 1));
+  constexpr int B1 = kBins1;
+  int lo = max(0, hb - 7);
   uint32_t dmask = (2u << (hb - lo)) - 1u;
 #pragma unroll
   for (int e = 0; e < E; ++e)
