@@ -129,6 +129,8 @@ int32_t lsa_sparse_attn_prefill(const lsa_bf16* q, const lsa_bf16* k, const lsa_
  * one-GPU form). The selected list of each index row is cut into n_split
  * contiguous parts of ceil(n_sel / n_split) entries; each part yields
  * (max, sum, output) partials, merged over parts in a fixed binary tree.
+ * The partials live in the workspace: max and sum in fp32, each part's output
+ * normalised by its own sum in fp16 (rounded to nearest).
  *   q [B, n_q, H, D] bf16; k_cache / v_cache [B, n_k, D] bf16
  *   idx [B, n_idx, K_tot], n_sel [B, n_idx]; n_idx = 1: every query row of a
  *   sequence uses the one index (MTP draft reuse), else n_idx = n_q
