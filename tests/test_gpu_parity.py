@@ -282,7 +282,7 @@ def random_index(B, rows, K_tot, t_of_row, n_k, seed):
     return idx, n_sel
 
 
-@pytest.mark.parametrize("H", [16, 64, 128])
+@pytest.mark.parametrize("H", [16, 32, 64, 128])
 def test_prefill_attention(H):
     say(f"prefill attention H={H}")
     B, Lq, K_tot = 2, 333, 96
