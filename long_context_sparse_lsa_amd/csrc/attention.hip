@@ -635,53 +635,58 @@ __global__ __launch_bounds__(64 * TW * KS) void attn_decode_partial(DecodeArgs a
   }
 }
 
-// One row per 32 threads, 4 output dims per thread. Weighted sums over the
+// One row per 16 threads, 8 output dims per thread. Weighted sums over the
 // NS >= n_split leaves (absent parts are exact zeros) use a fixed binary
 // tree; for NS up to 64 the leaves beyond the next power of two above
 // n_split add exact zeros only, so every NS gives the same result.
 template <int NS>
 __global__ __launch_bounds__(256) void attn_decode_merge(DecodeArgs a) {
   const int R = a.n_q * a.H;
-  const int64_t brow = (int64_t)blockIdx.x * 8 + (threadIdx.x >> 5);
+  const int64_t brow = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
   if (brow >= (int64_t)a.B * R) return;
   const int b = (int)(brow / R), r = (int)(brow % R);
-  const int d = 4 * (threadIdx.x & 31);
+  const int d = 8 * (threadIdx.x & 15);
   const int64_t row0 = (int64_t)b * a.n_split * R + r;
   const float* pm = a.ws_m + row0;
   const float* pl = a.ws_l + row0;
   const _Float16* po = a.ws_o + row0 * kD + d;
   float mj[NS], lv[NS];
-  v4f ov[NS];
+  v8h ov[NS];
 #pragma unroll
   for (int j = 0; j < NS; ++j) {
     const bool in = j < a.n_split;
     const int jr = in ? j * R : 0;
     mj[j] = in ? pm[jr] : -INFINITY;
     lv[j] = in ? pl[jr] : 0.f;
-    const v4h w = in ? *(const v4h*)(po + (int64_t)jr * kD) : v4h{};
-    ov[j] = v4f{(float)w[0], (float)w[1], (float)w[2], (float)w[3]};
+    ov[j] = in ? *(const v8h*)(po + (int64_t)jr * kD) : v8h{};
   }
   float M = -INFINITY;
 #pragma unroll
   for (int j = 0; j < NS; ++j) M = fmaxf(M, mj[j]);
+  // each part's normalised output weighed by l * 2^(m - M), summed in a
+  // fixed binary tree in fp32
+  float acc[NS][8];
 #pragma unroll
   for (int j = 0; j < NS; ++j) {
     const float wj = (j < a.n_split && M != -INFINITY) ? __builtin_amdgcn_exp2f(mj[j] - M) : 0.f;
     lv[j] *= wj;
-    ov[j] *= lv[j];  // the part's normalised output weighed by l * 2^(m - M)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[j][e] = (float)ov[j][e] * lv[j];
   }
 #pragma unroll
   for (int s = 1; s < NS; s <<= 1)
 #pragma unroll
     for (int j = 0; j + s < NS; j += 2 * s) {
       lv[j] += lv[j + s];
-      ov[j] += ov[j + s];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[j][e] += acc[j + s][e];
     }
   const float Lam = lv[0];
   const float inv = Lam > 0.f ? 1.f / Lam : 0.f;
-  const uint32_t w0 = pack_bf16x2(ov[0][0] * inv, ov[0][1] * inv);
-  const uint32_t w1 = pack_bf16x2(ov[0][2] * inv, ov[0][3] * inv);
-  *(v2u*)(a.o + brow * kD + d) = v2u{w0, w1};
+  v4u out;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) out[e] = pack_bf16x2(acc[0][2 * e] * inv, acc[0][2 * e + 1] * inv);
+  *(v4u*)(a.o + brow * kD + d) = out;
   if (a.lse && d == 0) a.lse[brow] = Lam > 0.f ? (M + log2f(Lam)) * 0.69314718055994531f : -INFINITY;
 }
 
@@ -721,7 +726,7 @@ static hipError_t launch_partial(const DecodeArgs& a, hipStream_t st) {
 hipError_t launch_attn_decode(const DecodeArgs& a, hipStream_t st) {
   hipError_t e = launch_partial(a, st);
   if (e != hipSuccess) return e;
-  const dim3 grid((unsigned)(((int64_t)a.B * a.n_q * a.H + 7) / 8));
+  const dim3 grid((unsigned)(((int64_t)a.B * a.n_q * a.H + 15) / 16));
   KernelTimer kt("attn_decode_merge", st);
   if (a.n_split <= 1) hipLaunchKernelGGL(attn_decode_merge<1>, grid, dim3(256), 0, st, a);
   else if (a.n_split <= 2) hipLaunchKernelGGL(attn_decode_merge<2>, grid, dim3(256), 0, st, a);

@@ -14,6 +14,7 @@ typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
 typedef unsigned int v4u __attribute__((ext_vector_type(4)));
 typedef unsigned int v2u __attribute__((ext_vector_type(2)));
 typedef _Float16 v4h __attribute__((ext_vector_type(4)));
+typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 
 constexpr int kWave = 64;
 constexpr int32_t kMasked = INT32_MIN;
