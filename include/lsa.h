@@ -119,7 +119,8 @@ int32_t lsa_hier_select(const int8_t* q_idx, const int8_t* k_idx, const int8_t* 
  * consecutive layers is cross-layer index reuse (CLI paragraph).
  *   q [B, L, H, D] bf16, k / v [B, n_k, D] bf16, idx [B, L, K_tot], n_sel [B, L]
  *   o [B, L, H, D] bf16 out; lse [B, L, H] fp32 out (natural log) or NULL
- * Supported: D = 128; H in {16, 32, 64, 128}. */
+ * Supported: D = 128; H in {16, 32, 64, 128}; n_k <= 16777215 (cache rows are
+ * addressed with 32-bit byte offsets). */
 int32_t lsa_sparse_attn_prefill(const lsa_bf16* q, const lsa_bf16* k, const lsa_bf16* v,
                                 const int32_t* idx, const int32_t* n_sel, int32_t B,
                                 int32_t L, int32_t n_k, int32_t H, int32_t D, int32_t K_tot,
@@ -135,7 +136,8 @@ int32_t lsa_sparse_attn_prefill(const lsa_bf16* q, const lsa_bf16* k, const lsa_
  *   idx [B, n_idx, K_tot], n_sel [B, n_idx]; n_idx = 1: every query row of a
  *   sequence uses the one index (MTP draft reuse), else n_idx = n_q
  *   o [B, n_q, H, D] bf16 out; lse [B, n_q, H] fp32 out or NULL
- * Supported: D = 128; H in {16, 32, 64, 128}; n_split in [1, 64]. */
+ * Supported: D = 128; H in {16, 32, 64, 128}; n_split in [1, 64];
+ * n_k <= 16777215. */
 int32_t lsa_sparse_attn_decode(const lsa_bf16* q, const lsa_bf16* k_cache,
                                const lsa_bf16* v_cache, const int32_t* idx,
                                const int32_t* n_sel, int32_t n_idx, int32_t B, int32_t n_q,

@@ -31,7 +31,12 @@ CFLAGS = [
 # accumulators in ordinary VGPRs, which their VALU epilogues read directly
 # (no copies between accumulation and vector registers in the loops).
 _VGPR_FORM = ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]
-FILE_FLAGS = {"index_prefill.hip": _VGPR_FORM, "index_decode.hip": _VGPR_FORM, "attention.hip": _VGPR_FORM}
+# The softmax takes no NaN inputs (scores of finite bf16 rows, -inf for
+# masked keys) and never depends on the sign of a zero sum, so its max and
+# sum chains need no NaN quieting or -0 handling.
+_NO_NAN = ["-fno-honor-nans", "-fno-signed-zeros"]
+FILE_FLAGS = {"index_prefill.hip": _VGPR_FORM, "index_decode.hip": _VGPR_FORM,
+              "attention.hip": _VGPR_FORM + _NO_NAN}
 
 
 def sources():

@@ -403,7 +403,7 @@ extern "C" int32_t lsa_sparse_attn_prefill(const lsa_bf16* q, const lsa_bf16* k,
   if (!al16(q) || !al16(k) || !al16(v) || !al4(idx) || !al4(n_sel) || !al16(o)) return LSA_INVALID_ARG;
   if (lse != nullptr && !al4(lse)) return LSA_INVALID_ARG;
   if (B <= 0 || L <= 0 || n_k <= 0 || K_tot <= 0 || !(scale > 0.f) || !isfinite(scale)) return LSA_INVALID_ARG;
-  if (D != 128 || !heads_ok(H)) return LSA_UNSUPPORTED;
+  if (D != 128 || !heads_ok(H) || n_k > kMaxCacheKeys) return LSA_UNSUPPORTED;
   PrefillArgs a{q, k, v, idx, n_sel, B, L, n_k, H, K_tot, scale * 1.4426950408889634f, o, lse};
   return hip_status(launch_attn_prefill(a, (hipStream_t)stream));
 }
@@ -417,7 +417,7 @@ extern "C" int32_t lsa_sparse_attn_decode(const lsa_bf16* q, const lsa_bf16* k_c
                                           void* stream) {
   if (B <= 0 || n_q <= 0 || n_k <= 0 || K_tot <= 0 || !(scale > 0.f) || !isfinite(scale)) return LSA_INVALID_ARG;
   if (n_idx != 1 && n_idx != n_q) return LSA_INVALID_ARG;
-  if (D != 128 || !heads_ok(H) || n_split < 1 || n_split > 64) return LSA_UNSUPPORTED;
+  if (D != 128 || !heads_ok(H) || n_split < 1 || n_split > 64 || n_k > kMaxCacheKeys) return LSA_UNSUPPORTED;
   const size_t need = align_up(decode_ws_bytes(B, n_q, H, n_split));
   if (ws_needed) *ws_needed = need;
   if (ws == nullptr) return ws_needed ? LSA_OK : LSA_WORKSPACE;  // size query

@@ -77,26 +77,47 @@ __device__ __forceinline__ void load_q(const uint16_t* qrow, int h0, int H, v8bf
 // to LDS, gathered by a group of TW waves that share the block: thread gt
 // of the group (gt = 64 * wave-in-group + lane) loads, for i < 8 / TW, the
 // 16 bytes at 16 * (gt % 16) of the K row and of the V row of key
-// gt / 16 + 4 * TW * i. A key outside [0, n_k) loads row 0 instead: its
-// score is set to -inf and its probability to 0 before use, so only
-// finiteness matters and the loads need no masking.
+// gt / 16 + 4 * TW * i. The loads are buffer loads over one sequence's
+// cache (a 32-bit byte offset from a wave-uniform base, range-checked by the
+// hardware): a key outside [0, n_k) reads zeros, or, where its offset wraps
+// past 2^32, some row of the cache. Its score is set to -inf and its
+// probability to 0 before use, so only finiteness matters and the loads need
+// no masking. The 32-bit offsets bound a cache at kMaxCacheKeys rows.
 template <int TW>
 struct KVStage {
   v4u k[8 / TW], v[8 / TW];
 };
+
+// Buffer resource over rows [0, n_k) of one sequence's K or V cache. The base
+// is wave-uniform by construction; readfirstlane lets the compiler keep the
+// resource in scalar registers.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t cache_rsrc(const uint16_t* base, int n_k) {
+  const uint64_t p = (uint64_t)(uintptr_t)base;
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)p);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(p >> 32));
+  const int bytes = __builtin_amdgcn_readfirstlane((int)((uint32_t)n_k * (uint32_t)(kD * 2)));
+  return __builtin_amdgcn_make_buffer_rsrc((void*)(uintptr_t)(((uint64_t)hi << 32) | lo), (short)0, bytes,
+                                           0x00020000);
+}
+
+// 16 bytes at part 16 * part of row pos (unsigned offset arithmetic: a
+// negative or huge pos wraps, and lands out of range or on some row)
+__device__ __forceinline__ v4u load_row16(__amdgpu_buffer_rsrc_t r, int pos, int part) {
+  const uint32_t off = (uint32_t)pos * (uint32_t)(kD * 2) + 16u * (uint32_t)part;
+  return __builtin_bit_cast(v4u, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
+}
 
 // pos: lane c (and c + 32) holds the cache position of key c of the block.
 template <int TW>
 __device__ __forceinline__ void gather_kv(const uint16_t* K, const uint16_t* V, int pos, int n_k, int gw,
                                           KVStage<TW>& s) {
   const int l = lane_id();
+  const __amdgpu_buffer_rsrc_t kr = cache_rsrc(K, n_k), vr = cache_rsrc(V, n_k);
 #pragma unroll
   for (int i = 0; i < 8 / TW; ++i) {
-    const int key = 4 * gw + (l >> 4) + 4 * TW * i;
-    const int pe = __shfl(pos, key, 64);
-    const int64_t off = ((unsigned)pe < (unsigned)n_k ? (int64_t)pe : 0) * kD + 8 * (l & 15);
-    s.k[i] = *(const v4u*)(K + off);
-    s.v[i] = *(const v4u*)(V + off);
+    const int pe = __shfl(pos, 4 * gw + (l >> 4) + 4 * TW * i, 64);
+    s.k[i] = load_row16(kr, pe, l & 15);
+    s.v[i] = load_row16(vr, pe, l & 15);
   }
 }
 
@@ -194,12 +215,12 @@ template <int TW>
 __device__ __forceinline__ void gather_kv_lds(const uint16_t* K, const uint16_t* V, const int* pb, int n_k, int gw,
                                               KVStage<TW>& s) {
   const int l = lane_id();
+  const __amdgpu_buffer_rsrc_t kr = cache_rsrc(K, n_k), vr = cache_rsrc(V, n_k);
 #pragma unroll
   for (int i = 0; i < 8 / TW; ++i) {
     const int pe = pb[4 * gw + (l >> 4) + 4 * TW * i];
-    const int64_t off = ((unsigned)pe < (unsigned)n_k ? (int64_t)pe : 0) * kD + 8 * (l & 15);
-    s.k[i] = *(const v4u*)(K + off);
-    s.v[i] = *(const v4u*)(V + off);
+    s.k[i] = load_row16(kr, pe, l & 15);
+    s.v[i] = load_row16(vr, pe, l & 15);
   }
 }
 

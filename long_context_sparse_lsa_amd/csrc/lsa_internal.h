@@ -86,7 +86,9 @@ void select_bind_ws(SelectArgs& a, void* ws, int n_rows);
 hipError_t launch_select(const SelectArgs& a, hipStream_t st);
 
 // Sparse attention launches (bf16 bit patterns as uint16_t; sl2 is
-// scale * log2(e): softmax runs in base 2).
+// scale * log2(e): softmax runs in base 2). K/V rows of one sequence are
+// gathered with 32-bit byte offsets, which bounds n_k.
+constexpr int32_t kMaxCacheKeys = (1 << 24) - 1;
 struct PrefillArgs {
   const uint16_t *q, *k, *v;
   const int32_t *idx, *n_sel;

@@ -135,6 +135,9 @@ def test_attention_checks():
     bad_h = list(args)
     bad_h[8] = 48
     assert lib.lsa_sparse_attn_prefill(*bad_h, f, None, None) == L.LSA_UNSUPPORTED
+    big = list(args)
+    big[7] = 1 << 24    # n_k past the 32-bit byte offsets of the cache gathers
+    assert lib.lsa_sparse_attn_prefill(*big, f, None, None) == L.LSA_UNSUPPORTED
     bad_s = list(args)
     bad_s[11] = float("nan")
     assert lib.lsa_sparse_attn_prefill(*bad_s, f, None, None) == L.LSA_INVALID_ARG
@@ -147,6 +150,9 @@ def test_attention_checks():
     bad = list(dargs)
     bad[5] = 3          # n_idx neither 1 nor n_q
     assert lib.lsa_sparse_attn_decode(*bad, f, None, None, 0, ctypes.byref(need), None) == L.LSA_INVALID_ARG
+    bad = list(dargs)
+    bad[8] = 1 << 24    # n_k
+    assert lib.lsa_sparse_attn_decode(*bad, f, None, None, 0, ctypes.byref(need), None) == L.LSA_UNSUPPORTED
     bad = list(dargs)
     bad[12] = 65        # n_split
     assert lib.lsa_sparse_attn_decode(*bad, f, None, None, 0, ctypes.byref(need), None) == L.LSA_UNSUPPORTED
