@@ -88,16 +88,20 @@ struct KVStage {
   v4u k[8 / TW], v[8 / TW];
 };
 
-// Buffer resource over rows [0, n_k) of one sequence's K or V cache. The base
-// is wave-uniform by construction; readfirstlane lets the compiler keep the
-// resource in scalar registers.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t cache_rsrc(const uint16_t* base, int n_k) {
+// Buffer resource over `bytes` bytes at base. Base and size are wave-uniform
+// at every use; readfirstlane lets the compiler keep the resource in scalar
+// registers.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t uniform_rsrc(const void* base, uint32_t bytes) {
   const uint64_t p = (uint64_t)(uintptr_t)base;
   const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)p);
   const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(p >> 32));
-  const int bytes = __builtin_amdgcn_readfirstlane((int)((uint32_t)n_k * (uint32_t)(kD * 2)));
-  return __builtin_amdgcn_make_buffer_rsrc((void*)(uintptr_t)(((uint64_t)hi << 32) | lo), (short)0, bytes,
-                                           0x00020000);
+  const int nb = __builtin_amdgcn_readfirstlane((int)bytes);
+  return __builtin_amdgcn_make_buffer_rsrc((void*)(uintptr_t)(((uint64_t)hi << 32) | lo), (short)0, nb, 0x00020000);
+}
+
+// Rows [0, n_k) of one sequence's K or V cache.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t cache_rsrc(const uint16_t* base, int n_k) {
+  return uniform_rsrc(base, (uint32_t)n_k * (uint32_t)(kD * 2));
 }
 
 // 16 bytes at part 16 * part of row pos (unsigned offset arithmetic: a
@@ -109,10 +113,9 @@ __device__ __forceinline__ v4u load_row16(__amdgpu_buffer_rsrc_t r, int pos, int
 
 // pos: lane c (and c + 32) holds the cache position of key c of the block.
 template <int TW>
-__device__ __forceinline__ void gather_kv(const uint16_t* K, const uint16_t* V, int pos, int n_k, int gw,
+__device__ __forceinline__ void gather_kv(__amdgpu_buffer_rsrc_t kr, __amdgpu_buffer_rsrc_t vr, int pos, int gw,
                                           KVStage<TW>& s) {
   const int l = lane_id();
-  const __amdgpu_buffer_rsrc_t kr = cache_rsrc(K, n_k), vr = cache_rsrc(V, n_k);
 #pragma unroll
   for (int i = 0; i < 8 / TW; ++i) {
     const int pe = __shfl(pos, 4 * gw + (l >> 4) + 4 * TW * i, 64);
@@ -174,8 +177,10 @@ __device__ void attn_keys(const v8bf (&Q)[NB][8], bool active, const uint16_t* K
   const int l = lane_id(), c = l & 31;
   const int G = l >> 4, jj = l & 15;
   const int vt_off = kVOff + (4 * (G >> 1) + (jj >> 2)) * kVRow + (16 * (G & 1) + 4 * (jj & 3)) * 2;
-  const int ilast = max(se - 1, 0);
-  auto raw_at = [&](int s0) { return ids[min(max(s0 + c, 0), ilast)]; };
+  // positions through a buffer over ids[0, se): entries past se read 0 (and
+  // eff replaces them by -1)
+  const __amdgpu_buffer_rsrc_t ir = uniform_rsrc(ids, (uint32_t)max(se, 0) * 4u);
+  auto raw_at = [&](int s0) { return __builtin_amdgcn_raw_buffer_load_b32(ir, (s0 + c) * 4, 0, 0); };
   auto eff = [&](int s0, int raw) { return s0 + c < se ? raw : -1; };
   // The memory counter is in order: waiting for a position also waits for
   // every gather issued before it. Positions are therefore loaded P blocks
@@ -185,8 +190,9 @@ __device__ void attn_keys(const v8bf (&Q)[NB][8], bool active, const uint16_t* K
   int pr[P + 1];  // raw positions of blocks i .. i + P
 #pragma unroll
   for (int j = 0; j <= P; ++j) pr[j] = raw_at(sb + 32 * j);
+  const __amdgpu_buffer_rsrc_t kr = cache_rsrc(K, n_k), vr = cache_rsrc(V, n_k);
 #pragma unroll
-  for (int j = 0; j < R; ++j) gather_kv<TW>(K, V, eff(sb + 32 * j, pr[j]), n_k, gw, stg[j]);
+  for (int j = 0; j < R; ++j) gather_kv<TW>(kr, vr, eff(sb + 32 * j, pr[j]), gw, stg[j]);
   store_kv<TW>(stg[0], lds, gw);
   for (int it = 0; it < trips; it += R) {
 #pragma unroll
@@ -194,7 +200,7 @@ __device__ void attn_keys(const v8bf (&Q)[NB][8], bool active, const uint16_t* K
       const int s0 = sb + 32 * (it + u);
       if constexpr (SYNC) __syncthreads();  // block it+u in its buffer for all; the other buffer free
       const int pnew = raw_at(s0 + 32 * (P + 1));
-      gather_kv<TW>(K, V, eff(s0 + 32 * R, pr[R]), n_k, gw, stg[u]);
+      gather_kv<TW>(kr, vr, eff(s0 + 32 * R, pr[R]), gw, stg[u]);
       if (active && s0 < se) attn_block<NB>(Q, lds + (u & 1) * kBlkLds, eff(s0, pr[0]), n_k, sl2, vt_off, st);
       store_kv<TW>(stg[(u + 1) % R], lds + ((u + 1) & 1) * kBlkLds, gw);
 #pragma unroll
@@ -212,10 +218,9 @@ __device__ void attn_keys(const v8bf (&Q)[NB][8], bool active, const uint16_t* K
 // trips_used: the key span of the chunk's longest subrange (the same for all
 // waves of the workgroup); steps past its last block are not run.
 template <int TW>
-__device__ __forceinline__ void gather_kv_lds(const uint16_t* K, const uint16_t* V, const int* pb, int n_k, int gw,
-                                              KVStage<TW>& s) {
+__device__ __forceinline__ void gather_kv_lds(__amdgpu_buffer_rsrc_t kr, __amdgpu_buffer_rsrc_t vr, const int* pb,
+                                              int gw, KVStage<TW>& s) {
   const int l = lane_id();
-  const __amdgpu_buffer_rsrc_t kr = cache_rsrc(K, n_k), vr = cache_rsrc(V, n_k);
 #pragma unroll
   for (int i = 0; i < 8 / TW; ++i) {
     const int pe = pb[4 * gw + (l >> 4) + 4 * TW * i];
@@ -233,8 +238,9 @@ __device__ void attn_keys_lds(const v8bf (&Q)[NB][8], bool active, const uint16_
   const int G = l >> 4, jj = l & 15;
   const int vt_off = kVOff + (4 * (G >> 1) + (jj >> 2)) * kVRow + (16 * (G & 1) + 4 * (jj & 3)) * 2;
   KVStage<TW> stg[R];
+  const __amdgpu_buffer_rsrc_t kr = cache_rsrc(K, n_k), vr = cache_rsrc(V, n_k);
 #pragma unroll
-  for (int j = 0; j < R; ++j) gather_kv_lds<TW>(K, V, pos + 32 * j, n_k, gw, stg[j]);
+  for (int j = 0; j < R; ++j) gather_kv_lds<TW>(kr, vr, pos + 32 * j, gw, stg[j]);
   store_kv<TW>(stg[0], lds, gw);
   const int nsteps = (trips_used + 31) / 32;  // the blocks of the chunk's longest subrange
   for (int it = 0; it < trips; it += R) {
@@ -243,7 +249,7 @@ __device__ void attn_keys_lds(const v8bf (&Q)[NB][8], bool active, const uint16_
       const int bi = it + u;
       if (bi >= nsteps) break;  // the same for every wave of the workgroup
       __syncthreads();  // block bi in its buffer for all; the other buffer free
-      gather_kv_lds<TW>(K, V, pos + 32 * (bi + R), n_k, gw, stg[u]);
+      gather_kv_lds<TW>(kr, vr, pos + 32 * (bi + R), gw, stg[u]);
       if (active && 32 * bi < cnt) attn_block<NB>(Q, lds + (u & 1) * kBlkLds, pos[32 * bi + c], n_k, sl2, vt_off, st);
       store_kv<TW>(stg[(u + 1) % R], lds + ((u + 1) & 1) * kBlkLds, gw);
     }
