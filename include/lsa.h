@@ -92,6 +92,26 @@ int32_t lsa_select_topk(const int32_t* scores, const int8_t* q_idx, const int8_t
                         int32_t* n_sel, void* ws, size_t ws_bytes, size_t* ws_needed,
                         void* stream);
 
+/* Flat selection for a decode batch whose sequences hold different numbers of
+ * cached keys (a ragged batch); the same selection as lsa_select_topk (SI
+ * paragraph; sinks), fused with the scoring.
+ *   ctx_len [B] int32, DEVICE: keys held by each sequence, read on the GPU
+ *           and clamped to [n_q, n_k] (so a bad length cannot read past the
+ *           cache); L_b = clamp(ctx_len[b], n_q, n_k)
+ *   q_idx [B, n_q, H_I, d_I] int8; k_idx [B, n_k, d_I] int8, n_k the cache
+ *           capacity; only keys 0 .. L_b - 1 of sequence b are ever visible
+ *   query row i of sequence b sits at position t = L_b - n_q + i (the last
+ *   n_q positions of the sequence)
+ *   idx [B, n_q, K_tot] int32 out, ascending, -1 padded; n_sel [B, n_q] out,
+ *   min(t + 1, K_tot)
+ * The workspace is sized for full-length sequences (L_b = n_k). Errors as
+ * lsa_select_topk; ctx_len NULL or misaligned is LSA_INVALID_ARG. */
+int32_t lsa_select_topk_ragged(const int8_t* q_idx, const int8_t* k_idx, const int32_t* w,
+                               int32_t B, int32_t n_q, int32_t n_k, int32_t H_I, int32_t d_I,
+                               const int32_t* ctx_len, lsa_select_cfg cfg, int32_t* idx,
+                               int32_t* n_sel, void* ws, size_t ws_bytes, size_t* ws_needed,
+                               void* stream);
+
 /* HI block summary: k_blk[b, j, :] = clamp(round-half-even(mean of the keys of
  * block j), -128, 127); a tail block of c < blk keys uses its own mean.
  *   k_idx [B, n_k, d_I] int8 -> k_blk [B, ceil(n_k / blk), d_I] int8

@@ -41,6 +41,7 @@ SIGNATURES = {
     "lsa_status_string": (ctypes.c_char_p, [_I]),
     "lsa_index_score": (_I, [_P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _P]),
     "lsa_select_topk": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, SelectCfg, _P, _P, _P, _Z, _ZP, _P]),
+    "lsa_select_topk_ragged": (_I, [_P, _P, _P, _I, _I, _I, _I, _I, _P, SelectCfg, _P, _P, _P, _Z, _ZP, _P]),
     "lsa_block_summary": (_I, [_P, _I, _I, _I, _I, _P, _P]),
     "lsa_hier_select": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, SelectCfg, _P, _P, _P, _Z, _ZP, _P]),
     "lsa_sparse_attn_prefill": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _P, _P, _P]),
@@ -162,6 +163,37 @@ def lsa_select_topk(q_idx=None, k_idx=None, w=None, n_sink=4, n_window=0, k_dyn=
         idx, n_sel = out
     _check("lsa_select_topk", lib.lsa_select_topk(*args, _ptr(idx), _ptr(n_sel), _ptr(ws), ws.numel(),
                                                   None, _stream()))
+    return idx, n_sel
+
+
+def lsa_select_topk_ragged(q_idx, k_idx, w, ctx_len, n_sink=4, n_window=0, k_dyn=0, out=None):
+    """Flat selection for a ragged decode batch: sequence b holds
+    clamp(ctx_len[b], n_q, n_k) keys of its cache k_idx [B, n_k, d_I], and its
+    n_q rows are its last n_q positions. ctx_len [B] int32 on the device.
+    Returns (idx [B, n_q, K_tot] int32, n_sel [B, n_q] int32)."""
+    lib = load()
+    _dev(q_idx, torch.int8, "q_idx")
+    _dev(k_idx, torch.int8, "k_idx")
+    _dev(ctx_len, torch.int32, "ctx_len")
+    B, n_q, H_I, d_I = q_idx.shape
+    n_k = k_idx.shape[1]
+    if k_idx.shape != (B, n_k, d_I) or tuple(ctx_len.shape) != (B,):
+        raise ValueError("k_idx / ctx_len shape mismatch")
+    wh, wp = _weights(w, H_I)
+    cfg = SelectCfg(n_sink, n_window, k_dyn)
+    K_tot = n_sink + n_window + k_dyn
+    need = ctypes.c_size_t(0)
+    args = (_ptr(q_idx), _ptr(k_idx), wp, B, n_q, n_k, H_I, d_I, _ptr(ctx_len), cfg)
+    _check("lsa_select_topk_ragged",
+           lib.lsa_select_topk_ragged(*args, None, None, None, 0, ctypes.byref(need), None))
+    ws = _workspace(need.value, q_idx.device)
+    if out is None:
+        idx = torch.empty((B, n_q, K_tot), dtype=torch.int32, device=q_idx.device)
+        n_sel = torch.empty((B, n_q), dtype=torch.int32, device=q_idx.device)
+    else:
+        idx, n_sel = out
+    _check("lsa_select_topk_ragged", lib.lsa_select_topk_ragged(*args, _ptr(idx), _ptr(n_sel), _ptr(ws),
+                                                                ws.numel(), None, _stream()))
     return idx, n_sel
 
 

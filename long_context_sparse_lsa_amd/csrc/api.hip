@@ -114,6 +114,79 @@ extern "C" int32_t lsa_index_score(const int8_t* q_idx, const int8_t* k_idx, con
   return hip_status(launch_index_score(a, (hipStream_t)stream));
 }
 
+// Fused path of the flat selection: score a pass of rows (candidates only)
+// into the workspace, then select. A pass covers nb sequences times one range
+// of Rr query rows. ctx_len (device, per sequence, or null): ragged lengths,
+// row i of sequence b at position clamp(ctx_len[b], n_q, n_k) - n_q + i
+// (q_off is then n_k - n_q).
+static int32_t fused_select(const int8_t* q_idx, const int8_t* k_idx, const WArgs& wa, int B, int n_q, int n_k,
+                            int H_I, int d_I, int q_off, const lsa_select_cfg& cfg, int R, int nb_pass,
+                            const int32_t* ctx_len, int32_t* idx, int32_t* n_sel, void* ws, hipStream_t st) {
+  const int K_tot = cfg.n_sink + cfg.n_window + cfg.k_dyn;
+  int32_t s = LSA_OK;
+  SelectArgs sa{};
+  sa.mode = SEL_FLAT;
+  sa.n_sink = cfg.n_sink;
+  sa.n_window = cfg.n_window;
+  sa.k_dyn = cfg.k_dyn;
+  sa.out_ld = K_tot;
+  sa.k_cap = k_cap_of(cfg.k_dyn);
+  int32_t* sbuf = (int32_t*)ws;
+  void* sel_ws = (char*)ws + align_up((size_t)R * nb_pass * n_k * sizeof(int32_t));
+  for (int b0 = 0; b0 < B; b0 += nb_pass) {
+    const int nb = std::min(nb_pass, B - b0);
+    const SeqShift shift{ctx_len ? ctx_len + b0 : nullptr, n_q, n_k};
+    for (int r0 = 0; r0 < n_q; r0 += R) {
+      const int Rr = std::min(R, n_q - r0);
+      const int t_last = q_off + r0 + Rr - 1;
+      const int64_t nc_last = (int64_t)t_last - cfg.n_window - cfg.n_sink + 1;
+      if (nc_last > 0 && t_last + 1 > K_tot) {
+        ScoreArgs a{};
+        a.w = wa;
+        a.q = q_idx + ((int64_t)b0 * n_q + r0) * H_I * d_I;
+        a.k = k_idx + (int64_t)b0 * n_k * d_I;
+        a.B = nb;
+        a.n_q = Rr;
+        a.n_k = n_k;
+        a.H_I = H_I;
+        a.d_I = d_I;
+        a.q_bstride = (int64_t)n_q * H_I * d_I;
+        a.k_bstride = (int64_t)n_k * d_I;
+        a.s_bstride = (int64_t)Rr * n_k;
+        a.ld = n_k;
+        a.n_keys = std::min<int64_t>(n_k, (int64_t)t_last - cfg.n_window + 1);
+        a.mask_off = q_off + r0 - cfg.n_window;
+        a.pos_lo = cfg.n_sink;
+        a.blocks = nullptr;
+        a.fill_masked = 0;
+        a.scores = sbuf;
+        a.shift = shift;
+        if (a.n_keys > 0) {
+          s = hip_status(launch_index_score(a, st));
+          if (s != LSA_OK) return s;
+        }
+      }
+      // rows of the pass: sequence b0 + j, query r0 + i at row j * Rr + i
+      sa.scores = sbuf;
+      sa.ld = n_k;
+      sa.n_rows = nb * Rr;
+      sa.n_q = Rr;
+      sa.q_off = q_off + r0;
+      sa.row0 = 0;
+      sa.shift = shift;
+      select_plan(sa, nc_last);
+      select_bind_ws(sa, sel_ws, nb * Rr);
+      // nb > 1 only when Rr == n_q (r0 == 0), so the pass's output rows are
+      // contiguous in idx / n_sel
+      sa.idx = idx + ((int64_t)b0 * n_q + r0) * K_tot;
+      sa.n_sel = n_sel + (int64_t)b0 * n_q + r0;
+      s = hip_status(launch_select(sa, st));
+      if (s != LSA_OK) return s;
+    }
+  }
+  return LSA_OK;
+}
+
 extern "C" int32_t lsa_select_topk(const int32_t* scores, const int8_t* q_idx, const int8_t* k_idx,
                                    const int32_t* w, int32_t B, int32_t n_q, int32_t n_k,
                                    int32_t H_I, int32_t d_I, int32_t q_off, lsa_select_cfg cfg,
@@ -185,59 +258,37 @@ extern "C" int32_t lsa_select_topk(const int32_t* scores, const int8_t* q_idx, c
     return LSA_OK;
   }
 
-  // Fused path: score a pass of rows (candidates only) into workspace, then
-  // select. A pass covers nb sequences times one range of Rr query rows.
-  int32_t* sbuf = (int32_t*)ws;
-  void* sel_ws = (char*)ws + align_up((size_t)R * nb_pass * n_k * sizeof(int32_t));
-  for (int b0 = 0; b0 < B; b0 += nb_pass) {
-    const int nb = std::min(nb_pass, B - b0);
-    for (int r0 = 0; r0 < n_q; r0 += R) {
-      const int Rr = std::min(R, n_q - r0);
-      const int t_last = q_off + r0 + Rr - 1;
-      const int64_t nc_last = (int64_t)t_last - cfg.n_window - cfg.n_sink + 1;
-      if (nc_last > 0 && t_last + 1 > K_tot) {
-        ScoreArgs a{};
-        a.w = wa;
-        a.q = q_idx + ((int64_t)b0 * n_q + r0) * H_I * d_I;
-        a.k = k_idx + (int64_t)b0 * n_k * d_I;
-        a.B = nb;
-        a.n_q = Rr;
-        a.n_k = n_k;
-        a.H_I = H_I;
-        a.d_I = d_I;
-        a.q_bstride = (int64_t)n_q * H_I * d_I;
-        a.k_bstride = (int64_t)n_k * d_I;
-        a.s_bstride = (int64_t)Rr * n_k;
-        a.ld = n_k;
-        a.n_keys = std::min<int64_t>(n_k, (int64_t)t_last - cfg.n_window + 1);
-        a.mask_off = q_off + r0 - cfg.n_window;
-        a.pos_lo = cfg.n_sink;
-        a.blocks = nullptr;
-        a.fill_masked = 0;
-        a.scores = sbuf;
-        if (a.n_keys > 0) {
-          s = hip_status(launch_index_score(a, st));
-          if (s != LSA_OK) return s;
-        }
-      }
-      // rows of the pass: sequence b0 + j, query r0 + i at row j * Rr + i
-      sa.scores = sbuf;
-      sa.ld = n_k;
-      sa.n_rows = nb * Rr;
-      sa.n_q = Rr;
-      sa.q_off = q_off + r0;
-      sa.row0 = 0;
-      select_plan(sa, nc_last);
-      select_bind_ws(sa, sel_ws, nb * Rr);
-      // nb > 1 only when Rr == n_q (r0 == 0), so the pass's output rows are
-      // contiguous in idx / n_sel
-      sa.idx = idx + ((int64_t)b0 * n_q + r0) * K_tot;
-      sa.n_sel = n_sel + (int64_t)b0 * n_q + r0;
-      s = hip_status(launch_select(sa, st));
-      if (s != LSA_OK) return s;
-    }
-  }
-  return LSA_OK;
+  return fused_select(q_idx, k_idx, wa, B, n_q, n_k, H_I, d_I, q_off, cfg, R, nb_pass, nullptr, idx, n_sel, ws,
+                      st);
+}
+
+extern "C" int32_t lsa_select_topk_ragged(const int8_t* q_idx, const int8_t* k_idx, const int32_t* w,
+                                          int32_t B, int32_t n_q, int32_t n_k, int32_t H_I, int32_t d_I,
+                                          const int32_t* ctx_len, lsa_select_cfg cfg, int32_t* idx,
+                                          int32_t* n_sel, void* ws, size_t ws_bytes, size_t* ws_needed,
+                                          void* stream) {
+  int32_t s = cfg_ok(cfg);
+  if (s != LSA_OK) return s;
+  if (B <= 0 || n_q <= 0 || n_k <= 0 || n_q > n_k) return LSA_INVALID_ARG;
+  if (!al16(q_idx) || !al16(k_idx) || !al4(ctx_len)) return LSA_INVALID_ARG;
+  if (!hi_ok(H_I) || !di_ok(d_I)) return LSA_UNSUPPORTED;
+  const int k_cap = k_cap_of(cfg.k_dyn);
+  const int64_t max_nc = (int64_t)n_k - cfg.n_window - cfg.n_sink;  // candidates of a full-length row
+  if (!survivors_ok(max_nc, k_cap)) return LSA_UNSUPPORTED;
+  WArgs wa{};
+  s = load_weights(w, H_I, d_I, wa);
+  if (s != LSA_OK) return s;
+  int R = 0, nb_pass = 1;
+  fused_pass(B, n_q, n_k, R, nb_pass);
+  const size_t rows = (size_t)R * nb_pass;
+  size_t need = align_up(rows * n_k * sizeof(int32_t)) + select_ws_bytes((int)rows, chunks_of(max_nc, k_cap), k_cap);
+  need = align_up(std::max<size_t>(need, 1));
+  if (ws_needed) *ws_needed = need;
+  if (ws == nullptr) return ws_needed ? LSA_OK : LSA_WORKSPACE;  // size query
+  if (!al4(idx) || !al4(n_sel) || !al16(ws)) return LSA_INVALID_ARG;
+  if (ws_bytes < need) return LSA_WORKSPACE;
+  return fused_select(q_idx, k_idx, wa, B, n_q, n_k, H_I, d_I, n_k - n_q, cfg, R, nb_pass, ctx_len, idx, n_sel,
+                      ws, (hipStream_t)stream);
 }
 
 extern "C" int32_t lsa_block_summary(const int8_t* k_idx, int32_t B, int32_t n_k, int32_t d_I,

@@ -77,6 +77,7 @@ __device__ __forceinline__ void scan_keys(const ScoreArgs& a, const v4i (&A)[HI 
                                           int v1) {
   constexpr int MB = HI >= 64 ? HI / 32 : 2;
   constexpr int NQ = 32 * MB / HI;  // query rows per wave: 1 or 2
+  const int mask_off = a.mask_off + seq_shift(a.shift, b);
   constexpr int MQ = MB / NQ;       // M-blocks per query
   constexpr int KS = DI / 32;
   const int l = lane_id(), g = l >> 5, c = l & 31;
@@ -99,7 +100,7 @@ __device__ __forceinline__ void scan_keys(const ScoreArgs& a, const v4i (&A)[HI 
   auto store = [&](int qi, int v, int p, int val) {
     const int gq = q0 + qi;
     if (gq >= a.n_q || v >= v1) return;
-    const bool vis = p >= a.pos_lo && p <= a.mask_off + gq;
+    const bool vis = p >= a.pos_lo && p <= mask_off + gq;
     if (vis) sc[(int64_t)gq * a.ld + v] = val;
     else if (a.fill_masked) sc[(int64_t)gq * a.ld + v] = kMasked;
   };
@@ -149,7 +150,8 @@ __global__ __launch_bounds__(64 * kWaves) void index_decode_kernel(ScoreArgs a, 
   const int v1 = min(v0 + kpw, a.n_keys);
   if (v0 >= v1) return;
   const bool direct = a.blocks == nullptr;
-  if (direct && (v0 > a.mask_off + q0 + nq_tile - 1 || v1 <= a.pos_lo)) {
+  const int mask_off = a.mask_off + seq_shift(a.shift, b);
+  if (direct && (v0 > mask_off + q0 + nq_tile - 1 || v1 <= a.pos_lo)) {
     // nothing in this range is visible to any row of the tile
     if (a.fill_masked) {
       int32_t* sc = a.scores + (int64_t)b * a.s_bstride;

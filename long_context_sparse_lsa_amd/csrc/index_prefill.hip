@@ -323,8 +323,8 @@ hipError_t launch_t(const ScoreArgs& a, int fold_ok, hipStream_t st) {
 }  // namespace
 
 bool index_prefill_supported(const ScoreArgs& a) {
-  return a.blocks == nullptr && (a.H_I == 32 || a.H_I == 64) && (a.d_I == 64 || a.d_I == 128) &&
-         a.n_q >= kQT;
+  return a.blocks == nullptr && a.shift.ctx_len == nullptr && (a.H_I == 32 || a.H_I == 64) &&
+         (a.d_I == 64 || a.d_I == 128) && a.n_q >= kQT;
 }
 
 hipError_t launch_index_prefill(const ScoreArgs& a, hipStream_t st) {

@@ -45,7 +45,8 @@ __global__ __launch_bounds__(256) void index_score_kernel(ScoreArgs a, int QT, i
 
   int32_t* sc = a.scores + (int64_t)b * a.s_bstride;
   const bool direct = a.blocks == nullptr;
-  const int vis_hi = a.mask_off + q0 + nq_tile - 1;
+  const int mask_off = a.mask_off + seq_shift(a.shift, b);
+  const int vis_hi = mask_off + q0 + nq_tile - 1;
   if (direct && (v_begin > vis_hi || v_end <= a.pos_lo)) {
     // nothing visible in this range for any row of the tile
     if (a.fill_masked) {
@@ -122,7 +123,7 @@ __global__ __launch_bounds__(256) void index_score_kernel(ScoreArgs a, int QT, i
     auto store = [&](int qi, int val) {
       const int gq = q0 + qi;
       if (gq >= a.n_q || v >= v_end) return;
-      const bool vis = pc >= a.pos_lo && pc <= a.mask_off + gq;
+      const bool vis = pc >= a.pos_lo && pc <= mask_off + gq;
       if (vis) sc[(int64_t)gq * a.ld + v] = val;
       else if (a.fill_masked) sc[(int64_t)gq * a.ld + v] = kMasked;
     };

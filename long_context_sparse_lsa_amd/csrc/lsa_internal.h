@@ -15,9 +15,21 @@ struct WArgs {
 // Indexer score launch. Row i of sequence b scores the virtual keys
 // [0, n_keys); virtual key v sits at position v, or, when `blocks` is given, at
 // blocks[b * nbr + v / blk] * blk + v % blk (a negative block id is invalid).
-// A key at position p is visible to row i iff pos_lo <= p <= mask_off + i.
-// Visible scores go to scores[b * s_bstride + i * ld + v]; invisible ones get
-// INT32_MIN when fill_masked, else are left untouched.
+// A key at position p is visible to row i iff pos_lo <= p <= mask_off + i
+// (+ the sequence's shift, below). Visible scores go to
+// scores[b * s_bstride + i * ld + v]; invisible ones get INT32_MIN when
+// fill_masked, else are left untouched.
+// Ragged batches: with ctx_len set (device, one entry per sequence of the
+// launch), sequence b holds L_b = clamp(ctx_len[b], ctx_rows, ctx_cap) keys
+// and every visibility limit of its rows moves by L_b - ctx_cap.
+struct SeqShift {
+  const int32_t* ctx_len;
+  int ctx_rows, ctx_cap;
+};
+__device__ __forceinline__ int seq_shift(const SeqShift& s, int b) {
+  if (s.ctx_len == nullptr) return 0;
+  return min(max(s.ctx_len[b], s.ctx_rows), s.ctx_cap) - s.ctx_cap;
+}
 struct ScoreArgs {
   const int8_t* q;
   const int8_t* k;
@@ -30,10 +42,11 @@ struct ScoreArgs {
   int blk, nbr;
   int fill_masked;
   int32_t* scores;
+  SeqShift shift;
 };
 hipError_t launch_index_score(const ScoreArgs& a, hipStream_t st);
 // Many-row variant (LDS-shared key tiles); covers direct keys (no blocks),
-// H_I in {32, 64}, n_q >= 8.
+// H_I in {32, 64}, n_q >= 16, no ragged shift.
 bool index_prefill_supported(const ScoreArgs& a);
 hipError_t launch_index_prefill(const ScoreArgs& a, hipStream_t st);
 // Few-row variant (long per-wave key ranges streamed through registers);
@@ -48,12 +61,14 @@ struct SelectArgs {
   const int32_t* scores;  // row r's scores at scores + r * ld, indexed by virtual key
   int64_t ld;
   int n_rows;
-  // FLAT: row r is query r % n_q at t = q_off + r % n_q; candidates are the
+  // FLAT: row r is query r % n_q at t = q_off + r % n_q (+ the shift of its
+  // sequence r / n_q when shift.ctx_len is set); candidates are the
   // positions [n_sink, t - n_window]; virtual key == position.
   // (row0 offsets the row count when a launch covers a slice of the rows.)
   int n_q, q_off, row0, n_sink, n_window, k_dyn;
   // RAW: candidates [raw_lo, raw_hi] (virtual == position), keep raw_k.
   int raw_lo, raw_hi, raw_k;
+  SeqShift shift;
   // INDIRECT: candidates are virtual keys [0, n_virt) of row r, at positions
   // blocks[r * nbr + v / blk] * blk + v % blk, valid iff score != INT32_MIN;
   // the query sits at t_fixed; keep k_dyn; sinks and window as in FLAT.

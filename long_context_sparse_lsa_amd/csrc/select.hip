@@ -58,7 +58,7 @@ struct RowGeom {
 __device__ __forceinline__ RowGeom row_geom(const SelectArgs& a, int r) {
   RowGeom gm{0, 0, 0, 0, 0};
   if (a.mode == SEL_FLAT) {
-    const int t = a.q_off + (a.row0 + r) % a.n_q;
+    const int t = a.q_off + (a.row0 + r) % a.n_q + seq_shift(a.shift, (a.row0 + r) / a.n_q);
     gm.t = t;
     if (t + 1 <= a.n_sink + a.n_window + a.k_dyn) {
       gm.trivial = 1;

@@ -108,6 +108,34 @@ def test_select_topk_checks_and_workspace_query():
                                P(FAKE), P(FAKE), P(FAKE), 1 << 30, None, None) == L.LSA_RANGE
 
 
+def test_select_topk_ragged_checks():
+    lib = L.load()
+    need = ctypes.c_size_t(0)
+    cfg = L.SelectCfg(4, 512, 2048)
+    w, wp = _w([1] * 64)
+    # sized for full-length sequences: the same workspace as the fused path at q_off = n_k - n_q
+    s = lib.lsa_select_topk_ragged(P(FAKE), P(FAKE), wp, 64, 1, 131072, 64, 128, P(FAKE), cfg,
+                                   None, None, None, 0, ctypes.byref(need), None)
+    assert s == L.LSA_OK and need.value > 0
+    ragged_need = need.value
+    s = lib.lsa_select_topk(None, P(FAKE), P(FAKE), wp, 64, 1, 131072, 64, 128, 131071, cfg,
+                            None, None, None, 0, ctypes.byref(need), None)
+    assert s == L.LSA_OK and need.value == ragged_need
+    # the length array is required
+    assert lib.lsa_select_topk_ragged(P(FAKE), P(FAKE), wp, 64, 1, 131072, 64, 128, None, cfg,
+                                      None, None, None, 0, ctypes.byref(need), None) == L.LSA_INVALID_ARG
+    # more query rows than cache slots, unsupported indexer shape, weights out of range, small workspace
+    assert lib.lsa_select_topk_ragged(P(FAKE), P(FAKE), wp, 2, 8, 4, 64, 128, P(FAKE), cfg,
+                                      None, None, None, 0, ctypes.byref(need), None) == L.LSA_INVALID_ARG
+    assert lib.lsa_select_topk_ragged(P(FAKE), P(FAKE), wp, 2, 1, 4096, 64, 96, P(FAKE), cfg,
+                                      None, None, None, 0, ctypes.byref(need), None) == L.LSA_UNSUPPORTED
+    big, bigp = _w([1 << 16] * 64)
+    assert lib.lsa_select_topk_ragged(P(FAKE), P(FAKE), bigp, 2, 1, 4096, 64, 128, P(FAKE), cfg,
+                                      None, None, None, 0, ctypes.byref(need), None) == L.LSA_RANGE
+    assert lib.lsa_select_topk_ragged(P(FAKE), P(FAKE), wp, 64, 1, 131072, 64, 128, P(FAKE), cfg,
+                                      P(FAKE), P(FAKE), P(FAKE), ragged_need - 256, None, None) == L.LSA_WORKSPACE
+
+
 def test_hier_and_summary_checks():
     lib = L.load()
     need = ctypes.c_size_t(0)

@@ -219,6 +219,39 @@ def test_fused_select_decode_batch(B, n_q):
             check_idx(In[b, i], Nn[b, i], ref, 4 + 512 + 2048, f"b{b} i{i}")
 
 
+@pytest.mark.parametrize("n_q,H_I", [(1, 64), (4, 64), (2, 32), (1, 128)])
+def test_fused_select_ragged_batch(n_q, H_I):
+    """A decode batch whose sequences hold different numbers of keys: every row
+    matches the oracle at its own position, and the batch equals one
+    lsa_select_topk call per sequence on that sequence's keys alone. Lengths
+    cover rows that keep every key, a length of 0 and one past the capacity
+    (both clamped)."""
+    say(f"fused select ragged n_q={n_q} H_I={H_I}")
+    n_k, d_I = 9000, 128
+    ns, W, kd = 4, 64, 500
+    K_tot = ns + W + kd
+    lens = [0, 300, K_tot, K_tot + 1, 2000, 5123, n_k, n_k + 77]
+    B = len(lens)
+    q = i8((B, n_q, H_I, d_I), -16, 15, "rgq", n_q, H_I)
+    k = i8((B, n_k, d_I), -16, 15, "rgk", n_q, H_I)
+    w = synth.int_weights(H_I, 1, 8, 13)
+    ctx = torch.tensor(lens, dtype=torch.int32, device=DEV)
+    idx, n_sel = L.lsa_select_topk_ragged(q, k, w, ctx, ns, W, kd)
+    idx2, n_sel2 = L.lsa_select_topk_ragged(q, k, w, ctx, ns, W, kd)
+    torch.cuda.synchronize()
+    assert torch.equal(idx, idx2) and torch.equal(n_sel, n_sel2)
+    In, Nn = np_(idx), np_(n_sel)
+    for b, ln in enumerate(lens):
+        Lb = min(max(ln, n_q), n_k)
+        kb = k[b:b + 1, :Lb].contiguous()
+        ref_i, ref_n = L.lsa_select_topk(q[b:b + 1].contiguous(), kb, w, ns, W, kd, q_off=Lb - n_q)
+        assert torch.equal(ref_i[0], idx[b]) and torch.equal(ref_n[0], n_sel[b]), f"b{b} len {ln}"
+        S = O.index_scores(np_(q[b]), np_(kb[0]), w, q_off=Lb - n_q)
+        for i in range(n_q):
+            ref = O.select_flat(S[i], Lb - n_q + i, ns, W, kd)
+            check_idx(In[b, i], Nn[b, i], ref, K_tot, f"b{b} i{i}")
+
+
 # ------------------------------------------------------------------ HI
 @pytest.mark.parametrize("blk", [32, 64, 128])
 def test_block_summary(blk):
