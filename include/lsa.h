@@ -119,6 +119,20 @@ int32_t lsa_select_topk_ragged(const int8_t* q_idx, const int8_t* k_idx, const i
 int32_t lsa_block_summary(const int8_t* k_idx, int32_t B, int32_t n_k, int32_t d_I,
                           int32_t blk, int8_t* k_blk, void* stream);
 
+/* HI block summaries kept current while keys are appended to a cache (same
+ * summary as lsa_block_summary; HI paragraph). k_idx [B, n_cap, d_I] holds
+ * n_new keys per sequence, of which keys n_old .. n_new-1 are new; k_blk
+ * [B, ceil(n_cap / blk), d_I] holds the summaries of the first n_old keys.
+ * Recomputes only the blocks the new keys fall in (block n_old / blk, which
+ * may have been a partial tail, up to block (n_new - 1) / blk); afterwards
+ * rows 0 .. ceil(n_new / blk) - 1 of k_blk equal lsa_block_summary of the
+ * first n_new keys. Rows past that are not touched.
+ * Requires 0 <= n_old <= n_new <= n_cap (n_old == n_new does nothing).
+ * Supported: blk in [1, 1024]; d_I in {64, 128}. */
+int32_t lsa_block_summary_append(const int8_t* k_idx, int32_t B, int32_t n_cap, int32_t n_old,
+                                 int32_t n_new, int32_t d_I, int32_t blk, int8_t* k_blk,
+                                 void* stream);
+
 /* HI decode selection for the query at position n_k - 1 (HI paragraph).
  * Coarse: blocks intersecting the candidate range are scored with the indexer
  * formula against k_blk; the n_blk_recall best (score desc, block asc) are

@@ -43,6 +43,7 @@ SIGNATURES = {
     "lsa_select_topk": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, SelectCfg, _P, _P, _P, _Z, _ZP, _P]),
     "lsa_select_topk_ragged": (_I, [_P, _P, _P, _I, _I, _I, _I, _I, _P, SelectCfg, _P, _P, _P, _Z, _ZP, _P]),
     "lsa_block_summary": (_I, [_P, _I, _I, _I, _I, _P, _P]),
+    "lsa_block_summary_append": (_I, [_P, _I, _I, _I, _I, _I, _I, _P, _P]),
     "lsa_hier_select": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, SelectCfg, _P, _P, _P, _Z, _ZP, _P]),
     "lsa_sparse_attn_prefill": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _P, _P, _P]),
     "lsa_sparse_attn_decode": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _F, _P, _P, _P, _Z, _ZP, _P]),
@@ -206,6 +207,20 @@ def lsa_block_summary(k_idx, blk):
     out = torch.empty((B, nb, d_I), dtype=torch.int8, device=k_idx.device)
     _check("lsa_block_summary", lib.lsa_block_summary(_ptr(k_idx), B, n_k, d_I, blk, _ptr(out), _stream()))
     return out
+
+
+def lsa_block_summary_append(k_cache, k_blk, n_old, n_new, blk):
+    """Update k_blk [B, ceil(n_cap/blk), d_I] in place after keys n_old..n_new-1
+    were written to k_cache [B, n_cap, d_I]. Returns k_blk."""
+    lib = load()
+    _dev(k_cache, torch.int8, "k_cache")
+    _dev(k_blk, torch.int8, "k_blk")
+    B, n_cap, d_I = k_cache.shape
+    if k_blk.shape != (B, -(-n_cap // blk), d_I):
+        raise ValueError("k_blk shape mismatch")
+    _check("lsa_block_summary_append", lib.lsa_block_summary_append(_ptr(k_cache), B, n_cap, int(n_old), int(n_new),
+                                                                    d_I, blk, _ptr(k_blk), _stream()))
+    return k_blk
 
 
 def lsa_hier_select(q_idx, k_idx, k_blk, w, blk, n_blk_recall, n_sink, n_window, k_dyn):

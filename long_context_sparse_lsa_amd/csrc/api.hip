@@ -296,7 +296,20 @@ extern "C" int32_t lsa_block_summary(const int8_t* k_idx, int32_t B, int32_t n_k
   if (!al16(k_idx) || !al16(k_blk)) return LSA_INVALID_ARG;
   if (B <= 0 || n_k <= 0 || blk <= 0) return LSA_INVALID_ARG;
   if (!di_ok(d_I) || blk > 1024) return LSA_UNSUPPORTED;
-  return hip_status(launch_block_summary(k_idx, B, n_k, d_I, blk, k_blk, (hipStream_t)stream));
+  const int nb = (int)(((int64_t)n_k + blk - 1) / blk);
+  return hip_status(launch_block_summary(k_idx, B, n_k, n_k, d_I, blk, 0, nb, k_blk, (hipStream_t)stream));
+}
+
+extern "C" int32_t lsa_block_summary_append(const int8_t* k_idx, int32_t B, int32_t n_cap, int32_t n_old,
+                                            int32_t n_new, int32_t d_I, int32_t blk, int8_t* k_blk,
+                                            void* stream) {
+  if (!al16(k_idx) || !al16(k_blk)) return LSA_INVALID_ARG;
+  if (B <= 0 || n_cap <= 0 || blk <= 0 || n_old < 0 || n_old > n_new || n_new > n_cap) return LSA_INVALID_ARG;
+  if (!di_ok(d_I) || blk > 1024) return LSA_UNSUPPORTED;
+  if (n_new == n_old) return LSA_OK;
+  const int j0 = n_old / blk, j1 = (n_new - 1) / blk;  // blocks holding the new keys
+  return hip_status(launch_block_summary(k_idx, B, n_cap, n_new, d_I, blk, j0, j1 - j0 + 1, k_blk,
+                                         (hipStream_t)stream));
 }
 
 extern "C" int32_t lsa_hier_select(const int8_t* q_idx, const int8_t* k_idx, const int8_t* k_blk,

@@ -127,9 +127,10 @@ struct DecodeArgs {
 size_t decode_ws_bytes(int B, int n_q, int H, int n_split);
 hipError_t launch_attn_decode(const DecodeArgs& a, hipStream_t st);
 
-// HI block summary launch.
-hipError_t launch_block_summary(const int8_t* k, int B, int n_k, int d_I, int blk, int8_t* kb,
-                                hipStream_t st);
+// HI block summary launch: blocks [j0, j0 + nbj) of k [B, n_cap, d_I] with
+// n_len keys present, into kb [B, ceil(n_cap / blk), d_I].
+hipError_t launch_block_summary(const int8_t* k, int B, int n_cap, int n_len, int d_I, int blk, int j0,
+                                int nbj, int8_t* kb, hipStream_t st);
 
 // Brackets one kernel launch with HIP events on its stream while kernel
 // timing (lsa_kernel_timing) is on; name is the kernel's base name.

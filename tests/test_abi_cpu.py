@@ -138,6 +138,13 @@ def test_select_topk_ragged_checks():
 
 def test_hier_and_summary_checks():
     lib = L.load()
+    # appending to a cache: order and bounds of the key counts
+    f = P(FAKE)
+    assert lib.lsa_block_summary_append(f, 1, 1000, 10, 5, 128, 64, f, None) == L.LSA_INVALID_ARG
+    assert lib.lsa_block_summary_append(f, 1, 1000, 10, 1001, 128, 64, f, None) == L.LSA_INVALID_ARG
+    assert lib.lsa_block_summary_append(f, 1, 1000, -1, 5, 128, 64, f, None) == L.LSA_INVALID_ARG
+    assert lib.lsa_block_summary_append(f, 1, 1000, 10, 20, 100, 64, f, None) == L.LSA_UNSUPPORTED
+    assert lib.lsa_block_summary_append(f, 1, 1000, 10, 10, 128, 64, f, None) == L.LSA_OK  # nothing new
     need = ctypes.c_size_t(0)
     cfg = L.SelectCfg(4, 512, 2048)
     w, wp = _w([1] * 64)

@@ -266,6 +266,29 @@ def test_block_summary(blk):
         assert torch.all(L.lsa_block_summary(k, 64) == v)
 
 
+@pytest.mark.parametrize("blk", [64, 96])
+def test_block_summary_append(blk):
+    """Summaries kept current while keys are appended: after every append the
+    summaries of the keys so far equal the oracle's (partial tail blocks use
+    their own count) and a full lsa_block_summary of those keys; rows past the
+    last block are untouched."""
+    say(f"block summary append blk={blk}")
+    B, n_cap, d_I = 3, 1000, 128
+    k = i8((B, n_cap, d_I), -128, 127, "bsa", blk)
+    nbr = -(-n_cap // blk)
+    kb = torch.full((B, nbr, d_I), 77, dtype=torch.int8, device=DEV)
+    n = 0
+    for n_new in (1, 5, blk - 1, blk, blk + 1, 3 * blk, 3 * blk, 3 * blk + 7, 999, 1000):
+        L.lsa_block_summary_append(k, kb, n, n_new, blk)
+        n = n_new
+        nb = -(-n // blk)
+        full = L.lsa_block_summary(k[:, :n].contiguous(), blk)
+        assert torch.equal(kb[:, :nb], full), f"after {n} keys"
+        for b in range(B):
+            assert np.array_equal(np_(kb[b, :nb]).astype(np.int64), O.block_summary(np_(k[b, :n]), blk))
+        assert torch.all(kb[:, nb:] == 77)
+
+
 @pytest.mark.parametrize("rec,ns,W,kd", [(32, 4, 512, 300), (8, 4, 64, 1000), (1000, 4, 128, 500), (3, 0, 0, 64)])
 def test_hier_select_matches_oracle(rec, ns, W, kd):
     say(f"hier select rec={rec} ns={ns} W={W} kd={kd}")
