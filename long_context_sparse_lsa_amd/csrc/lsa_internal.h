@@ -83,14 +83,16 @@ struct SelectArgs {
   int32_t* ws_score;
   int32_t* ws_pos;
   int32_t* ws_cnt;
-  int max_chunks;  // chunks of the longest row (select_chunks)
+  int max_chunks;  // chunks of the longest row (select_plan)
   int chunk_e;     // candidates per thread of a chunk (select_plan)
+  int chunk_nt;    // threads of a stage-A workgroup (select_plan)
   int k_cap;
 };
 // Chunk geometry for rows of at most max_nc candidates keeping k_cap each:
-// the chunk count of the longest row (workspace sizing), whether the
-// stage-two input of such rows fits kSelMaxSurvivors, and a plan that sets
-// max_chunks and chunk_e together.
+// the largest chunk count a plan can pick for such rows (workspace sizing),
+// whether the stage-two input of such rows fits kSelMaxSurvivors, and a plan
+// (from max_nc, a.n_rows and a.k_cap) that sets max_chunks, chunk_e and
+// chunk_nt together.
 int select_chunks(int64_t max_nc, int k_cap);
 bool select_fits(int64_t max_nc, int k_cap);
 void select_plan(SelectArgs& a, int64_t max_nc);

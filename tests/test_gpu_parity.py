@@ -123,6 +123,28 @@ def test_select_given_scores_ties_and_chunks(cfg, n_k, hi):
             check_idx(In[b, i], Nn[b, i], ref, K_tot, f"b{b} i{i}")
 
 
+@pytest.mark.parametrize("hi", [50, 1 << 24])
+def test_select_many_long_rows_half_chunks(hi):
+    """Many rows longer than one 1024-thread chunk (enough chunks to take the
+    512-thread chunk geometry): sampled rows against the oracle, including the
+    first and last rows and rows with heavy ties."""
+    say(f"select many long rows hi={hi}")
+    n_sink, W, kd = 4, 1024, 1020
+    n_q, n_k = 720, 41000
+    g = torch.Generator(device=DEV)
+    g.manual_seed(83)
+    scores = torch.randint(0, hi, (1, n_q, n_k), dtype=torch.int32, generator=g, device=DEV)
+    q_off = n_k - n_q
+    idx, n_sel = L.lsa_select_topk(scores=scores, n_sink=n_sink, n_window=W, k_dyn=kd, q_off=q_off)
+    torch.cuda.synchronize()
+    Sn, In, Nn = np_(scores), np_(idx), np_(n_sel)
+    K_tot = n_sink + W + kd
+    rng = np.random.default_rng(7)
+    for i in sorted({0, 1, n_q - 1, *rng.integers(0, n_q, 10).tolist()}):
+        ref = O.select_flat(Sn[0, i], q_off + i, n_sink, W, kd)
+        check_idx(In[0, i], Nn[0, i], ref, K_tot, f"row {i}")
+
+
 @pytest.mark.parametrize("n_k", [20000, 70000])
 def test_select_structured_rows(n_k):
     """Structured rows: every 8th candidate scores low (or only those score
