@@ -345,6 +345,46 @@ def test_hier_planted_block():
     assert int(n_sel[0]) == 28 and np.all((fine >= 40 * blk) & (fine < 41 * blk))
 
 
+def test_hier_index_reused_by_two_layers():
+    """HI and CLI together: one HI selection per step, consumed unchanged by
+    the decode attention of two layers (independent q, K, V per layer, 4 MTP
+    rows sharing the index); the index matches the oracle and every layer's
+    output matches the oracle's attention over that index; reuse equals
+    recomputing the index for the second layer."""
+    say("hier + CLI two layers")
+    B, n_k, H_I, d_I, blk, H, n_q = 2, 12000, 64, 128, 64, 64, 4
+    ns, W, kd, rec = 4, 256, 700, 24
+    q_idx = i8((B, H_I, d_I), -16, 15, "hcq")
+    k_idx = i8((B, n_k, d_I), -16, 15, "hck")
+    w = synth.int_weights(H_I, 1, 8, 17)
+    kb = L.lsa_block_summary(k_idx, blk)
+    idx, n_sel = L.lsa_hier_select(q_idx, k_idx, kb, w, blk, rec, ns, W, kd)
+    outs = []
+    for layer in range(2):
+        q = bf((B, n_q, H, 128), "hcl", layer)
+        kc, vc = bf((B, n_k, 128), "hck", layer), bf((B, n_k, 128), "hcv", layer)
+        outs.append((L.lsa_sparse_attn_decode(q, kc, vc, idx[:, None], n_sel[:, None], n_split=8), q, kc, vc))
+    idx_re, n_sel_re = L.lsa_hier_select(q_idx, k_idx, kb, w, blk, rec, ns, W, kd)
+    q, kc, vc = outs[1][1:]
+    o_re = L.lsa_sparse_attn_decode(q, kc, vc, idx_re[:, None], n_sel_re[:, None], n_split=8)
+    torch.cuda.synchronize()
+    assert torch.equal(idx, idx_re) and torch.equal(outs[1][0], o_re)
+    In, Nn = np_(idx), np_(n_sel)
+    for b in range(B):
+        kn = np_(k_idx[b])
+        ref = O.hier_select(np_(q_idx[b]), kn, O.block_summary(kn, blk), w, blk, rec, ns, W, kd)
+        check_idx(In[b], Nn[b], ref, ns + W + kd, f"b{b}")
+    for layer, (o, q, kc, vc) in enumerate(outs):
+        qf, kf, vf, of = f64(q), f64(kc), f64(vc), f64(o)
+        err = AttnErrors(f"HI+CLI layer {layer}")
+        for b in range(B):
+            sel = In[b, : Nn[b]]
+            for r in range(n_q):
+                ref_o, _ = O.attend(qf[b, r], kf[b], vf[b], sel, 128 ** -0.5)
+                err.add(of[b, r], ref_o)
+        err.check()
+
+
 # ------------------------------------------------------------------ attention
 def random_index(B, rows, K_tot, t_of_row, n_k, seed):
     rng = np.random.default_rng(seed)
