@@ -419,6 +419,59 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(PrefillArgs a) {
   }
 }
 
+// Length of the longest run of consecutive positions that ends a row's list,
+// in whole blocks of 32: the largest T = 32 m <= n with
+// ids[n - 1] - ids[n - T] == T - 1 (the list is strictly ascending, so the T
+// entries are then exactly the positions ids[n - T] .. ids[n - 1]). Lane l
+// tests T = 32 (l + 1); the lanes that pass form a prefix. Returns the same
+// value in every lane; 0 when no block-long run ends the list.
+__device__ __forceinline__ int contiguous_tail(const int32_t* ids, int n) {
+  const int T = 32 * (lane_id() + 1);
+  bool ok = false;
+  if (T <= n) ok = ids[n - T] == ids[n - 1] - (T - 1);
+  const uint64_t m = (uint64_t)__ballot(ok);
+  return m ? 32 * (64 - __clzll((long long)m)) : 0;
+}
+
+// Keys at the consecutive cache positions [u0, u1], 32 per block, gathered
+// once by all TW waves of the workgroup into one pair of LDS buffers (the
+// rows' SI windows, which overlap almost entirely). A wave attends only to
+// the positions [lo, hi] of its own row: the others enter its block as
+// invalid keys. trips: steps, a multiple of R covering the range.
+template <int TW, int R>
+__device__ void attn_keys_range(const v8bf (&Q)[1][8], const uint16_t* K, const uint16_t* V, int u0, int u1,
+                                int lo, int hi, int trips, int n_k, float sl2, int gw, AttnState<1>& st,
+                                char* lds) {
+  static_assert(R % 2 == 0, "block parity selects the LDS buffer");
+  const int l = lane_id(), c = l & 31;
+  const int G = l >> 4, jj = l & 15;
+  const int vt_off = kVOff + (4 * (G >> 1) + (jj >> 2)) * kVRow + (16 * (G & 1) + 4 * (jj & 3)) * 2;
+  const __amdgpu_buffer_rsrc_t kr = cache_rsrc(K, n_k), vr = cache_rsrc(V, n_k);
+  auto gpos = [&](int bi) {
+    const int p = u0 + 32 * bi + c;
+    return p <= u1 ? p : -1;
+  };
+  auto rpos = [&](int bi) {
+    const int p = u0 + 32 * bi + c;
+    return p >= lo && p <= hi ? p : -1;
+  };
+  const int nblk = (u1 - u0 + 32) / 32;
+  KVStage<TW> stg[R];
+#pragma unroll
+  for (int j = 0; j < R; ++j) gather_kv<TW>(kr, vr, gpos(j), gw, stg[j]);
+  store_kv<TW>(stg[0], lds, gw);
+  for (int it = 0; it < trips; it += R) {
+#pragma unroll
+    for (int u = 0; u < R; ++u) {
+      const int bi = it + u;
+      __syncthreads();  // block bi in its buffer for all; the other buffer free
+      gather_kv<TW>(kr, vr, gpos(bi + R), gw, stg[u]);
+      if (bi < nblk) attn_block<1>(Q, lds + (u & 1) * kBlkLds, rpos(bi), n_k, sl2, vt_off, st);
+      store_kv<TW>(stg[(u + 1) % R], lds + ((u + 1) & 1) * kBlkLds, gw);
+    }
+  }
+}
+
 // Prefill with 32 heads per wave (two waves per SIMD): the TW waves of a
 // query row (H = 32 * TW) share one gather of each K/V block in LDS, and a
 // workgroup of 4 waves takes 4 / TW rows. Barriers run over the whole
@@ -442,15 +495,54 @@ __global__ __launch_bounds__(256) void attn_prefill_shared(PrefillArgs a) {
   AttnState<1> st;
   attn_init(st);
   const int n = min(max(a.n_sel[gq], 0), a.K_tot);
-  int nmax = 0;
-#pragma unroll
-  for (int r = 0; r < RW; ++r) nmax = max(nmax, min(max(a.n_sel[min(gq0 + r, rows - 1)], 0), a.K_tot));
   const uint16_t* K = a.k + (int64_t)b * a.n_k * kD;
   const uint16_t* V = a.v + (int64_t)b * a.n_k * kD;
   constexpr int kR = 2;
-  const int trips = ((nmax + 31) / 32 + kR - 1) / kR * kR;
-  attn_keys<1, TW, kR, true>(Q, true, K, V, a.idx + gq * a.K_tot, 0, n, trips, a.n_k, a.sl2, gw, st,
+  // Two rows of one sequence whose lists both end in long runs of
+  // consecutive positions (their SI windows) that nearly coincide: the runs
+  // are left out of the per-row pass and attended in a second pass over
+  // their union, gathered once for both rows. Every wave derives the same
+  // decision from both rows' lists.
+  int cut[RW], hi_r[RW], lo_r[RW];
+  int u0 = 0, u1 = -1;
+  bool share = false;
+  if constexpr (RW == 2) {
+    const int64_t g1 = min(gq0 + 1, rows - 1);
+    bool same_seq = gq0 / a.L == g1 / a.L;
+#pragma unroll
+    for (int r = 0; r < RW; ++r) {
+      const int64_t gr = min(gq0 + r, rows - 1);
+      const int nr = min(max(a.n_sel[gr], 0), a.K_tot);
+      const int32_t* ids = a.idx + gr * a.K_tot;
+      const int T = contiguous_tail(ids, nr);
+      cut[r] = nr - T;
+      hi_r[r] = T > 0 ? ids[nr - 1] : -1;
+      lo_r[r] = hi_r[r] - T + 1;
+      share = (r == 0 || share) && T >= 64;
+    }
+    if (share && same_seq) {
+      u0 = min(lo_r[0], lo_r[1]);
+      u1 = max(hi_r[0], hi_r[1]);
+      share = u1 - u0 + 1 <= max(hi_r[0] - lo_r[0], hi_r[1] - lo_r[1]) + 1 + 32;
+    } else {
+      share = false;
+    }
+  }
+  int n1 = n, n1max = 0;
+#pragma unroll
+  for (int r = 0; r < RW; ++r) {
+    const int nr = min(max(a.n_sel[min(gq0 + r, rows - 1)], 0), a.K_tot);
+    n1max = max(n1max, share ? cut[r] : nr);
+  }
+  if (share) n1 = cut[sr];
+  const int trips = ((n1max + 31) / 32 + kR - 1) / kR * kR;
+  attn_keys<1, TW, kR, true>(Q, true, K, V, a.idx + gq * a.K_tot, 0, n1, trips, a.n_k, a.sl2, gw, st,
                              lds_all + sr * 2 * kBlkLds);
+  if (share) {
+    __syncthreads();  // every wave is done with its row's buffers
+    const int trips2 = ((u1 - u0 + 32) / 32 + kR - 1) / kR * kR;
+    attn_keys_range<4, kR>(Q, K, V, u0, u1, lo_r[sr], hi_r[sr], trips2, a.n_k, a.sl2, wv, st, lds_all);
+  }
   st.l[0] += shfl_xor_f(st.l[0], 32);  // both key halves
   const int h = gw * 32 + c;
   if (!active || h >= a.H) return;

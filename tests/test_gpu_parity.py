@@ -427,6 +427,49 @@ def test_prefill_attention(H):
         assert np.abs(lf[b] - ref_l).max() < 1e-3
 
 
+@pytest.mark.parametrize("H", [64, 128])
+def test_prefill_attention_windows(H):
+    """Lists that end in runs of consecutive positions (SI windows) of many
+    lengths, where neighbouring rows' runs are shifted by one position, equal,
+    far apart, shorter than two blocks, or not a whole number of blocks; the
+    two rows of a workgroup attend a shared run once. Every row against the
+    oracle, and bit-identical repeats."""
+    say(f"prefill attention windows H={H}")
+    B, Lq, n_k, K_tot = 2, 300, 5000, 700
+    q = bf((B, Lq, H, 128), "wq", H)
+    k = bf((B, n_k, 128), "wk", H)
+    v = bf((B, n_k, 128), "wv", H)
+    rng = np.random.default_rng(H + 1)
+    idx = np.full((B, Lq, K_tot), -1, dtype=np.int32)
+    n_sel = np.zeros((B, Lq), dtype=np.int32)
+    for b in range(B):
+        for t in range(Lq):
+            kind = (t // 2) % 6
+            W = [512, 300, 96, 64, 40, 600][kind]
+            end = 3000 + t + (0 if kind != 2 else 700 * (t % 2))   # kind 2: the two rows' runs far apart
+            if kind == 5 and t % 2:
+                end -= 1                                          # equal runs in both rows
+            win = np.arange(end - W + 1, end + 1)
+            n_pre = int(rng.integers(0, K_tot - W + 1))
+            pre = np.sort(rng.choice(end - W - 1, n_pre, replace=False)) if n_pre else np.zeros(0, np.int64)
+            sel = np.concatenate([pre, win])
+            idx[b, t, : len(sel)] = sel
+            n_sel[b, t] = len(sel)
+    idx_t, ns_t = torch.from_numpy(idx).to(DEV), torch.from_numpy(n_sel).to(DEV)
+    o, lse = L.lsa_sparse_attn_prefill(q, k, v, idx_t, ns_t, want_lse=True)
+    o2, lse2 = L.lsa_sparse_attn_prefill(q, k, v, idx_t, ns_t, want_lse=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o2) and torch.equal(lse, lse2)
+    qf, kf, vf, of, lf = f64(q), f64(k), f64(v), f64(o), np_(lse)
+    for b in range(B):
+        ref_o = np.zeros((Lq, H, 128))
+        ref_l = np.zeros((Lq, H))
+        for t in range(Lq):
+            ref_o[t], ref_l[t] = O.attend(qf[b, t], kf[b], vf[b], idx[b, t, : n_sel[b, t]], 128 ** -0.5)
+        assert_attn_close(of[b], ref_o, f"o b{b}")
+        assert np.abs(lf[b] - ref_l).max() < 1e-3
+
+
 @pytest.mark.parametrize("H,n_q,n_idx,n_split", [(64, 4, 1, 8), (64, 4, 4, 3), (16, 2, 1, 5), (128, 1, 1, 1),
                                                  (64, 1, 1, 64), (32, 4, 1, 2), (32, 1, 1, 8), (128, 2, 2, 16),
                                                  (64, 3, 1, 4), (16, 8, 8, 1)])
