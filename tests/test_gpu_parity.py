@@ -123,14 +123,15 @@ def test_select_given_scores_ties_and_chunks(cfg, n_k, hi):
             check_idx(In[b, i], Nn[b, i], ref, K_tot, f"b{b} i{i}")
 
 
+@pytest.mark.parametrize("n_q,n_k", [(720, 41000), (2100, 10000)])
 @pytest.mark.parametrize("hi", [50, 1 << 24])
-def test_select_many_long_rows_half_chunks(hi):
-    """Many rows longer than one 1024-thread chunk (enough chunks to take the
-    512-thread chunk geometry): sampled rows against the oracle, including the
+def test_select_many_long_rows_half_chunks(hi, n_q, n_k):
+    """Launches with many rows that take the 512-thread chunk geometry: rows
+    longer than one 1024-thread chunk (two-stage), and rows of at most 16384
+    candidates (one chunk). Sampled rows against the oracle, including the
     first and last rows and rows with heavy ties."""
-    say(f"select many long rows hi={hi}")
+    say(f"select many long rows hi={hi} n_q={n_q} n_k={n_k}")
     n_sink, W, kd = 4, 1024, 1020
-    n_q, n_k = 720, 41000
     g = torch.Generator(device=DEV)
     g.manual_seed(83)
     scores = torch.randint(0, hi, (1, n_q, n_k), dtype=torch.int32, generator=g, device=DEV)
