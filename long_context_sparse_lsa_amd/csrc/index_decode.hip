@@ -8,9 +8,13 @@
 // With one query row per sequence the scan reads every key once and does
 // little arithmetic per byte, so it is bound by HBM streaming. Each wave owns
 // a long contiguous key range, loads its query rows (the MFMA A operand) once,
-// and streams 32-key tiles straight into registers through a ring of kDepth
-// tiles: the loads of tile t + kDepth are issued as soon as tile t has gone
-// through the MFMAs, so kDepth tiles are in flight per wave at all times.
+// and streams 32-key tiles straight into registers through a ring of DEPTH
+// tiles: the loads of tile t + DEPTH are issued as soon as tile t has gone
+// through the MFMAs, so DEPTH tiles are in flight per wave at all times.
+// Long scans use a ring of 4 (a deeper or shallower ring, or twice the
+// waves, was no faster at C3); launches whose waves get at most four tiles
+// each (the HI stages) use a ring of 2 and twice the waves, which shortens
+// their latency-bound run (C4: -2 us per launch).
 // No load is conditional: keys past the range re-read the range's last key,
 // which only touches lines already in cache. In the HI fine stage (keys
 // addressed through a block table) the wave first copies its slice of the
@@ -34,7 +38,8 @@ namespace lsa {
 namespace {
 
 constexpr int kWaves = 4;
-constexpr int kDepth = 4;          // key tiles in flight per wave
+constexpr int kDepthLong = 4;      // key tiles in flight per wave, long scans
+constexpr int kDepthShort = 2;     // and in launches of at most 4 tiles per wave
 constexpr int kMaxBlkIds = 136;    // block-table entries per wave in LDS
 constexpr int kMaxKeysPerWave = 4096;
 
@@ -71,7 +76,7 @@ __device__ __forceinline__ int query_sum(const v16i (&acc)[MB], int qi, const in
   return s;
 }
 
-template <int HI, int DI, bool FOLD>
+template <int HI, int DI, int DEPTH, bool FOLD>
 __device__ __forceinline__ void scan_keys(const ScoreArgs& a, const v4i (&A)[HI >= 64 ? HI / 32 : 2][DI / 32],
                                           const int* wl, const int* blw, int bfirst, int b, int q0, int v0,
                                           int v1) {
@@ -106,12 +111,12 @@ __device__ __forceinline__ void scan_keys(const ScoreArgs& a, const v4i (&A)[HI 
   };
 
   const int T = (v1 - v0 + 31) / 32;
-  v4i ring[kDepth][KS];
+  v4i ring[DEPTH][KS];
 #pragma unroll
-  for (int u = 0; u < kDepth; ++u) load(u, ring[u]);
-  for (int t0 = 0; t0 < T; t0 += kDepth) {
+  for (int u = 0; u < DEPTH; ++u) load(u, ring[u]);
+  for (int t0 = 0; t0 < T; t0 += DEPTH) {
 #pragma unroll
-    for (int u = 0; u < kDepth; ++u) {
+    for (int u = 0; u < DEPTH; ++u) {
       const int t = t0 + u;
       if (t < T) {
         v16i acc[MB];
@@ -128,12 +133,12 @@ __device__ __forceinline__ void scan_keys(const ScoreArgs& a, const v4i (&A)[HI 
           store(g, v, p, pair_sum32(s0, s1));
         }
       }
-      load(t + kDepth, ring[u]);
+      load(t + DEPTH, ring[u]);
     }
   }
 }
 
-template <int HI, int DI>
+template <int HI, int DI, int DEPTH>
 __global__ __launch_bounds__(64 * kWaves) void index_decode_kernel(ScoreArgs a, int kpw, int fold_ok) {
   constexpr int MB = HI >= 64 ? HI / 32 : 2;
   constexpr int NQ = 32 * MB / HI;
@@ -188,9 +193,9 @@ __global__ __launch_bounds__(64 * kWaves) void index_decode_kernel(ScoreArgs a, 
     for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
       for (int j = 0; j < KS; ++j) A[mb][j] = scale_bytes(A[mb][j], wl[(32 * mb + c) % HI]);
-    scan_keys<HI, DI, true>(a, A, wl, blw, bfirst, b, q0, v0, v1);
+    scan_keys<HI, DI, DEPTH, true>(a, A, wl, blw, bfirst, b, q0, v0, v1);
   } else {
-    scan_keys<HI, DI, false>(a, A, wl, blw, bfirst, b, q0, v0, v1);
+    scan_keys<HI, DI, DEPTH, false>(a, A, wl, blw, bfirst, b, q0, v0, v1);
   }
 }
 
@@ -201,17 +206,24 @@ hipError_t launch_t(const ScoreArgs& a, hipStream_t st) {
   const int qtiles = (a.n_q + NQ - 1) / NQ;
   // one wave per wave slot of the GPU (256 CUs x 2 waves per SIMD x 4), so
   // that every wave streams from start to end without a second round; each
-  // wave takes a multiple of 32 * kDepth keys
+  // wave takes a multiple of 32 * DEPTH keys
   const int64_t total = (int64_t)a.B * qtiles * a.n_keys;
   int64_t kpw = (total + 2047) / 2048;
-  kpw = (kpw + 32 * kDepth - 1) / (32 * kDepth) * (32 * kDepth);
-  kpw = std::min<int64_t>(std::max<int64_t>(kpw, 32 * kDepth), kMaxKeysPerWave);
+  const bool short_scan = kpw <= 32 * kDepthLong;
+  const int depth = short_scan ? kDepthShort : kDepthLong;
+  kpw = (kpw + 32 * depth - 1) / (32 * depth) * (32 * depth);
+  kpw = std::min<int64_t>(std::max<int64_t>(kpw, 32 * depth), kMaxKeysPerWave);
   const int64_t per_wg = kpw * kWaves;
   dim3 grid((unsigned)qtiles, (unsigned)((a.n_keys + per_wg - 1) / per_wg), (unsigned)a.B);
   int fold_ok = 1;
   for (int h = 0; h < a.H_I; ++h) fold_ok &= a.w.w[h] >= 0;
   KernelTimer kt("index_decode_kernel", st);
-  hipLaunchKernelGGL((index_decode_kernel<HI, DI>), grid, dim3(64 * kWaves), 0, st, a, (int)kpw, fold_ok);
+  if (short_scan)
+    hipLaunchKernelGGL((index_decode_kernel<HI, DI, kDepthShort>), grid, dim3(64 * kWaves), 0, st, a, (int)kpw,
+                       fold_ok);
+  else
+    hipLaunchKernelGGL((index_decode_kernel<HI, DI, kDepthLong>), grid, dim3(64 * kWaves), 0, st, a, (int)kpw,
+                       fold_ok);
   return hipGetLastError();
 }
 
