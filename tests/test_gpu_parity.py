@@ -428,15 +428,15 @@ def test_prefill_attention(H):
         assert np.abs(lf[b] - ref_l).max() < 1e-3
 
 
-@pytest.mark.parametrize("H", [64, 128])
-def test_prefill_attention_windows(H):
+@pytest.mark.parametrize("H,Lq", [(64, 300), (128, 300), (64, 301)])
+def test_prefill_attention_windows(H, Lq):
     """Lists that end in runs of consecutive positions (SI windows) of many
     lengths, where neighbouring rows' runs are shifted by one position, equal,
     far apart, shorter than two blocks, or not a whole number of blocks; the
     two rows of a workgroup attend a shared run once. Every row against the
     oracle, and bit-identical repeats."""
-    say(f"prefill attention windows H={H}")
-    B, Lq, n_k, K_tot = 2, 300, 5000, 700
+    say(f"prefill attention windows H={H} Lq={Lq}")
+    B, n_k, K_tot = 2, 5000, 700
     q = bf((B, Lq, H, 128), "wq", H)
     k = bf((B, n_k, 128), "wk", H)
     v = bf((B, n_k, 128), "wv", H)
@@ -456,6 +456,10 @@ def test_prefill_attention_windows(H):
             sel = np.concatenate([pre, win])
             idx[b, t, : len(sel)] = sel
             n_sel[b, t] = len(sel)
+    n_sel[0, 17] = 0                      # rows with nothing selected
+    idx[0, 17] = -1
+    n_sel[1, Lq - 1] = 0
+    idx[1, Lq - 1] = -1
     idx_t, ns_t = torch.from_numpy(idx).to(DEV), torch.from_numpy(n_sel).to(DEV)
     o, lse = L.lsa_sparse_attn_prefill(q, k, v, idx_t, ns_t, want_lse=True)
     o2, lse2 = L.lsa_sparse_attn_prefill(q, k, v, idx_t, ns_t, want_lse=True)
@@ -464,11 +468,14 @@ def test_prefill_attention_windows(H):
     qf, kf, vf, of, lf = f64(q), f64(k), f64(v), f64(o), np_(lse)
     for b in range(B):
         ref_o = np.zeros((Lq, H, 128))
-        ref_l = np.zeros((Lq, H))
+        ref_l = np.full((Lq, H), -np.inf)
         for t in range(Lq):
-            ref_o[t], ref_l[t] = O.attend(qf[b, t], kf[b], vf[b], idx[b, t, : n_sel[b, t]], 128 ** -0.5)
+            if n_sel[b, t] > 0:
+                ref_o[t], ref_l[t] = O.attend(qf[b, t], kf[b], vf[b], idx[b, t, : n_sel[b, t]], 128 ** -0.5)
         assert_attn_close(of[b], ref_o, f"o b{b}")
-        assert np.abs(lf[b] - ref_l).max() < 1e-3
+        empty = n_sel[b] == 0
+        assert np.all(np.isneginf(lf[b][empty])) and np.all(of[b][empty] == 0)
+        assert np.abs(lf[b][~empty] - ref_l[~empty]).max() < 1e-3
 
 
 @pytest.mark.parametrize("H,n_q,n_idx,n_split", [(64, 4, 1, 8), (64, 4, 4, 3), (16, 2, 1, 5), (128, 1, 1, 1),
