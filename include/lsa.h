@@ -147,6 +147,22 @@ int32_t lsa_hier_select(const int8_t* q_idx, const int8_t* k_idx, const int8_t* 
                         int32_t* n_sel, void* ws, size_t ws_bytes, size_t* ws_needed,
                         void* stream);
 
+/* MTP draft rows that also see the drafts before them (a causal variant of the
+ * index reuse across the MTP draft steps, CLI paragraph). The target row of
+ * sequence b sits at tgt_pos[b]; draft row j (1 <= j < n_q) sits at
+ * tgt_pos[b] + j, its key and value already appended to the cache. Row j's
+ * list is the target's list followed by tgt_pos[b] + 1 .. tgt_pos[b] + j;
+ * row 0's is the target's list.
+ *   idx [B, K_tot], n_sel [B]: the target's selection (positions <= tgt_pos)
+ *   tgt_pos [B] int32, DEVICE
+ *   idx_rows [B, n_q, K_tot + n_q - 1] int32 out, ascending, -1 padded;
+ *   n_sel_rows [B, n_q] int32 out (n_sel + j)
+ * Pass them to lsa_sparse_attn_decode with n_idx = n_q and K_tot + n_q - 1.
+ * Errors: LSA_INVALID_ARG for NULL/misaligned pointers or non-positive sizes. */
+int32_t lsa_mtp_row_index(const int32_t* idx, const int32_t* n_sel, int32_t B, int32_t K_tot,
+                          int32_t n_q, const int32_t* tgt_pos, int32_t* idx_rows, int32_t* n_sel_rows,
+                          void* stream);
+
 /* Sparse attention, prefill: query row t of sequence b attends over the keys
  * idx[b, t, 0 .. n_sel[b, t]-1] of its sequence (one KV head shared by H query
  * heads); softmax(scale * q.k) in fp32, output bf16. Passing the same idx to
@@ -189,7 +205,8 @@ int32_t lsa_sparse_attn_decode(const lsa_bf16* q, const lsa_bf16* k_cache,
  *     Names: "index_prefill_kernel", "index_decode_kernel",
  *     "index_score_kernel", "select_stage_a", "select_stage_b",
  *     "attn_prefill_kernel", "attn_decode_partial", "attn_decode_merge",
- *     "block_summary_kernel". An unknown name reports 0 launches.
+ *     "block_summary_kernel", "mtp_index_kernel". An unknown name reports 0
+ *     launches.
  * Errors: LSA_INVALID_ARG for NULL pointers, LSA_HIP for a failed event call.
  * Not for concurrent use from several host threads while launches run. */
 int32_t lsa_kernel_timing(int32_t on);

@@ -43,6 +43,7 @@ SIGNATURES = {
     "lsa_select_topk": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, SelectCfg, _P, _P, _P, _Z, _ZP, _P]),
     "lsa_select_topk_ragged": (_I, [_P, _P, _P, _I, _I, _I, _I, _I, _P, SelectCfg, _P, _P, _P, _Z, _ZP, _P]),
     "lsa_block_summary": (_I, [_P, _I, _I, _I, _I, _P, _P]),
+    "lsa_mtp_row_index": (_I, [_P, _P, _I, _I, _I, _P, _P, _P, _P]),
     "lsa_block_summary_append": (_I, [_P, _I, _I, _I, _I, _I, _I, _P, _P]),
     "lsa_hier_select": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, SelectCfg, _P, _P, _P, _Z, _ZP, _P]),
     "lsa_sparse_attn_prefill": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _P, _P, _P]),
@@ -196,6 +197,23 @@ def lsa_select_topk_ragged(q_idx, k_idx, w, ctx_len, n_sink=4, n_window=0, k_dyn
     _check("lsa_select_topk_ragged", lib.lsa_select_topk_ragged(*args, _ptr(idx), _ptr(n_sel), _ptr(ws),
                                                                 ws.numel(), None, _stream()))
     return idx, n_sel
+
+
+def lsa_mtp_row_index(idx, n_sel, tgt_pos, n_q):
+    """Rows of an MTP step whose drafts see the drafts before them: idx [B, K_tot],
+    n_sel [B] (the target's selection), tgt_pos [B] int32 on the device.
+    Returns (idx_rows [B, n_q, K_tot + n_q - 1], n_sel_rows [B, n_q]) for
+    lsa_sparse_attn_decode with one index per row."""
+    lib = load()
+    _dev(idx, torch.int32, "idx")
+    _dev(n_sel, torch.int32, "n_sel")
+    _dev(tgt_pos, torch.int32, "tgt_pos")
+    B, K_tot = idx.shape
+    idx_rows = torch.empty((B, n_q, K_tot + n_q - 1), dtype=torch.int32, device=idx.device)
+    n_sel_rows = torch.empty((B, n_q), dtype=torch.int32, device=idx.device)
+    _check("lsa_mtp_row_index", lib.lsa_mtp_row_index(_ptr(idx), _ptr(n_sel), B, K_tot, n_q, _ptr(tgt_pos),
+                                                      _ptr(idx_rows), _ptr(n_sel_rows), _stream()))
+    return idx_rows, n_sel_rows
 
 
 def lsa_block_summary(k_idx, blk):

@@ -291,6 +291,16 @@ extern "C" int32_t lsa_select_topk_ragged(const int8_t* q_idx, const int8_t* k_i
                       ws, (hipStream_t)stream);
 }
 
+extern "C" int32_t lsa_mtp_row_index(const int32_t* idx, const int32_t* n_sel, int32_t B, int32_t K_tot,
+                                     int32_t n_q, const int32_t* tgt_pos, int32_t* idx_rows,
+                                     int32_t* n_sel_rows, void* stream) {
+  if (!al4(idx) || !al4(n_sel) || !al4(tgt_pos) || !al4(idx_rows) || !al4(n_sel_rows)) return LSA_INVALID_ARG;
+  if (B <= 0 || K_tot <= 0 || n_q <= 0 || (int64_t)K_tot + n_q - 1 > (1 << 20)) return LSA_INVALID_ARG;
+  if (n_q > 65535) return LSA_UNSUPPORTED;
+  return hip_status(
+      launch_mtp_index(idx, n_sel, B, K_tot, n_q, tgt_pos, idx_rows, n_sel_rows, (hipStream_t)stream));
+}
+
 extern "C" int32_t lsa_block_summary(const int8_t* k_idx, int32_t B, int32_t n_k, int32_t d_I,
                                      int32_t blk, int8_t* k_blk, void* stream) {
   if (!al16(k_idx) || !al16(k_blk)) return LSA_INVALID_ARG;

@@ -134,6 +134,10 @@ hipError_t launch_attn_decode(const DecodeArgs& a, hipStream_t st);
 hipError_t launch_block_summary(const int8_t* k, int B, int n_cap, int n_len, int d_I, int blk, int j0,
                                 int nbj, int8_t* kb, hipStream_t st);
 
+// MTP draft rows' lists: the target's list plus the drafts up to each row.
+hipError_t launch_mtp_index(const int32_t* idx, const int32_t* n_sel, int B, int K_tot, int n_q,
+                            const int32_t* tgt_pos, int32_t* idx_rows, int32_t* n_sel_rows, hipStream_t st);
+
 // Brackets one kernel launch with HIP events on its stream while kernel
 // timing (lsa_kernel_timing) is on; name is the kernel's base name.
 class KernelTimer {

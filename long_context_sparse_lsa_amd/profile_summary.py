@@ -26,7 +26,7 @@ CSRC = os.path.join(PKG, "csrc")
 COPY_BYTES = 1 << 30
 KERNELS = ("index_prefill_kernel", "index_decode_kernel", "index_score_kernel", "select_stage_a",
            "select_stage_b", "attn_prefill_kernel", "attn_decode_partial", "attn_decode_merge",
-           "block_summary_kernel")
+           "block_summary_kernel", "mtp_index_kernel")
 
 
 def sources_hash():

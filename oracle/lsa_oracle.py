@@ -238,3 +238,14 @@ def decode_select(q_row, k_idx, w, n_sink, n_window, k_dyn):
     n_k = np.asarray(k_idx).shape[0]
     S = index_scores(np.asarray(q_row)[None], k_idx, w, q_off=n_k - 1)[0]
     return select_flat(S, n_k - 1, n_sink, n_window, k_dyn)
+
+
+def mtp_row_lists(sel, tgt, n_q):
+    """Per-row key lists of an MTP step whose draft rows see the drafts before
+    them (the causal variant of the index reuse across the MTP draft steps in
+    [LSA]'s CLI paragraph): the target row, at position tgt, keeps the
+    target's selection `sel` (positions <= tgt); draft row j (1 <= j < n_q),
+    at tgt + j, adds the positions tgt + 1 .. tgt + j, whose keys the drafts
+    appended to the cache."""
+    sel = np.asarray(sel, dtype=np.int64)
+    return [np.concatenate([sel, np.arange(tgt + 1, tgt + j + 1, dtype=np.int64)]) for j in range(n_q)]

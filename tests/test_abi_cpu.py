@@ -136,6 +136,16 @@ def test_select_topk_ragged_checks():
                                       P(FAKE), P(FAKE), P(FAKE), ragged_need - 256, None, None) == L.LSA_WORKSPACE
 
 
+def test_mtp_row_index_checks():
+    lib = L.load()
+    f = P(FAKE)
+    assert lib.lsa_mtp_row_index(None, f, 2, 100, 4, f, f, f, None) == L.LSA_INVALID_ARG
+    assert lib.lsa_mtp_row_index(f, f, 2, 100, 4, None, f, f, None) == L.LSA_INVALID_ARG
+    assert lib.lsa_mtp_row_index(f, f, 0, 100, 4, f, f, f, None) == L.LSA_INVALID_ARG
+    assert lib.lsa_mtp_row_index(f, f, 2, 0, 4, f, f, f, None) == L.LSA_INVALID_ARG
+    assert lib.lsa_mtp_row_index(f, f, 2, 100, 0, f, f, f, None) == L.LSA_INVALID_ARG
+
+
 def test_hier_and_summary_checks():
     lib = L.load()
     # appending to a cache: order and bounds of the key counts

@@ -386,6 +386,39 @@ def test_hier_index_reused_by_two_layers():
         err.check()
 
 
+@pytest.mark.parametrize("n_q,n_split", [(4, 8), (2, 3)])
+def test_mtp_rows_with_causal_tails(n_q, n_split):
+    """MTP step whose draft rows also see the drafts before them: the target's
+    flat selection, extended per row by lsa_mtp_row_index, equals the oracle's
+    row lists exactly; decode attention with one index per row matches the
+    oracle's attention over those lists."""
+    say(f"mtp rows n_q={n_q} n_split={n_split}")
+    B, n_k, H_I, d_I, H = 3, 6000, 64, 128, 64
+    ns, W, kd = 4, 128, 500
+    n_c = n_k + n_q - 1                      # cache with the drafts' keys appended
+    q_idx = i8((B, 1, H_I, d_I), -16, 15, "mq", n_q)
+    k_idx = i8((B, n_k, d_I), -16, 15, "mk", n_q)
+    w = synth.int_weights(H_I, 1, 8, 19)
+    idx, n_sel = L.lsa_select_topk(q_idx, k_idx, w, ns, W, kd, q_off=n_k - 1)
+    tgt = torch.full((B,), n_k - 1, dtype=torch.int32, device=DEV)
+    rows, n_rows = L.lsa_mtp_row_index(idx[:, 0].contiguous(), n_sel[:, 0].contiguous(), tgt, n_q)
+    q = bf((B, n_q, H, 128), "mtq", n_q)
+    kc, vc = bf((B, n_c, 128), "mtk", n_q), bf((B, n_c, 128), "mtv", n_q)
+    o = L.lsa_sparse_attn_decode(q, kc, vc, rows, n_rows, n_split=n_split)
+    torch.cuda.synchronize()
+    Rn, Nn, In, Sn = np_(rows), np_(n_rows), np_(idx), np_(n_sel)
+    qf, kf, vf, of = f64(q), f64(kc), f64(vc), f64(o)
+    err = AttnErrors(f"mtp rows n_q={n_q}")
+    for b in range(B):
+        ref_sel = O.decode_select(np_(q_idx[b, 0]), np_(k_idx[b]), w, ns, W, kd)
+        assert np.array_equal(In[b, 0, : Sn[b, 0]], ref_sel)
+        for j, ref in enumerate(O.mtp_row_lists(ref_sel, n_k - 1, n_q)):
+            check_idx(Rn[b, j], Nn[b, j], ref, ns + W + kd + n_q - 1, f"b{b} row {j}")
+            ref_o, _ = O.attend(qf[b, j], kf[b], vf[b], ref, 128 ** -0.5)
+            err.add(of[b, j], ref_o)
+    err.check()
+
+
 # ------------------------------------------------------------------ attention
 def random_index(B, rows, K_tot, t_of_row, n_k, seed):
     rng = np.random.default_rng(seed)

@@ -355,3 +355,21 @@ def test_bf16_bits_exact():
     x = torch.randn(1000).to(torch.bfloat16)
     bits = x.view(torch.int16).numpy().view(np.uint16)
     assert np.array_equal(O.bf16_bits_to_f64(bits), x.double().numpy())
+
+
+def test_mtp_row_lists_causal_tails():
+    """Hand case and invariants: row j ends in the j positions after the
+    target, keeps the target's list in front, stays strictly ascending, and
+    its last position is its own (tgt + j); row 0 is the target's list."""
+    rows = O.mtp_row_lists([0, 3, 9, 10], 10, 4)
+    assert [r.tolist() for r in rows] == [[0, 3, 9, 10], [0, 3, 9, 10, 11], [0, 3, 9, 10, 11, 12],
+                                          [0, 3, 9, 10, 11, 12, 13]]
+    rng = np.random.default_rng(3)
+    for _ in range(20):
+        tgt = int(rng.integers(5, 500))
+        sel = np.sort(rng.choice(tgt + 1, int(rng.integers(1, tgt + 1)), replace=False))
+        n_q = int(rng.integers(1, 6))
+        for j, r in enumerate(O.mtp_row_lists(sel, tgt, n_q)):
+            assert len(r) == len(sel) + j and np.all(np.diff(r) > 0)
+            assert np.array_equal(r[: len(sel)], sel)
+            assert j == 0 or r[-1] == tgt + j
