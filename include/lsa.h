@@ -195,6 +195,23 @@ int32_t lsa_sparse_attn_decode(const lsa_bf16* q, const lsa_bf16* k_cache,
                                int32_t n_split, float scale, lsa_bf16* o, float* lse,
                                void* ws, size_t ws_bytes, size_t* ws_needed, void* stream);
 
+/* The same split-KV decode for MTP rows with causal tails, without building
+ * per-row lists: all n_q rows of a sequence share the target's list idx
+ * (n_idx = 1), and row j (1 <= j < n_q, at position tgt_pos[b] + j)
+ * additionally attends to tgt_pos[b] + 1 .. tgt_pos[b] + j, the drafts' keys
+ * already in the cache; row 0 attends to the list alone. Equal, up to the
+ * order of float accumulation, to lsa_sparse_attn_decode over the lists of
+ * lsa_mtp_row_index. The drafts' keys join the last of the n_split parts.
+ *   idx [B, 1, K_tot], n_sel [B, 1]; tgt_pos [B] int32, DEVICE; the rest as
+ *   lsa_sparse_attn_decode (same workspace size)
+ * Supported: as lsa_sparse_attn_decode, and n_q <= 32. */
+int32_t lsa_sparse_attn_decode_mtp(const lsa_bf16* q, const lsa_bf16* k_cache,
+                                   const lsa_bf16* v_cache, const int32_t* idx,
+                                   const int32_t* n_sel, const int32_t* tgt_pos, int32_t B,
+                                   int32_t n_q, int32_t n_k, int32_t H, int32_t D, int32_t K_tot,
+                                   int32_t n_split, float scale, lsa_bf16* o, float* lse,
+                                   void* ws, size_t ws_bytes, size_t* ws_needed, void* stream);
+
 /* Kernel timing, a measurement aid (not part of the method). While on, every
  * kernel launch of the library is bracketed by two HIP events recorded on
  * the launch stream; a launch costs two event records more.

@@ -48,6 +48,8 @@ SIGNATURES = {
     "lsa_hier_select": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, SelectCfg, _P, _P, _P, _Z, _ZP, _P]),
     "lsa_sparse_attn_prefill": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _P, _P, _P]),
     "lsa_sparse_attn_decode": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _F, _P, _P, _P, _Z, _ZP, _P]),
+    "lsa_sparse_attn_decode_mtp": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F, _P, _P, _P, _Z, _ZP,
+                                        _P]),
     "lsa_kernel_timing": (_I, [_I]),
     "lsa_kernel_time": (_I, [ctypes.c_char_p, ctypes.POINTER(_F), ctypes.POINTER(_I)]),
 }
@@ -311,6 +313,37 @@ def lsa_sparse_attn_decode(q, k_cache, v_cache, idx, n_sel, n_split=8, scale=Non
     lse = torch.empty((B, n_q, H), dtype=torch.float32, device=q.device) if want_lse else None
     _check("lsa_sparse_attn_decode", lib.lsa_sparse_attn_decode(*args, _ptr(o), _ptr(lse), _ptr(ws), ws.numel(),
                                                                 None, _stream()))
+    return (o, lse) if want_lse else o
+
+
+def lsa_sparse_attn_decode_mtp(q, k_cache, v_cache, idx, n_sel, tgt_pos, n_split=8, scale=None, want_lse=False,
+                               ws=None):
+    """Decode for MTP rows with causal tails: idx [B, 1, K_tot] (the target's
+    list, shared), tgt_pos [B] int32 on the device; row j also attends to
+    tgt_pos + 1 .. tgt_pos + j. Returns o [B, n_q, H, D] (and lse)."""
+    lib = load()
+    for t, n in ((q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache")):
+        _dev(t, torch.bfloat16, n)
+    _dev(idx, torch.int32, "idx")
+    _dev(n_sel, torch.int32, "n_sel")
+    _dev(tgt_pos, torch.int32, "tgt_pos")
+    B, n_q, H, D = q.shape
+    n_k = k_cache.shape[1]
+    if idx.shape[:2] != (B, 1) or n_sel.shape != (B, 1) or tuple(tgt_pos.shape) != (B,):
+        raise ValueError("shape mismatch")
+    K_tot = idx.shape[2]
+    scale = D ** -0.5 if scale is None else float(scale)
+    need = ctypes.c_size_t(0)
+    args = (_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(idx), _ptr(n_sel), _ptr(tgt_pos), B, n_q, n_k, H, D, K_tot,
+            n_split, scale)
+    _check("lsa_sparse_attn_decode_mtp",
+           lib.lsa_sparse_attn_decode_mtp(*args, None, None, None, 0, ctypes.byref(need), None))
+    if ws is None or ws.numel() < need.value:
+        ws = _workspace(need.value, q.device)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, n_q, H), dtype=torch.float32, device=q.device) if want_lse else None
+    _check("lsa_sparse_attn_decode_mtp", lib.lsa_sparse_attn_decode_mtp(*args, _ptr(o), _ptr(lse), _ptr(ws),
+                                                                        ws.numel(), None, _stream()))
     return (o, lse) if want_lse else o
 
 

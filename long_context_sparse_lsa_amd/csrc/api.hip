@@ -482,13 +482,11 @@ extern "C" int32_t lsa_sparse_attn_prefill(const lsa_bf16* q, const lsa_bf16* k,
   return hip_status(launch_attn_prefill(a, (hipStream_t)stream));
 }
 
-extern "C" int32_t lsa_sparse_attn_decode(const lsa_bf16* q, const lsa_bf16* k_cache,
-                                          const lsa_bf16* v_cache, const int32_t* idx,
-                                          const int32_t* n_sel, int32_t n_idx, int32_t B,
-                                          int32_t n_q, int32_t n_k, int32_t H, int32_t D,
-                                          int32_t K_tot, int32_t n_split, float scale, lsa_bf16* o,
-                                          float* lse, void* ws, size_t ws_bytes, size_t* ws_needed,
-                                          void* stream) {
+static int32_t attn_decode(const lsa_bf16* q, const lsa_bf16* k_cache, const lsa_bf16* v_cache,
+                           const int32_t* idx, const int32_t* n_sel, const int32_t* tgt_pos, int32_t n_idx,
+                           int32_t B, int32_t n_q, int32_t n_k, int32_t H, int32_t D, int32_t K_tot,
+                           int32_t n_split, float scale, lsa_bf16* o, float* lse, void* ws, size_t ws_bytes,
+                           size_t* ws_needed, void* stream) {
   if (B <= 0 || n_q <= 0 || n_k <= 0 || K_tot <= 0 || !(scale > 0.f) || !isfinite(scale)) return LSA_INVALID_ARG;
   if (n_idx != 1 && n_idx != n_q) return LSA_INVALID_ARG;
   if (D != 128 || !heads_ok(H) || n_split < 1 || n_split > 64 || n_k > kMaxCacheKeys) return LSA_UNSUPPORTED;
@@ -520,5 +518,29 @@ extern "C" int32_t lsa_sparse_attn_decode(const lsa_bf16* q, const lsa_bf16* k_c
   a.ws_m = (float*)ws;
   a.ws_l = a.ws_m + rows;
   a.ws_o = (_Float16*)((char*)ws + align_up(rows * 2 * sizeof(float)));
+  a.tgt_pos = tgt_pos;
   return hip_status(launch_attn_decode(a, (hipStream_t)stream));
+}
+
+extern "C" int32_t lsa_sparse_attn_decode(const lsa_bf16* q, const lsa_bf16* k_cache,
+                                          const lsa_bf16* v_cache, const int32_t* idx,
+                                          const int32_t* n_sel, int32_t n_idx, int32_t B,
+                                          int32_t n_q, int32_t n_k, int32_t H, int32_t D,
+                                          int32_t K_tot, int32_t n_split, float scale, lsa_bf16* o,
+                                          float* lse, void* ws, size_t ws_bytes, size_t* ws_needed,
+                                          void* stream) {
+  return attn_decode(q, k_cache, v_cache, idx, n_sel, nullptr, n_idx, B, n_q, n_k, H, D, K_tot, n_split, scale, o,
+                     lse, ws, ws_bytes, ws_needed, stream);
+}
+
+extern "C" int32_t lsa_sparse_attn_decode_mtp(const lsa_bf16* q, const lsa_bf16* k_cache,
+                                              const lsa_bf16* v_cache, const int32_t* idx,
+                                              const int32_t* n_sel, const int32_t* tgt_pos, int32_t B,
+                                              int32_t n_q, int32_t n_k, int32_t H, int32_t D, int32_t K_tot,
+                                              int32_t n_split, float scale, lsa_bf16* o, float* lse, void* ws,
+                                              size_t ws_bytes, size_t* ws_needed, void* stream) {
+  if (!al4(tgt_pos)) return LSA_INVALID_ARG;
+  if (n_q > 32) return LSA_UNSUPPORTED;  // the drafts' keys fit one 32-key block
+  return attn_decode(q, k_cache, v_cache, idx, n_sel, tgt_pos, 1, B, n_q, n_k, H, D, K_tot, n_split, scale, o,
+                     lse, ws, ws_bytes, ws_needed, stream);
 }

@@ -701,6 +701,24 @@ __global__ __launch_bounds__(64 * TW * KS) void attn_decode_partial(DecodeArgs a
     attn_keys_lds<NB, TW, kR>(Q, active, K, V, posg, cnt, tr, min(Cfg::kCap, span - ch * Cfg::kCap), a.n_k, a.sl2,
                               gw, st, lds_all + sr * 2 * kBlkLds);
   }
+  if (a.tgt_pos != nullptr && split == a.n_split - 1) {
+    // MTP rows with causal tails: the last part also holds the positions
+    // tgt + 1 .. tgt + n_q - 1 (the drafts' keys); row qr sees the first qr
+    // of them. One block, gathered by the first subrange's waves.
+    const int tgt = a.tgt_pos[b];
+    const int l2 = lane_id(), G = l2 >> 4, jj = l2 & 15;
+    const int vt_off = kVOff + (4 * (G >> 1) + (jj >> 2)) * kVRow + (16 * (G & 1) + 4 * (jj & 3)) * 2;
+    const int p = c_lane() < a.n_q - 1 ? tgt + 1 + c_lane() : -1;
+    __syncthreads();  // every wave is done with its buffers
+    if (sr == 0) {
+      KVStage<TW> stg;
+      gather_kv<TW>(cache_rsrc(K, a.n_k), cache_rsrc(V, a.n_k), p, gw, stg);
+      store_kv<TW>(stg, lds_all, gw);
+    }
+    __syncthreads();
+    if (sr == 0 && active)
+      attn_block<NB>(Q, lds_all, c_lane() < qr ? p : -1, a.n_k, a.sl2, vt_off, st);
+  }
   st.l[0] += shfl_xor_f(st.l[0], 32);  // both key halves
   const int64_t rbase = ((int64_t)b * a.n_split + split) * R + (int64_t)qr * a.H;
   if constexpr (KS == 1) {

@@ -21,6 +21,7 @@ constexpr int32_t kMasked = INT32_MIN;
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
 __device__ __forceinline__ int wave_id() { return threadIdx.x >> 6; }
+__device__ __forceinline__ int c_lane() { return threadIdx.x & 31; }
 
 // 32x32x32 int8 MFMA: each lane brings 16 int8 of A (row lane%32) and of B
 // (column lane%32); lanes 0-31 and 32-63 bring two disjoint halves of the

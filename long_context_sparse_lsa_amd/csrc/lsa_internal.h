@@ -125,6 +125,7 @@ struct DecodeArgs {
   float* lse;
   float *ws_m, *ws_l;
   _Float16* ws_o;
+  const int32_t* tgt_pos;  // MTP causal tails (n_idx == 1), or null
 };
 size_t decode_ws_bytes(int B, int n_q, int H, int n_split);
 hipError_t launch_attn_decode(const DecodeArgs& a, hipStream_t st);

@@ -139,6 +139,15 @@ def test_select_topk_ragged_checks():
 def test_mtp_row_index_checks():
     lib = L.load()
     f = P(FAKE)
+    need = ctypes.c_size_t(0)
+    dargs = [f, f, f, f, f, f, 64, 4, 131072, 64, 128, 2564, 8, 0.088]
+    assert lib.lsa_sparse_attn_decode_mtp(*dargs, f, None, None, 0, ctypes.byref(need), None) == L.LSA_OK
+    bad = list(dargs)
+    bad[5] = None       # tgt_pos
+    assert lib.lsa_sparse_attn_decode_mtp(*bad, f, None, None, 0, ctypes.byref(need), None) == L.LSA_INVALID_ARG
+    bad = list(dargs)
+    bad[7] = 33         # n_q: the drafts' keys must fit one block
+    assert lib.lsa_sparse_attn_decode_mtp(*bad, f, None, None, 0, ctypes.byref(need), None) == L.LSA_UNSUPPORTED
     assert lib.lsa_mtp_row_index(None, f, 2, 100, 4, f, f, f, None) == L.LSA_INVALID_ARG
     assert lib.lsa_mtp_row_index(f, f, 2, 100, 4, None, f, f, None) == L.LSA_INVALID_ARG
     assert lib.lsa_mtp_row_index(f, f, 0, 100, 4, f, f, f, None) == L.LSA_INVALID_ARG

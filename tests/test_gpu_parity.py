@@ -405,18 +405,26 @@ def test_mtp_rows_with_causal_tails(n_q, n_split):
     q = bf((B, n_q, H, 128), "mtq", n_q)
     kc, vc = bf((B, n_c, 128), "mtk", n_q), bf((B, n_c, 128), "mtv", n_q)
     o = L.lsa_sparse_attn_decode(q, kc, vc, rows, n_rows, n_split=n_split)
+    # the same rows without per-row lists: the shared list plus each row's tail
+    o2, lse2 = L.lsa_sparse_attn_decode_mtp(q, kc, vc, idx, n_sel, tgt, n_split=n_split, want_lse=True)
+    o3, lse3 = L.lsa_sparse_attn_decode_mtp(q, kc, vc, idx, n_sel, tgt, n_split=n_split, want_lse=True)
     torch.cuda.synchronize()
+    assert torch.equal(o2, o3) and torch.equal(lse2, lse3)
     Rn, Nn, In, Sn = np_(rows), np_(n_rows), np_(idx), np_(n_sel)
-    qf, kf, vf, of = f64(q), f64(kc), f64(vc), f64(o)
+    qf, kf, vf, of, of2, lf2 = f64(q), f64(kc), f64(vc), f64(o), f64(o2), np_(lse2)
     err = AttnErrors(f"mtp rows n_q={n_q}")
+    err2 = AttnErrors(f"mtp shared list n_q={n_q}")
     for b in range(B):
         ref_sel = O.decode_select(np_(q_idx[b, 0]), np_(k_idx[b]), w, ns, W, kd)
         assert np.array_equal(In[b, 0, : Sn[b, 0]], ref_sel)
         for j, ref in enumerate(O.mtp_row_lists(ref_sel, n_k - 1, n_q)):
             check_idx(Rn[b, j], Nn[b, j], ref, ns + W + kd + n_q - 1, f"b{b} row {j}")
-            ref_o, _ = O.attend(qf[b, j], kf[b], vf[b], ref, 128 ** -0.5)
+            ref_o, ref_l = O.attend(qf[b, j], kf[b], vf[b], ref, 128 ** -0.5)
             err.add(of[b, j], ref_o)
+            err2.add(of2[b, j], ref_o)
+            assert np.abs(lf2[b, j] - ref_l).max() < 1e-3
     err.check()
+    err2.check()
 
 
 # ------------------------------------------------------------------ attention
