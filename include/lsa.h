@@ -147,6 +147,23 @@ int32_t lsa_hier_select(const int8_t* q_idx, const int8_t* k_idx, const int8_t* 
                         int32_t* n_sel, void* ws, size_t ws_bytes, size_t* ws_needed,
                         void* stream);
 
+/* HI decode selection for a ragged batch (HI paragraph; as lsa_hier_select,
+ * per sequence). Sequence b holds L_b = clamp(ctx_len[b], 1, n_k) keys of its
+ * cache and its query sits at L_b - 1; only those keys are ever candidates.
+ *   ctx_len [B] int32, DEVICE, read on the GPU
+ *   k_idx [B, n_k, d_I], n_k the cache capacity; k_blk [B, ceil(n_k / blk),
+ *   d_I] whose first ceil(L_b / blk) rows of sequence b summarize its first
+ *   L_b keys (lsa_block_summary / lsa_block_summary_append per sequence)
+ *   idx [B, K_tot] out, ascending, -1 padded; n_sel [B] out, min(L_b, K_tot)
+ *     when all candidates fit the recalled blocks
+ * The workspace is sized for full-length sequences. Errors as
+ * lsa_hier_select; ctx_len NULL or misaligned is LSA_INVALID_ARG. */
+int32_t lsa_hier_select_ragged(const int8_t* q_idx, const int8_t* k_idx, const int8_t* k_blk,
+                               const int32_t* w, int32_t B, int32_t n_k, const int32_t* ctx_len,
+                               int32_t H_I, int32_t d_I, int32_t blk, int32_t n_blk_recall,
+                               lsa_select_cfg cfg, int32_t* idx, int32_t* n_sel, void* ws,
+                               size_t ws_bytes, size_t* ws_needed, void* stream);
+
 /* MTP draft rows that also see the drafts before them (a causal variant of the
  * index reuse across the MTP draft steps, CLI paragraph). The target row of
  * sequence b sits at tgt_pos[b]; draft row j (1 <= j < n_q) sits at

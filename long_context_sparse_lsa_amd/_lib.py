@@ -46,6 +46,8 @@ SIGNATURES = {
     "lsa_mtp_row_index": (_I, [_P, _P, _I, _I, _I, _P, _P, _P, _P]),
     "lsa_block_summary_append": (_I, [_P, _I, _I, _I, _I, _I, _I, _P, _P]),
     "lsa_hier_select": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, SelectCfg, _P, _P, _P, _Z, _ZP, _P]),
+    "lsa_hier_select_ragged": (_I, [_P, _P, _P, _P, _I, _I, _P, _I, _I, _I, _I, SelectCfg, _P, _P, _P, _Z, _ZP,
+                                    _P]),
     "lsa_sparse_attn_prefill": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _P, _P, _P]),
     "lsa_sparse_attn_decode": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _F, _P, _P, _P, _Z, _ZP, _P]),
     "lsa_sparse_attn_decode_mtp": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F, _P, _P, _P, _Z, _ZP,
@@ -243,9 +245,7 @@ def lsa_block_summary_append(k_cache, k_blk, n_old, n_new, blk):
     return k_blk
 
 
-def lsa_hier_select(q_idx, k_idx, k_blk, w, blk, n_blk_recall, n_sink, n_window, k_dyn):
-    """HI decode selection for the query at n_k - 1.
-    q_idx [B, H_I, d_I] int8. Returns (idx [B, K_tot], n_sel [B])."""
+def _hier(name, q_idx, k_idx, k_blk, w, ctx_len, blk, n_blk_recall, n_sink, n_window, k_dyn):
     lib = load()
     _dev(q_idx, torch.int8, "q_idx")
     _dev(k_idx, torch.int8, "k_idx")
@@ -256,14 +256,36 @@ def lsa_hier_select(q_idx, k_idx, k_blk, w, blk, n_blk_recall, n_sink, n_window,
     cfg = SelectCfg(n_sink, n_window, k_dyn)
     K_tot = n_sink + n_window + k_dyn
     need = ctypes.c_size_t(0)
-    args = (_ptr(q_idx), _ptr(k_idx), _ptr(k_blk), wp, B, n_k, H_I, d_I, blk, n_blk_recall, cfg)
-    _check("lsa_hier_select", lib.lsa_hier_select(*args, None, None, None, 0, ctypes.byref(need), None))
+    if ctx_len is None:
+        args = (_ptr(q_idx), _ptr(k_idx), _ptr(k_blk), wp, B, n_k, H_I, d_I, blk, n_blk_recall, cfg)
+    else:
+        _dev(ctx_len, torch.int32, "ctx_len")
+        if tuple(ctx_len.shape) != (B,):
+            raise ValueError("ctx_len shape mismatch")
+        args = (_ptr(q_idx), _ptr(k_idx), _ptr(k_blk), wp, B, n_k, _ptr(ctx_len), H_I, d_I, blk, n_blk_recall,
+                cfg)
+    fn = getattr(lib, name)
+    _check(name, fn(*args, None, None, None, 0, ctypes.byref(need), None))
     ws = _workspace(need.value, q_idx.device)
     idx = torch.empty((B, K_tot), dtype=torch.int32, device=q_idx.device)
     n_sel = torch.empty((B,), dtype=torch.int32, device=q_idx.device)
-    _check("lsa_hier_select", lib.lsa_hier_select(*args, _ptr(idx), _ptr(n_sel), _ptr(ws), ws.numel(),
-                                                  None, _stream()))
+    _check(name, fn(*args, _ptr(idx), _ptr(n_sel), _ptr(ws), ws.numel(), None, _stream()))
     return idx, n_sel
+
+
+def lsa_hier_select(q_idx, k_idx, k_blk, w, blk, n_blk_recall, n_sink, n_window, k_dyn):
+    """HI decode selection for the query at n_k - 1.
+    q_idx [B, H_I, d_I] int8. Returns (idx [B, K_tot], n_sel [B])."""
+    return _hier("lsa_hier_select", q_idx, k_idx, k_blk, w, None, blk, n_blk_recall, n_sink, n_window, k_dyn)
+
+
+def lsa_hier_select_ragged(q_idx, k_idx, k_blk, w, ctx_len, blk, n_blk_recall, n_sink, n_window, k_dyn):
+    """HI decode selection for a ragged batch: sequence b holds
+    clamp(ctx_len[b], 1, n_k) keys of k_idx [B, n_k, d_I] and its query sits
+    at the last of them; k_blk holds each sequence's summaries of those keys.
+    ctx_len [B] int32 on the device. Returns (idx [B, K_tot], n_sel [B])."""
+    return _hier("lsa_hier_select_ragged", q_idx, k_idx, k_blk, w, ctx_len, blk, n_blk_recall, n_sink, n_window,
+                 k_dyn)
 
 
 def lsa_sparse_attn_prefill(q, k, v, idx, n_sel, scale=None, want_lse=False, out=None):

@@ -322,11 +322,13 @@ extern "C" int32_t lsa_block_summary_append(const int8_t* k_idx, int32_t B, int3
                                          (hipStream_t)stream));
 }
 
-extern "C" int32_t lsa_hier_select(const int8_t* q_idx, const int8_t* k_idx, const int8_t* k_blk,
-                                   const int32_t* w, int32_t B, int32_t n_k, int32_t H_I,
-                                   int32_t d_I, int32_t blk, int32_t n_blk_recall,
-                                   lsa_select_cfg cfg, int32_t* idx, int32_t* n_sel, void* ws,
-                                   size_t ws_bytes, size_t* ws_needed, void* stream) {
+// HI selection; with ctx_len set, sequence b holds clamp(ctx_len[b], 1, n_k)
+// keys and its query sits at the last of them (every range below is the
+// full-length one, narrowed per sequence on the GPU).
+static int32_t hier_select(const int8_t* q_idx, const int8_t* k_idx, const int8_t* k_blk, const int32_t* w,
+                           int32_t B, int32_t n_k, const int32_t* ctx_len, int32_t H_I, int32_t d_I, int32_t blk,
+                           int32_t n_blk_recall, lsa_select_cfg cfg, int32_t* idx, int32_t* n_sel, void* ws,
+                           size_t ws_bytes, size_t* ws_needed, void* stream) {
   int32_t s = cfg_ok(cfg);
   if (s != LSA_OK) return s;
   if (B <= 0 || n_k <= 0 || blk <= 0 || n_blk_recall <= 0) return LSA_INVALID_ARG;
@@ -359,6 +361,7 @@ extern "C" int32_t lsa_hier_select(const int8_t* q_idx, const int8_t* k_idx, con
   if (s != LSA_OK) return s;
   if (ws_bytes < need) return LSA_WORKSPACE;
   hipStream_t st = (hipStream_t)stream;
+  const SeqShift shift{ctx_len, 1, n_k};
 
   if (trivial) {
     SelectArgs sa{};
@@ -366,6 +369,7 @@ extern "C" int32_t lsa_hier_select(const int8_t* q_idx, const int8_t* k_idx, con
     sa.n_rows = B;
     sa.n_q = 1;
     sa.q_off = t;
+    sa.shift = shift;
     sa.n_sink = cfg.n_sink;
     sa.n_window = cfg.n_window;
     sa.k_dyn = cfg.k_dyn;
@@ -420,6 +424,9 @@ extern "C" int32_t lsa_hier_select(const int8_t* q_idx, const int8_t* k_idx, con
   sc.raw_lo = b_lo;
   sc.raw_hi = b_hi;
   sc.raw_k = n_blk_recall;
+  sc.raw_hi_pos = hi;
+  sc.raw_div = blk;
+  sc.shift = shift;
   sc.idx = blocks;
   sc.n_sel = nblk;
   sc.out_ld = n_blk_recall;
@@ -444,6 +451,7 @@ extern "C" int32_t lsa_hier_select(const int8_t* q_idx, const int8_t* k_idx, con
   f.nbr = n_blk_recall;
   f.fill_masked = 1;
   f.scores = fine;
+  f.shift = shift;
   s = hip_status(launch_index_score(f, st));
   if (s != LSA_OK) return s;
 
@@ -460,6 +468,7 @@ extern "C" int32_t lsa_hier_select(const int8_t* q_idx, const int8_t* k_idx, con
   sf.nbr = n_blk_recall;
   sf.n_virt = n_virt;
   sf.t_fixed = t;
+  sf.shift = shift;
   sf.idx = idx;
   sf.n_sel = n_sel;
   sf.out_ld = K_tot;
@@ -467,6 +476,25 @@ extern "C" int32_t lsa_hier_select(const int8_t* q_idx, const int8_t* k_idx, con
   select_plan(sf, n_virt);
   select_bind_ws(sf, sel_ws, B);
   return hip_status(launch_select(sf, st));
+}
+
+extern "C" int32_t lsa_hier_select(const int8_t* q_idx, const int8_t* k_idx, const int8_t* k_blk,
+                                   const int32_t* w, int32_t B, int32_t n_k, int32_t H_I,
+                                   int32_t d_I, int32_t blk, int32_t n_blk_recall,
+                                   lsa_select_cfg cfg, int32_t* idx, int32_t* n_sel, void* ws,
+                                   size_t ws_bytes, size_t* ws_needed, void* stream) {
+  return hier_select(q_idx, k_idx, k_blk, w, B, n_k, nullptr, H_I, d_I, blk, n_blk_recall, cfg, idx, n_sel, ws,
+                     ws_bytes, ws_needed, stream);
+}
+
+extern "C" int32_t lsa_hier_select_ragged(const int8_t* q_idx, const int8_t* k_idx, const int8_t* k_blk,
+                                          const int32_t* w, int32_t B, int32_t n_k, const int32_t* ctx_len,
+                                          int32_t H_I, int32_t d_I, int32_t blk, int32_t n_blk_recall,
+                                          lsa_select_cfg cfg, int32_t* idx, int32_t* n_sel, void* ws,
+                                          size_t ws_bytes, size_t* ws_needed, void* stream) {
+  if (!al4(ctx_len)) return LSA_INVALID_ARG;
+  return hier_select(q_idx, k_idx, k_blk, w, B, n_k, ctx_len, H_I, d_I, blk, n_blk_recall, cfg, idx, n_sel, ws,
+                     ws_bytes, ws_needed, stream);
 }
 
 extern "C" int32_t lsa_sparse_attn_prefill(const lsa_bf16* q, const lsa_bf16* k, const lsa_bf16* v,

@@ -67,11 +67,15 @@ struct SelectArgs {
   // (row0 offsets the row count when a launch covers a slice of the rows.)
   int n_q, q_off, row0, n_sink, n_window, k_dyn;
   // RAW: candidates [raw_lo, raw_hi] (virtual == position), keep raw_k.
-  int raw_lo, raw_hi, raw_k;
+  // With shift.ctx_len set, row r (sequence row0 + r) stops at
+  // min(raw_hi, floor((raw_hi_pos + its shift) / raw_div)) instead.
+  int raw_lo, raw_hi, raw_k, raw_hi_pos, raw_div;
   SeqShift shift;
   // INDIRECT: candidates are virtual keys [0, n_virt) of row r, at positions
   // blocks[r * nbr + v / blk] * blk + v % blk, valid iff score != INT32_MIN;
-  // the query sits at t_fixed; keep k_dyn; sinks and window as in FLAT.
+  // the query sits at t_fixed (+ the shift of sequence row0 + r, whose row
+  // keeps every position 0 .. t when t + 1 <= K_tot); keep k_dyn; sinks and
+  // window as in FLAT.
   const int32_t* blocks;
   int blk, nbr, n_virt, t_fixed;
   // outputs: FLAT / INDIRECT write the assembled list (sinks, top-k, window),

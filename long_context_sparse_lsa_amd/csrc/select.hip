@@ -68,14 +68,23 @@ __device__ __forceinline__ RowGeom row_geom(const SelectArgs& a, int r) {
     gm.nc = t - a.n_window - a.n_sink + 1;
     gm.k = a.k_dyn;
   } else if (a.mode == SEL_RAW) {
+    int hi = a.raw_hi;
+    if (a.shift.ctx_len != nullptr) {
+      const int hp = a.raw_hi_pos + seq_shift(a.shift, a.row0 + r);
+      hi = min(hp >= 0 ? hp / a.raw_div : -1, a.raw_hi);
+    }
     gm.c_lo = a.raw_lo;
-    gm.nc = max(0, a.raw_hi - a.raw_lo + 1);
+    gm.nc = max(0, hi - a.raw_lo + 1);
     gm.k = a.raw_k;
   } else {
     gm.t = a.t_fixed;
     gm.c_lo = 0;
     gm.nc = a.n_virt;
     gm.k = a.k_dyn;
+    if (a.shift.ctx_len != nullptr) {
+      gm.t += seq_shift(a.shift, a.row0 + r);
+      gm.trivial = gm.t + 1 <= a.n_sink + a.n_window + a.k_dyn;
+    }
   }
   return gm;
 }

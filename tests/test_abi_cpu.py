@@ -136,6 +136,28 @@ def test_select_topk_ragged_checks():
                                       P(FAKE), P(FAKE), P(FAKE), ragged_need - 256, None, None) == L.LSA_WORKSPACE
 
 
+def test_hier_select_ragged_checks():
+    lib = L.load()
+    need = ctypes.c_size_t(0)
+    cfg = L.SelectCfg(4, 512, 2048)
+    w, wp = _w([1] * 64)
+    f = P(FAKE)
+    # sized for full-length sequences: the same workspace as the uniform call
+    assert lib.lsa_hier_select(f, f, f, wp, 4, 1 << 20, 64, 128, 64, 256, cfg,
+                               None, None, None, 0, ctypes.byref(need), None) == L.LSA_OK
+    uniform_need = need.value
+    assert lib.lsa_hier_select_ragged(f, f, f, wp, 4, 1 << 20, f, 64, 128, 64, 256, cfg,
+                                      None, None, None, 0, ctypes.byref(need), None) == L.LSA_OK
+    assert need.value == uniform_need > 0
+    # the length array is required; block size and workspace checks as the uniform call
+    assert lib.lsa_hier_select_ragged(f, f, f, wp, 4, 1 << 20, None, 64, 128, 64, 256, cfg,
+                                      None, None, None, 0, ctypes.byref(need), None) == L.LSA_INVALID_ARG
+    assert lib.lsa_hier_select_ragged(f, f, f, wp, 4, 1 << 20, f, 64, 128, 48, 256, cfg,
+                                      None, None, None, 0, ctypes.byref(need), None) == L.LSA_UNSUPPORTED
+    assert lib.lsa_hier_select_ragged(f, f, f, wp, 4, 1 << 20, f, 64, 128, 64, 256, cfg,
+                                      f, f, f, uniform_need - 256, None, None) == L.LSA_WORKSPACE
+
+
 def test_mtp_row_index_checks():
     lib = L.load()
     f = P(FAKE)

@@ -334,6 +334,45 @@ def test_hier_select_matches_oracle(rec, ns, W, kd):
         assert torch.equal(flat[:, 0], idx) and torch.equal(nf[:, 0], n_sel)
 
 
+@pytest.mark.parametrize("rec", [6, 24])
+def test_hier_select_ragged_batch(rec):
+    """HI selection for a ragged batch: every sequence matches the oracle's HI
+    selection on its own keys (query at its last key, summaries of those keys),
+    and equals lsa_hier_select run on that sequence alone. Summary rows past a
+    sequence's keys hold noise, which must not be read. Lengths cover sequences
+    that keep every key, a length of 0 and one past the capacity (both
+    clamped), and a partial last block; rec = 6 recalls fewer candidates than
+    k_dyn, so lists come out short."""
+    say(f"hier select ragged rec={rec}")
+    n_k, d_I, H_I, blk = 12000, 128, 64, 64
+    ns, W, kd = 4, 64, 500
+    K_tot = ns + W + kd
+    lens = [0, 300, K_tot, K_tot + 1, 2000, blk * 60 + 17, n_k, n_k + 77]
+    B = len(lens)
+    q = i8((B, H_I, d_I), -16, 15, "hrq", rec)
+    k = i8((B, n_k, d_I), -16, 15, "hrk", rec)
+    w = synth.int_weights(H_I, 1, 8, 21)
+    nbk = (n_k + blk - 1) // blk
+    kb = i8((B, nbk, d_I), -128, 127, "hrn", rec)
+    Ls = [min(max(ln, 1), n_k) for ln in lens]
+    for b, Lb in enumerate(Ls):
+        kb[b, :(Lb + blk - 1) // blk] = L.lsa_block_summary(k[b:b + 1, :Lb].contiguous(), blk)[0]
+    ctx = torch.tensor(lens, dtype=torch.int32, device=DEV)
+    idx, n_sel = L.lsa_hier_select_ragged(q, k, kb, w, ctx, blk, rec, ns, W, kd)
+    idx2, n_sel2 = L.lsa_hier_select_ragged(q, k, kb, w, ctx, blk, rec, ns, W, kd)
+    torch.cuda.synchronize()
+    assert torch.equal(idx, idx2) and torch.equal(n_sel, n_sel2)
+    In, Nn = np_(idx), np_(n_sel)
+    for b, Lb in enumerate(Ls):
+        kn = np_(k[b, :Lb])
+        ref = O.hier_select(np_(q[b]), kn, O.block_summary(kn, blk), w, blk, rec, ns, W, kd)
+        check_idx(In[b], Nn[b], ref, K_tot, f"b{b} len {lens[b]}")
+        kbb = kb[b:b + 1, :(Lb + blk - 1) // blk].contiguous()
+        one, n_one = L.lsa_hier_select(q[b:b + 1].contiguous(), k[b:b + 1, :Lb].contiguous(), kbb, w, blk, rec,
+                                       ns, W, kd)
+        assert torch.equal(one[0], idx[b]) and torch.equal(n_one[0], n_sel[b]), f"b{b} len {lens[b]}"
+
+
 def test_hier_planted_block():
     say("hier planted block")
     n_k, blk = 8192, 64
