@@ -242,6 +242,88 @@ def test_hier_planted_block_recalled_first():
     assert len(fine) == blk and fine.tolist() == list(range(10 * blk, 11 * blk))
 
 
+def _py_score(q_row, key, w):
+    """One indexer score in Python ints (brute force)."""
+    return sum(int(wh) * max(0, sum(int(a) * int(b) for a, b in zip(qh, key))) for wh, qh in zip(w, q_row))
+
+
+def _hier_brute(q, k, kbar, w, blk, rec, n_sink, W, kd):
+    """HI selection by enumeration: the blocks that hold at least one
+    candidate position n_sink..t-W, ranked by a full sort on (-score, block);
+    the candidates of the recalled blocks ranked by (-score, position)."""
+    t = len(k) - 1
+    if t + 1 <= n_sink + W + kd:
+        return list(range(t + 1))
+    cand = set(range(n_sink, t - W + 1))
+    elig = sorted({s // blk for s in cand})
+    ranked = sorted(elig, key=lambda b: (-_py_score(q, kbar[b], w), b))
+    recalled = set(ranked[:rec])
+    fine = [s for s in sorted(cand) if s // blk in recalled]
+    fine = sorted(sorted(fine, key=lambda s: (-_py_score(q, k[s], w), s))[:kd])
+    return list(range(n_sink)) + fine + list(range(t - W + 1, t + 1))
+
+
+def test_hier_window_only_blocks_never_recalled():
+    # W >= 2 * blk, so the last blocks hold window positions only; the block
+    # with the best summary score is one of them and must not take a recall
+    # slot (R12: only blocks that meet the candidate range compete)
+    rng = np.random.default_rng(13)
+    blk, d, n_sink = 16, 8, 4
+    for trial in range(4):
+        W = int(rng.integers(2 * blk, 4 * blk))
+        n = int(rng.integers(12 * blk, 20 * blk))
+        k = rng.integers(-3, 4, (n, d))
+        q = rng.integers(1, 4, (2, d))
+        t = n - 1
+        wo = (t - W) // blk + 1 + int(rng.integers(0, (t // blk) - (t - W) // blk))  # a window-only block
+        assert wo * blk > t - W and wo <= t // blk
+        k[wo * blk: min(n, (wo + 1) * blk)] = 12     # aligned with q: highest summary score
+        k[3 * blk: 4 * blk] = 6                      # a candidate block, second highest
+        kbar = O.block_summary(k, blk)
+        w = [1, 2]
+        for rec, kd in ((1, 5), (1, 40), (3, 20)):
+            got = O.hier_select(q, k, kbar, w, blk, rec, n_sink, W, kd)
+            ref = _hier_brute(q, k, kbar, w, blk, rec, n_sink, W, kd)
+            assert got.tolist() == ref, (trial, rec, kd)
+            fine = got[n_sink: len(got) - W]
+            assert len(fine) == min(kd, rec * blk) and np.all((fine >= n_sink) & (fine <= t - W))
+            if rec == 1:   # the one recalled block is the candidate block 3
+                assert np.all(fine // blk == 3)
+
+
+def test_hier_random_against_enumeration():
+    rng = np.random.default_rng(14)
+    for trial in range(8):
+        blk = int(rng.choice([8, 16]))
+        n_sink, W, kd = int(rng.integers(0, 6)), int(rng.integers(0, 3 * blk)), int(rng.integers(1, 30))
+        n = int(rng.integers(n_sink + W + kd + 2, 300))
+        k = rng.integers(-8, 8, (n, 6))
+        q = rng.integers(-8, 8, (3, 6))
+        w = rng.integers(1, 5, 3)
+        kbar = O.block_summary(k, blk)
+        rec = int(rng.integers(1, 6))
+        got = O.hier_select(q, k, kbar, w, blk, rec, n_sink, W, kd)
+        assert got.tolist() == _hier_brute(q, k, kbar, w, blk, rec, n_sink, W, kd), trial
+
+
+def test_hier_short_context_keeps_every_key():
+    # t + 1 <= K_tot: every position 0..t, whatever the scores (R7); one more
+    # key than K_tot selects again
+    rng = np.random.default_rng(15)
+    n_sink, W, kd, blk = 4, 20, 12, 8
+    K_tot = n_sink + W + kd
+    for n in (1, 2, 17, K_tot - 1, K_tot):
+        k = rng.integers(-8, 8, (n, 6))
+        q = rng.integers(-8, 8, (2, 6))
+        got = O.hier_select(q, k, O.block_summary(k, blk), [1, 3], blk, 1, n_sink, W, kd)
+        assert got.tolist() == list(range(n))
+    k = rng.integers(-8, 8, (K_tot + 1, 6))
+    q = rng.integers(-8, 8, (2, 6))
+    got = O.hier_select(q, k, O.block_summary(k, blk), [1, 3], blk, 1, n_sink, W, kd)
+    assert len(got) < K_tot + 1
+    assert got.tolist() == _hier_brute(q, k, O.block_summary(k, blk), [1, 3], blk, 1, n_sink, W, kd)
+
+
 # ----------------------------------------------------------------------------- O6
 def _bf16_round(x):
     return torch.tensor(x, dtype=torch.float32).to(torch.bfloat16).double().numpy()
