@@ -249,3 +249,80 @@ def mtp_row_lists(sel, tgt, n_q):
     appended to the cache."""
     sel = np.asarray(sel, dtype=np.int64)
     return [np.concatenate([sel, np.arange(tgt + 1, tgt + j + 1, dtype=np.int64)]) for j in range(n_q)]
+
+
+# ----------------------------------------------------------------------------
+# Sparse attention backward (the deterministic attention operators of the
+# training write-ups: "如何在 5 万张国产芯片训练出 1.6T 万亿参数模型？", section
+# "④ 痛点③", which pairs the LSA operator with deterministic attention; the
+# haoling.cc article, section 三, on a deterministic attention backward)
+# ----------------------------------------------------------------------------
+def attend_backward(q_rows, k, v, sel, scale, do_rows):
+    """Gradients of the loss sum(dO * o) for query rows attending over one
+    selected key set (the chain rule through o = softmax(scale q k^T) v).
+
+    q_rows, do_rows: [R, D]; k, v: [N, D]; sel: selected positions (unique).
+    Returns dq [R, D] and the gradients of the selected rows of k and v,
+    dk_sel, dv_sel [len(sel), D] (rows in the order of `sel`).
+    """
+    Ks = k[sel]
+    Vs = v[sel]
+    z = (q_rows @ Ks.T) * scale
+    p = np.exp(z - z.max(axis=1, keepdims=True))
+    p = p / p.sum(axis=1, keepdims=True)          # softmax over the selected keys
+    o = p @ Vs
+    dp = do_rows @ Vs.T                            # d loss / d p
+    delta = (do_rows * o).sum(axis=1, keepdims=True)
+    ds = p * (dp - delta)                          # d loss / d z (softmax Jacobian)
+    dq = (ds @ Ks) * scale
+    dk_sel = (ds.T @ q_rows) * scale
+    dv_sel = p.T @ do_rows
+    return dq, dk_sel, dv_sel
+
+
+def sparse_attn_backward(q, k, v, lists, scale, do):
+    """Backward of sparse prefill attention over one sequence.
+
+    q, do: [L, H, D]; k, v: [N, D] (one KV head shared by the H heads);
+    lists[t]: the positions row t attends to (unique). Every head of row t
+    uses row t's list. Returns dq [L, H, D], dk [N, D], dv [N, D]: a key's
+    gradient is the sum of the contributions of every row that selected it.
+    """
+    L = q.shape[0]
+    dq = np.zeros_like(q, dtype=np.float64)
+    dk = np.zeros(k.shape, dtype=np.float64)
+    dv = np.zeros(v.shape, dtype=np.float64)
+    for t in range(L):
+        sel = np.asarray(lists[t], dtype=np.int64)
+        if len(sel) == 0:
+            continue
+        dq[t], dks, dvs = attend_backward(q[t], k, v, sel, scale, do[t])
+        dk[sel] += dks
+        dv[sel] += dvs
+    return dq, dk, dv
+
+
+# ----------------------------------------------------------------------------
+# LSA warm-up KL operator ([LSA training] release article, section
+# "长上下文训练 — LSA 算子与前向优化": a KL loss operator that gives loss and
+# gradient from one forward pass)
+# ----------------------------------------------------------------------------
+def kl_warmup_row(q_row, k, sel, scale, logits):
+    """KL(p || softmax(logits)) over one row's key list and its gradient.
+
+    q_row: [H, D] attention queries of the row; k: [N, D]; sel: the row's key
+    positions; logits: [len(sel)] indexer logits of those keys. The target p
+    is the attention distribution averaged over the H heads,
+    p_s = (1/H) sum_h softmax_s(scale q_h . k_s). Returns (KL, d KL / d logits),
+    the gradient being softmax(logits) - p.
+    """
+    z = (q_row @ k[sel].T) * scale                          # [H, n]
+    a = np.exp(z - z.max(axis=1, keepdims=True))
+    a = a / a.sum(axis=1, keepdims=True)
+    p = a.mean(axis=0)
+    lg = np.asarray(logits, dtype=np.float64)
+    log_q = lg - (lg.max() + np.log(np.exp(lg - lg.max()).sum()))
+    qd = np.exp(log_q)
+    nz = p > 0
+    kl = float(np.sum(p[nz] * (np.log(p[nz]) - log_q[nz])))
+    return kl, qd - p

@@ -455,3 +455,149 @@ def test_mtp_row_lists_causal_tails():
             assert len(r) == len(sel) + j and np.all(np.diff(r) > 0)
             assert np.array_equal(r[: len(sel)], sel)
             assert j == 0 or r[-1] == tgt + j
+
+
+# ----------------------------------------------------------------------------- backward
+def _loss(q, k, v, lists, scale, do):
+    """sum(dO * o) through the oracle's forward (itself pinned to SDPA)."""
+    tot = 0.0
+    for t, sel in enumerate(lists):
+        o, _ = O.attend(q[t], k, v, np.asarray(sel), scale)
+        tot += float((do[t] * o).sum())
+    return tot
+
+
+def _rand_lists(rng, L, N, max_len):
+    return [np.sort(rng.choice(N, int(rng.integers(1, max_len + 1)), replace=False)) for _ in range(L)]
+
+
+def test_backward_matches_finite_differences():
+    rng = np.random.default_rng(21)
+    L, H, D, N, scale = 5, 2, 4, 7, 0.7
+    q, do = rng.standard_normal((L, H, D)), rng.standard_normal((L, H, D))
+    k, v = rng.standard_normal((N, D)), rng.standard_normal((N, D))
+    lists = _rand_lists(rng, L, N, 5)
+    dq, dk, dv = O.sparse_attn_backward(q, k, v, lists, scale, do)
+    eps = 1e-6
+    for name, x, g in (("q", q, dq), ("k", k, dk), ("v", v, dv)):
+        num = np.zeros_like(x)
+        for ix in np.ndindex(x.shape):
+            x0 = x[ix]
+            x[ix] = x0 + eps
+            up = _loss(q, k, v, lists, scale, do)
+            x[ix] = x0 - eps
+            dn = _loss(q, k, v, lists, scale, do)
+            x[ix] = x0
+            num[ix] = (up - dn) / (2 * eps)
+        assert np.abs(num - g).max() < 1e-7 * max(1.0, np.abs(g).max()), name
+
+
+def _torch_grads(q, k, v, mask, scale, do):
+    """float64 autograd of torch SDPA with a boolean keep-mask [L, N]; the one
+    KV head is expanded over the query heads, so its gradients sum over them."""
+    qt = torch.tensor(q.transpose(1, 0, 2), requires_grad=True)        # [H, L, D]
+    kt = torch.tensor(k, requires_grad=True)
+    vt = torch.tensor(v, requires_grad=True)
+    H = q.shape[1]
+    o = torch.nn.functional.scaled_dot_product_attention(
+        qt, kt.expand(H, -1, -1), vt.expand(H, -1, -1), attn_mask=torch.tensor(mask), scale=scale)
+    o.backward(torch.tensor(do.transpose(1, 0, 2)))
+    return qt.grad.numpy().transpose(1, 0, 2), kt.grad.numpy(), vt.grad.numpy()
+
+
+def test_backward_dense_budget_equals_torch_autograd():
+    # every key 0..t selected (K_tot >= L): the sparse backward is the dense
+    # causal one
+    rng = np.random.default_rng(22)
+    L, H, D = 40, 3, 16
+    q, do = rng.standard_normal((L, H, D)), rng.standard_normal((L, H, D))
+    k, v = rng.standard_normal((L, D)), rng.standard_normal((L, D))
+    lists = [np.arange(t + 1) for t in range(L)]
+    got = O.sparse_attn_backward(q, k, v, lists, D ** -0.5, do)
+    ref = _torch_grads(q, k, v, np.tril(np.ones((L, L), dtype=bool)), D ** -0.5, do)
+    for g, r, n in zip(got, ref, "qkv"):
+        assert np.abs(g - r).max() < 1e-12, n
+
+
+def test_backward_sparse_lists_equal_masked_torch_autograd():
+    rng = np.random.default_rng(23)
+    L, H, D, N = 24, 4, 8, 50
+    q, do = rng.standard_normal((L, H, D)), rng.standard_normal((L, H, D))
+    k, v = rng.standard_normal((N, D)), rng.standard_normal((N, D))
+    lists = _rand_lists(rng, L, N, 12)
+    mask = np.zeros((L, N), dtype=bool)
+    for t, sel in enumerate(lists):
+        mask[t, sel] = True
+    got = O.sparse_attn_backward(q, k, v, lists, 0.3, do)
+    ref = _torch_grads(q, k, v, mask, 0.3, do)
+    for g, r, n in zip(got, ref, "qkv"):
+        assert np.abs(g - r).max() < 1e-12, n
+
+
+def test_backward_closed_forms():
+    rng = np.random.default_rng(24)
+    L, H, D, N = 6, 2, 8, 10
+    q, do = rng.standard_normal((L, H, D)), rng.standard_normal((L, H, D))
+    k, v = rng.standard_normal((N, D)), rng.standard_normal((N, D))
+    # one key per row: p = 1, so dS = 0 (dq = 0, dk = 0) and dv[s] sums dO
+    lists = [np.array([t % 3]) for t in range(L)]
+    dq, dk, dv = O.sparse_attn_backward(q, k, v, lists, 0.5, do)
+    assert np.abs(dq).max() < 1e-14 and np.abs(dk).max() < 1e-14
+    for s in range(3):
+        rows = [t for t in range(L) if t % 3 == s]
+        assert np.allclose(dv[s], do[rows].sum(axis=(0, 1)), atol=1e-12)
+    assert np.all(dv[3:] == 0)
+    # all keys equal: the softmax gradient rows sum to zero, so dq = 0
+    kc = np.tile(rng.standard_normal(D), (N, 1))
+    lists = _rand_lists(rng, L, N, N)
+    dq, _, _ = O.sparse_attn_backward(q, kc, v, lists, 0.5, do)
+    assert np.abs(dq).max() < 1e-12
+
+
+# ----------------------------------------------------------------------------- KL operator
+def _head_avg_p(q_row, k, sel, scale):
+    """Target distribution from torch's softmax (a library routine)."""
+    z = torch.tensor(q_row) @ torch.tensor(k[sel]).T * scale
+    return torch.softmax(z, dim=-1).mean(dim=0).numpy()
+
+
+def test_kl_matches_scipy_and_softmax():
+    from scipy.special import rel_entr, softmax
+    rng = np.random.default_rng(31)
+    for trial in range(6):
+        H, D, N = int(rng.integers(1, 5)), 16, 60
+        k = rng.standard_normal((N, D))
+        q = rng.standard_normal((H, D))
+        sel = np.sort(rng.choice(N, int(rng.integers(1, 40)), replace=False))
+        lg = 3 * rng.standard_normal(len(sel))
+        kl, g = O.kl_warmup_row(q, k, sel, 0.25, lg)
+        p = _head_avg_p(q, k, sel, 0.25)
+        qd = softmax(lg)
+        assert abs(kl - rel_entr(p, qd).sum()) < 1e-12
+        assert np.abs(g - (qd - p)).max() < 1e-14
+        assert kl >= 0 and abs(g.sum()) < 1e-12
+
+
+def test_kl_closed_forms_and_finite_differences():
+    from scipy.stats import entropy
+    rng = np.random.default_rng(32)
+    H, D, N = 3, 8, 30
+    k, q = rng.standard_normal((N, D)), rng.standard_normal((H, D))
+    sel = np.arange(5, 25)
+    p = _head_avg_p(q, k, sel, 0.4)
+    # logits = log p (+ any constant): KL = 0, gradient 0
+    kl, g = O.kl_warmup_row(q, k, sel, 0.4, np.log(p) + 7.0)
+    assert abs(kl) < 1e-12 and np.abs(g).max() < 1e-12
+    # uniform indexer: KL = log n - entropy(p)
+    kl, _ = O.kl_warmup_row(q, k, sel, 0.4, np.zeros(len(sel)))
+    assert abs(kl - (np.log(len(sel)) - entropy(p))) < 1e-12
+    # gradient by central differences
+    lg = rng.standard_normal(len(sel))
+    _, g = O.kl_warmup_row(q, k, sel, 0.4, lg)
+    eps = 1e-6
+    for i in range(len(sel)):
+        a, b = lg.copy(), lg.copy()
+        a[i] += eps
+        b[i] -= eps
+        num = (O.kl_warmup_row(q, k, sel, 0.4, a)[0] - O.kl_warmup_row(q, k, sel, 0.4, b)[0]) / (2 * eps)
+        assert abs(num - g[i]) < 1e-8
