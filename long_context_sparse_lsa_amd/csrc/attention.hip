@@ -88,17 +88,6 @@ struct KVStage {
   v4u k[8 / TW], v[8 / TW];
 };
 
-// Buffer resource over `bytes` bytes at base. Base and size are wave-uniform
-// at every use; readfirstlane lets the compiler keep the resource in scalar
-// registers.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t uniform_rsrc(const void* base, uint32_t bytes) {
-  const uint64_t p = (uint64_t)(uintptr_t)base;
-  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)p);
-  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(p >> 32));
-  const int nb = __builtin_amdgcn_readfirstlane((int)bytes);
-  return __builtin_amdgcn_make_buffer_rsrc((void*)(uintptr_t)(((uint64_t)hi << 32) | lo), (short)0, nb, 0x00020000);
-}
-
 // Rows [0, n_k) of one sequence's K or V cache.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t cache_rsrc(const uint16_t* base, int n_k) {
   return uniform_rsrc(base, (uint32_t)n_k * (uint32_t)(kD * 2));
@@ -144,7 +133,6 @@ __device__ __forceinline__ void store_kv(const KVStage<TW>& s, char* blk, int gw
 // dims 16(G % 2) + 4(j % 4) (G = lane / 16). Lane (g, c) then holds dim c of
 // keys 16js + 4g + {0..3} and 16js + 8 + 4g + {0..3}: the key order of the P^T
 // operand.
-typedef short v4s __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ v8bf read_vt(const char* vblk, int lane_off, int mb, int js) {
   const char* p = vblk + lane_off + 16 * js * kVRow + 64 * mb;
   const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s*)p);
@@ -327,7 +315,8 @@ __device__ __forceinline__ void attn_block(const v8bf (&Q)[NB][8], const char* b
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
         const float mnew = mx[nb] > st.m[nb] + kSlack ? mx[nb] : st.m[nb];
-        const float alpha = __builtin_amdgcn_exp2f(st.m[nb] - mnew);  // 0 when st.m is -inf
+        // 0 when st.m is -inf; 1 when the reference stays (also -inf - -inf)
+        const float alpha = mnew == st.m[nb] ? 1.f : __builtin_amdgcn_exp2f(st.m[nb] - mnew);
         st.l[nb] *= alpha;
 #pragma unroll
         for (int mb = 0; mb < 4; ++mb) st.o[mb][nb] *= alpha;
@@ -335,11 +324,13 @@ __device__ __forceinline__ void attn_block(const v8bf (&Q)[NB][8], const char* b
       }
     }
     // p = 2^(S*sl2 - m) (exp2 of -inf is 0); l sums p in fp32, and P is
-    // rounded to bf16 for the PV product
+    // rounded to bf16 for the PV product. A block whose keys are all masked
+    // while nothing has been seen yet (m still -inf) adds zeros: the
+    // reference is taken as 0 there, not +inf (which would make -inf + inf).
     v8bf P[NB][2];
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
-      const float nm = -st.m[nb];
+      const float nm = st.m[nb] == -INFINITY ? 0.f : -st.m[nb];
       float rs = 0.f;
 #pragma unroll
       for (int js = 0; js < 2; ++js) {

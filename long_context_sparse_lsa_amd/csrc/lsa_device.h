@@ -64,6 +64,38 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
 }
 
+// Buffer resource over `bytes` bytes at base. Base and size are wave-uniform
+// at every use; readfirstlane lets the compiler keep the resource in scalar
+// registers. Loads through it at offsets past `bytes` return zeros.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t uniform_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t p = (uint64_t)(uintptr_t)base;
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)p);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(p >> 32));
+  const int nb = __builtin_amdgcn_readfirstlane((int)bytes);
+  return __builtin_amdgcn_make_buffer_rsrc((void*)(uintptr_t)(((uint64_t)hi << 32) | lo), (short)0, nb, 0x00020000);
+}
+
+typedef short v4s __attribute__((ext_vector_type(4)));
+
+// Transposed MFMA operand from a row-major bf16 matrix in LDS (rows = the
+// contraction index, `pitch` bytes apart; 32 columns from the start of p):
+// two ds_read_b64_tr_b16 give lane (g, c) column c and the 8 contraction rows
+// 4g + {0..3} and 8 + 4g + {0..3} of the 16 at p. The lane's address offset
+// is tr_lane_off(pitch). This row order is the row order of a 32x32 MFMA
+// accumulator's lane entries 0..7 (and, 16 rows on, 8..15), so the operand
+// pairs with one taken from an accumulator in place.
+__device__ __forceinline__ int tr_lane_off(int pitch) {
+  const int l = lane_id(), G = l >> 4, jj = l & 15;
+  return (4 * (G >> 1) + (jj >> 2)) * pitch + (16 * (G & 1) + 4 * (jj & 3)) * 2;
+}
+__device__ __forceinline__ v8bf read_tr(const char* p, int pitch) {
+  const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s*)p);
+  const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s*)(p + 8 * pitch));
+  const v4u u = v4u{__builtin_bit_cast(v2u, lo)[0], __builtin_bit_cast(v2u, lo)[1], __builtin_bit_cast(v2u, hi)[0],
+                    __builtin_bit_cast(v2u, hi)[1]};
+  return __builtin_bit_cast(v8bf, u);
+}
+
 // Order-preserving map of int32 scores to uint32 (INT32_MIN -> 0).
 __device__ __forceinline__ uint32_t score_key(int32_t s) { return (uint32_t)s ^ 0x80000000u; }
 

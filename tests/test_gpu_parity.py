@@ -466,6 +466,42 @@ def test_mtp_rows_with_causal_tails(n_q, n_split):
     err2.check()
 
 
+@pytest.mark.parametrize("n_split", [8, 3])
+def test_mtp_short_lists(n_split):
+    """MTP rows with causal tails on lists shorter than the split count (empty
+    parts), including an empty target list: the target row then attends to
+    nothing (o = 0, lse = -inf) and draft row j to the j drafts alone."""
+    B, n_q, H, n_k = 4, 4, 64, 400
+    lens, tgts = [0, 5, 49, 1], [10, 30, 200, 0]
+    K_tot = 64
+    rng = np.random.default_rng(77)
+    idx = np.full((B, 1, K_tot), -1, dtype=np.int32)
+    for b in range(B):
+        idx[b, 0, : lens[b]] = np.sort(rng.choice(tgts[b] + 1, lens[b], replace=False))
+    idx_d = torch.tensor(idx, device=DEV)
+    n_sel = torch.tensor(np.array(lens, dtype=np.int32)[:, None], device=DEV)
+    tgt = torch.tensor(np.array(tgts, dtype=np.int32), device=DEV)
+    say(f"mtp short lists n_split={n_split} lens={lens}")
+    q = bf((B, n_q, H, 128), "msq", n_split)
+    kc, vc = bf((B, n_k, 128), "msk", n_split), bf((B, n_k, 128), "msv", n_split)
+    o, lse = L.lsa_sparse_attn_decode_mtp(q, kc, vc, idx_d, n_sel, tgt, n_split=n_split, want_lse=True)
+    o2, lse2 = L.lsa_sparse_attn_decode_mtp(q, kc, vc, idx_d, n_sel, tgt, n_split=n_split, want_lse=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o2) and torch.equal(lse, lse2)
+    qf, kf, vf, of, lf = f64(q), f64(kc), f64(vc), f64(o), np_(lse)
+    assert np.all(np.isfinite(of)), "non-finite output"
+    err = AttnErrors(f"mtp short lists n_split={n_split}")
+    for b in range(B):
+        for j, ref in enumerate(O.mtp_row_lists(idx[b, 0, : lens[b]], tgts[b], n_q)):
+            if len(ref) == 0:
+                assert np.all(of[b, j] == 0) and np.all(np.isneginf(lf[b, j])), f"b{b} row {j}"
+                continue
+            ref_o, ref_l = O.attend(qf[b, j], kf[b], vf[b], ref, 128 ** -0.5)
+            err.add(of[b, j], ref_o)
+            assert np.abs(lf[b, j] - ref_l).max() < 1e-3, f"b{b} row {j} lse"
+    err.check()
+
+
 # ------------------------------------------------------------------ attention
 def random_index(B, rows, K_tot, t_of_row, n_k, seed):
     rng = np.random.default_rng(seed)
