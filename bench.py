@@ -1,11 +1,13 @@
 #!/usr/bin/env python3
 """Benchmark of the LSA hot path on one MI355X.
 
-Default workload (--config c2): prefill of one sequence of L = 32768 tokens;
-indexer H_I = 64 heads, d_I = 128, int8; 4 sinks + 512-token window + top-k
-to 2048 keys; 64 query heads on one bf16 KV head of dim 128. One step =
-fused indexer scoring + top-k selection for every row (lsa_select_topk),
-then sparse attention for every row and layer (lsa_sparse_attn_prefill).
+Default workload (--config c5): cross-layer-index prefill of one sequence of
+L = 131072 tokens over two layers; indexer H_I = 64 heads, d_I = 128, int8;
+4 sinks + 1024-token window + top-k to 2048 keys; per layer 64 query heads
+on one bf16 KV head of dim 128. One step = fused indexer scoring + top-k
+selection for every row (lsa_select_topk), then sparse attention for every
+row of both layers, which reuse the one index (lsa_sparse_attn_prefill).
+--config c2 is the same step at L = 32768 with one layer and a 512 window.
 Decode workloads (--config c3 / c4) time one decode step: selection for
 the target row of every sequence, then split-KV attention with the merge;
 the step is captured once as a HIP graph and the timed steps replay it
@@ -18,7 +20,7 @@ library's own event timing over the same number of further steps, the
 roofline of the kernel with the most time per step, and the CPU oracle timed
 on a bounded sample of the same workload.
 
-  python bench.py [--gpus 1] [--steps K] [--warmup W] [--config c2]
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--config c5]
 """
 import argparse
 import json
@@ -39,7 +41,7 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=5)
     p.add_argument("--warmup", type=int, default=2)
-    p.add_argument("--config", default="c2", choices=["c1", "c2", "c3", "c4", "c5"])
+    p.add_argument("--config", default="c5", choices=["c1", "c2", "c3", "c4", "c5"])
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=10.0, help="time budget of the oracle sample")
     p.add_argument("--copy-probe", action="store_true",
@@ -132,6 +134,22 @@ def kernel_times(L, torch, step, steps, park=False):
     finally:
         L.lsa_kernel_timing(False)
     return out
+
+
+def measured_mfma_peak(torch, L, kind, n_wg=256 * 8, iters=2048, reps=3):
+    """TOP/s (kind 0, int8) or TFLOP/s (kind 1, bf16) of the library's
+    matrix-core probe: register-only MFMA chains on every CU, event-timed."""
+    sink = torch.empty(n_wg, dtype=torch.int32, device="cuda")
+    L.lsa_probe_mfma(kind, n_wg, iters // 8, sink)  # warm the clock up
+    best = 0.0
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        ops = L.lsa_probe_mfma(kind, n_wg, iters, sink)
+        e1.record()
+        torch.cuda.synchronize()
+        best = max(best, ops / (e0.elapsed_time(e1) * 1e-3) / 1e12)
+    return best
 
 
 def roofline(bound, name, work_per_step, kt, peak, unit):
@@ -423,6 +441,14 @@ def main():
     wl = configs.BY_ID[args.config]
     out = run_prefill(args, wl, torch) if wl.kind == "prefill" else run_decode(args, wl, torch)
     roof = out["roofline"]
+    if roof["bound"] == "mfma":
+        # the rate the matrix cores sustain for this dtype on this GPU in this
+        # run (register-only probe): the attainable ceiling next to the
+        # published peak
+        kind = 0 if roof["unit"] == "TOP/s" else 1
+        mp = measured_mfma_peak(torch, L, kind)
+        roof["measured_peak"] = round(mp, 1)
+        roof["frac_of_measured"] = round(roof["achieved"] / mp, 4)
     if roof["bound"] == "hbm":
         # the bandwidth a plain device copy reaches on this GPU in this run: the
         # attainable ceiling next to the 8 TB/s figure

@@ -246,6 +246,19 @@ int32_t lsa_sparse_attn_decode_mtp(const lsa_bf16* q, const lsa_bf16* k_cache,
 int32_t lsa_kernel_timing(int32_t on);
 int32_t lsa_kernel_time(const char* name, float* ms_mean, int32_t* launches);
 
+/* Matrix-core peak probe, a measurement aid (not part of the method): enqueues
+ * n_wg workgroups of 4 waves, each wave issuing `iters` rounds of 8
+ * independent MFMA instructions on register operands (no memory traffic),
+ * so that the caller's event timing of the launch gives the rate the chip
+ * sustains at its current clock.
+ *   kind 0: v_mfma_i32_32x32x32_i8 (65536 int8 ops each); kind 1:
+ *   v_mfma_f32_32x32x16_bf16 (32768 flop each)
+ *   sink [n_wg] int32, DEVICE: one value per workgroup (keeps results live)
+ *   *ops (may be NULL): the operations one launch performs
+ * Errors: LSA_INVALID_ARG for a NULL or misaligned sink or non-positive
+ * sizes, LSA_UNSUPPORTED for another kind, LSA_HIP for a launch error. */
+int32_t lsa_probe_mfma(int32_t kind, int32_t n_wg, int32_t iters, int32_t* sink, double* ops, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -54,6 +54,7 @@ SIGNATURES = {
                                         _P]),
     "lsa_kernel_timing": (_I, [_I]),
     "lsa_kernel_time": (_I, [ctypes.c_char_p, ctypes.POINTER(_F), ctypes.POINTER(_I)]),
+    "lsa_probe_mfma": (_I, [_I, _I, _I, _P, ctypes.POINTER(ctypes.c_double), _P]),
 }
 
 _lib = None
@@ -380,3 +381,16 @@ def lsa_kernel_time(name):
     ms, n = _F(), _I()
     _check("lsa_kernel_time", load().lsa_kernel_time(name.encode(), ctypes.byref(ms), ctypes.byref(n)))
     return float(ms.value), int(n.value)
+
+
+def lsa_probe_mfma(kind, n_wg, iters, sink):
+    """Enqueue the matrix-core peak probe (kind 0 int8, 1 bf16) on the
+    current stream; sink is an int32 device tensor of n_wg entries. Returns
+    the operations one launch performs (time the launch with events)."""
+    _dev(sink, torch.int32, "sink")
+    if sink.numel() < n_wg:
+        raise ValueError("sink needs n_wg entries")
+    ops = ctypes.c_double(0.0)
+    _check("lsa_probe_mfma", load().lsa_probe_mfma(int(kind), int(n_wg), int(iters), _ptr(sink), ctypes.byref(ops),
+                                                   _stream()))
+    return float(ops.value)
