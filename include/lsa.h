@@ -63,7 +63,8 @@ enum {
   LSA_UNSUPPORTED = 2, /* shape outside the tuned set (see each call)         */
   LSA_WORKSPACE = 3,   /* workspace too small                                 */
   LSA_RANGE = 4,       /* sum_h |w[h]| * d_I * 128 * 128 >= 2^31: int32 not exact */
-  LSA_HIP = 5          /* a HIP launch reported an error                       */
+  LSA_HIP = 5,         /* a HIP launch reported an error                       */
+  LSA_SCRATCH_LIMIT = 6 /* sizes exceed the fixed scratch of a no-alloc call    */
 };
 
 /* Human-readable name of a status code (static storage). */
@@ -211,6 +212,28 @@ int32_t lsa_sparse_attn_decode(const lsa_bf16* q, const lsa_bf16* k_cache,
                                int32_t n_k, int32_t H, int32_t D, int32_t K_tot,
                                int32_t n_split, float scale, lsa_bf16* o, float* lse,
                                void* ws, size_t ws_bytes, size_t* ws_needed, void* stream);
+
+/* lsa_sparse_attn_decode for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same computation and kernels, with the split-KV partials in
+ * a fixed scratch array inside the library instead of a caller workspace. The
+ * array holds lsa_noalloc_scratch_bytes() bytes (40 MiB; C3's batch of 64
+ * sequences x 8 parts x 4 rows x 64 heads needs 35 MB) per GPU, allocated
+ * with the library's code on each device and held until the process ends.
+ * The call allocates nothing and issues no memset: every partial is written
+ * before it is read. Calls that overlap on one GPU (several streams or host
+ * threads) share that array and race; serialize them.
+ *   arguments as lsa_sparse_attn_decode, without ws / ws_bytes / ws_needed
+ * Errors: as lsa_sparse_attn_decode; LSA_SCRATCH_LIMIT when the partials
+ * (B * n_split * n_q * H rows of 264 bytes) exceed the array; LSA_HIP when the
+ * array's device address cannot be found. */
+int32_t lsa_sparse_attn_decode_noalloc(const lsa_bf16* q, const lsa_bf16* k_cache,
+                                       const lsa_bf16* v_cache, const int32_t* idx,
+                                       const int32_t* n_sel, int32_t n_idx, int32_t B, int32_t n_q,
+                                       int32_t n_k, int32_t H, int32_t D, int32_t K_tot,
+                                       int32_t n_split, float scale, lsa_bf16* o, float* lse,
+                                       void* stream);
+size_t lsa_noalloc_scratch_bytes(void);
 
 /* The same split-KV decode for MTP rows with causal tails, without building
  * per-row lists: all n_q rows of a sequence share the target's list idx

@@ -14,7 +14,7 @@ import torch
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "liblsa.so")
 
-LSA_OK, LSA_INVALID_ARG, LSA_UNSUPPORTED, LSA_WORKSPACE, LSA_RANGE, LSA_HIP = range(6)
+LSA_OK, LSA_INVALID_ARG, LSA_UNSUPPORTED, LSA_WORKSPACE, LSA_RANGE, LSA_HIP, LSA_SCRATCH_LIMIT = range(7)
 
 
 class LSAError(RuntimeError):
@@ -55,6 +55,8 @@ SIGNATURES = {
     "lsa_kernel_timing": (_I, [_I]),
     "lsa_kernel_time": (_I, [ctypes.c_char_p, ctypes.POINTER(_F), ctypes.POINTER(_I)]),
     "lsa_probe_mfma": (_I, [_I, _I, _I, _P, ctypes.POINTER(ctypes.c_double), _P]),
+    "lsa_sparse_attn_decode_noalloc": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _F, _P, _P, _P]),
+    "lsa_noalloc_scratch_bytes": (_Z, []),
 }
 
 _lib = None
@@ -336,6 +338,28 @@ def lsa_sparse_attn_decode(q, k_cache, v_cache, idx, n_sel, n_split=8, scale=Non
     lse = torch.empty((B, n_q, H), dtype=torch.float32, device=q.device) if want_lse else None
     _check("lsa_sparse_attn_decode", lib.lsa_sparse_attn_decode(*args, _ptr(o), _ptr(lse), _ptr(ws), ws.numel(),
                                                                 None, _stream()))
+    return (o, lse) if want_lse else o
+
+
+def lsa_sparse_attn_decode_noalloc(q, k_cache, v_cache, idx, n_sel, n_split=8, scale=None, want_lse=False):
+    """lsa_sparse_attn_decode with the partials in the library's fixed scratch
+    array (no workspace). Returns o [B, n_q, H, D] bf16 (and lse)."""
+    lib = load()
+    for t, n in ((q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache")):
+        _dev(t, torch.bfloat16, n)
+    _dev(idx, torch.int32, "idx")
+    _dev(n_sel, torch.int32, "n_sel")
+    B, n_q, H, D = q.shape
+    n_k = k_cache.shape[1]
+    n_idx, K_tot = idx.shape[1], idx.shape[2]
+    if idx.shape[0] != B or n_sel.shape != (B, n_idx):
+        raise ValueError("shape mismatch")
+    scale = D ** -0.5 if scale is None else float(scale)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, n_q, H), dtype=torch.float32, device=q.device) if want_lse else None
+    _check("lsa_sparse_attn_decode_noalloc", lib.lsa_sparse_attn_decode_noalloc(
+        _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(idx), _ptr(n_sel), n_idx, B, n_q, n_k, H, D, K_tot, n_split,
+        scale, _ptr(o), _ptr(lse), _stream()))
     return (o, lse) if want_lse else o
 
 

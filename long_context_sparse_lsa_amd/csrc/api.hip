@@ -1,12 +1,15 @@
 // C ABI of the LSA hot path: argument checks, workspace sizing, launches.
 //
 // Every check that the host can make runs before the first launch, so an
-// argument error never leaves half of the work enqueued. The library keeps no
-// state and allocates nothing: workspace comes from the caller.
+// argument error never leaves half of the work enqueued. The library
+// allocates nothing at run time: workspace comes from the caller, except for
+// the no-alloc decode entry at the end of this file, whose fixed scratch array
+// is part of the loaded code (its per-device address is the only state kept).
 #include <math.h>
 #include <stdint.h>
 
 #include <algorithm>
+#include <mutex>
 
 #include "lsa.h"
 #include "lsa_internal.h"
@@ -81,6 +84,8 @@ extern "C" const char* lsa_status_string(int32_t s) {
     case LSA_WORKSPACE: return "LSA_WORKSPACE: workspace too small";
     case LSA_RANGE: return "LSA_RANGE: sum|w| * d_I * 128^2 >= 2^31, scores would not be exact int32";
     case LSA_HIP: return "LSA_HIP: a HIP launch failed";
+    case LSA_SCRATCH_LIMIT:
+      return "LSA_SCRATCH_LIMIT: the sizes need more than the library's fixed scratch array";
     default: return "LSA_UNKNOWN_STATUS";
   }
 }
@@ -571,4 +576,56 @@ extern "C" int32_t lsa_sparse_attn_decode_mtp(const lsa_bf16* q, const lsa_bf16*
   if (n_q > 32) return LSA_UNSUPPORTED;  // the drafts' keys fit one 32-key block
   return attn_decode(q, k_cache, v_cache, idx, n_sel, tgt_pos, 1, B, n_q, n_k, H, D, K_tot, n_split, scale, o,
                      lse, ws, ws_bytes, ws_needed, stream);
+}
+
+// ------------------------------------------------------------------ no-alloc
+// Split-KV decode for callers that cannot allocate (code under graph capture,
+// tight serving loops): the partials live in a fixed file-scope device array
+// instead of a caller workspace. Each GPU the library runs on holds its own
+// copy of the array until the process ends. Host code never passes the
+// array's name to a kernel (on the host it is only a stand-in for the
+// symbol): its device address is looked up once per device, with that device
+// current, and that address is what the launches get.
+namespace {
+
+constexpr size_t kNoAllocScratchBytes = (size_t)40 << 20;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+// Device address of `scratch` on the current device, or null on failure.
+void* scratch_ptr() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess) return nullptr;
+    g_scratch_ptr[dev] = ptr;
+  }
+  return g_scratch_ptr[dev];
+}
+
+}  // namespace
+
+extern "C" size_t lsa_noalloc_scratch_bytes(void) { return kNoAllocScratchBytes; }
+
+extern "C" int32_t lsa_sparse_attn_decode_noalloc(const lsa_bf16* q, const lsa_bf16* k_cache,
+                                                  const lsa_bf16* v_cache, const int32_t* idx,
+                                                  const int32_t* n_sel, int32_t n_idx, int32_t B, int32_t n_q,
+                                                  int32_t n_k, int32_t H, int32_t D, int32_t K_tot,
+                                                  int32_t n_split, float scale, lsa_bf16* o, float* lse,
+                                                  void* stream) {
+  // size checks first (no device call yet): the partials must fit the array
+  size_t need = 0;
+  const int32_t s = attn_decode(q, k_cache, v_cache, idx, n_sel, nullptr, n_idx, B, n_q, n_k, H, D, K_tot,
+                                n_split, scale, o, lse, nullptr, 0, &need, stream);
+  if (s != LSA_OK) return s;
+  if (need > kNoAllocScratchBytes) return LSA_SCRATCH_LIMIT;
+  void* ws = scratch_ptr();
+  if (ws == nullptr) return LSA_HIP;
+  return attn_decode(q, k_cache, v_cache, idx, n_sel, nullptr, n_idx, B, n_q, n_k, H, D, K_tot, n_split, scale,
+                     o, lse, ws, kNoAllocScratchBytes, nullptr, stream);
 }

@@ -32,7 +32,7 @@ def test_exports_every_declared_symbol():
 
 
 def test_status_strings():
-    for s in range(6):
+    for s in range(7):
         msg = L.status_string(s)
         assert msg.startswith("LSA_")
     assert "UNKNOWN" in L.status_string(99)
