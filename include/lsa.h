@@ -213,6 +213,62 @@ int32_t lsa_sparse_attn_decode(const lsa_bf16* q, const lsa_bf16* k_cache,
                                int32_t n_split, float scale, lsa_bf16* o, float* lse,
                                void* ws, size_t ws_bytes, size_t* ws_needed, void* stream);
 
+/* Sparse attention backward, deterministic (training; "如何在 5 万张国产芯片训练出
+ * 1.6T 万亿参数模型？", section "④ 痛点③：长上下文训练三招": the LSA operator comes with
+ * deterministic attention operators; haoling.cc article, section 三: a
+ * deterministic attention backward and deterministic scatter operators).
+ * Gradients of a loss L through o = lsa_sparse_attn_prefill(q, k, v, idx,
+ * n_sel), given d_o = dL/do:
+ *   dq[t, h] = scale sum_s dS[t,h,s] k[s],  dk[s] = scale sum_{t,h} dS[t,h,s] q[t,h],
+ *   dv[s] = sum_{t,h} P[t,h,s] d_o[t,h],     dS = P (d_o . v_s - sum_d d_o . o)
+ * over the keys s of each row's list; a key's gradient sums the contributions
+ * of every row that selected it. P is recomputed from lse.
+ *   q, d_o, o [B, L, H, D] bf16 (o: the forward's output); lse [B, L, H] fp32
+ *   (the forward's natural-log lse); k, v [B, n_k, D] bf16; idx [B, L, K_tot],
+ *   n_sel [B, L]: each row's list of distinct positions (as the selection
+ *   writes them)
+ *   dq [B, L, H, D] bf16 out; dk, dv [B, n_k, D] fp32 out (keys no row
+ *   selected get 0)
+ * The key gradients are summed in the workspace as int64 fixed point (each
+ * contribution rounded to a multiple of 2^-32, to nearest even) by integer
+ * atomic adds, which are associative: the result does not depend on the order
+ * rows are processed, so repeated calls are bit-identical, and the only
+ * rounding beyond fp32 arithmetic is that 2^-32 per contribution. Every
+ * contribution and every partial sum of one element must stay below 2^31 in
+ * magnitude (the int64 range); larger values wrap.
+ *   ws: 2 * B * n_k * 128 * 8 bytes (size query with ws = NULL)
+ * Supported: D = 128; H in {32, 64, 128}; n_k <= 16777215.
+ * Errors: LSA_INVALID_ARG for NULL/misaligned pointers or bad sizes,
+ * LSA_UNSUPPORTED for other shapes, LSA_WORKSPACE, LSA_HIP. */
+int32_t lsa_sparse_attn_backward(const lsa_bf16* q, const lsa_bf16* k, const lsa_bf16* v,
+                                 const int32_t* idx, const int32_t* n_sel, const lsa_bf16* o,
+                                 const float* lse, const lsa_bf16* d_o, int32_t B, int32_t L,
+                                 int32_t n_k, int32_t H, int32_t D, int32_t K_tot, float scale,
+                                 lsa_bf16* dq, float* dk, float* dv, void* ws, size_t ws_bytes,
+                                 size_t* ws_needed, void* stream);
+
+/* LSA warm-up KL operator (LongCat-2.0 release article, section "长上下文训练",
+ * paragraph "LSA 算子与前向优化": a KL-loss operator whose single forward pass
+ * gives both the loss and its gradient). For query row t of sequence b with
+ * key list idx[b, t, :n] (n = n_sel[b, t]; the selected keys, or every key
+ * 0..t for a dense warm-up) and indexer logits logits[b, t, :n] of those keys:
+ *   p_j  = (1/H) sum_h exp(scale q[t,h] . k[idx_j] - lse[t,h])   (the row's
+ *          attention distribution averaged over its H heads; lse is the
+ *          forward's, lsa_sparse_attn_prefill over the same lists)
+ *   kl[b, t] = sum_j p_j (log p_j - log softmax(logits)_j)
+ *   dlogits[b, t, j] = softmax(logits)_j - p_j  (d kl / d logits; 0 for j >= n)
+ * No gradient flows into the attention (warm-up trains the indexer alone).
+ *   q [B, L, H, D] bf16, k [B, n_k, D] bf16, lse [B, L, H] fp32, idx / n_sel as
+ *   for lsa_sparse_attn_prefill (distinct positions), logits [B, L, K_tot] fp32
+ *   kl [B, L] fp32 out (a row with n = 0 gets 0), dlogits [B, L, K_tot] fp32 out
+ * Deterministic: the head and key sums run in a fixed order.
+ * Supported: D = 128; H in {32, 64, 128}; n_k <= 16777215.
+ * Errors: LSA_INVALID_ARG for NULL/misaligned pointers or bad sizes,
+ * LSA_UNSUPPORTED for other shapes, LSA_HIP. */
+int32_t lsa_kl_warmup(const lsa_bf16* q, const lsa_bf16* k, const int32_t* idx, const int32_t* n_sel,
+                      const float* lse, const float* logits, int32_t B, int32_t L, int32_t n_k, int32_t H,
+                      int32_t D, int32_t K_tot, float scale, float* kl, float* dlogits, void* stream);
+
 /* lsa_sparse_attn_decode for callers that cannot allocate device memory
  * (code under HIP graph capture, tight serving loops, harnesses that forbid
  * hipMalloc): the same computation and kernels, with the split-KV partials in

@@ -57,6 +57,9 @@ SIGNATURES = {
     "lsa_probe_mfma": (_I, [_I, _I, _I, _P, ctypes.POINTER(ctypes.c_double), _P]),
     "lsa_sparse_attn_decode_noalloc": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _F, _P, _P, _P]),
     "lsa_noalloc_scratch_bytes": (_Z, []),
+    "lsa_sparse_attn_backward": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _P, _P, _P, _P, _Z,
+                                      _ZP, _P]),
+    "lsa_kl_warmup": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _P, _P, _P]),
 }
 
 _lib = None
@@ -339,6 +342,63 @@ def lsa_sparse_attn_decode(q, k_cache, v_cache, idx, n_sel, n_split=8, scale=Non
     _check("lsa_sparse_attn_decode", lib.lsa_sparse_attn_decode(*args, _ptr(o), _ptr(lse), _ptr(ws), ws.numel(),
                                                                 None, _stream()))
     return (o, lse) if want_lse else o
+
+
+def lsa_sparse_attn_backward(q, k, v, idx, n_sel, o, lse, d_o, scale=None, ws=None):
+    """Deterministic backward of lsa_sparse_attn_prefill: q, o, d_o [B, L, H, D]
+    bf16, lse [B, L, H] fp32 (the forward's), k/v [B, n_k, D] bf16, idx
+    [B, L, K_tot], n_sel [B, L]. Returns (dq bf16 like q, dk fp32, dv fp32)."""
+    lib = load()
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (d_o, "d_o")):
+        _dev(t, torch.bfloat16, n)
+    _dev(lse, torch.float32, "lse")
+    _dev(idx, torch.int32, "idx")
+    _dev(n_sel, torch.int32, "n_sel")
+    B, L, H, D = q.shape
+    n_k = k.shape[1]
+    K_tot = idx.shape[-1]
+    if (idx.shape != (B, L, K_tot) or n_sel.shape != (B, L) or v.shape != k.shape or o.shape != q.shape
+            or d_o.shape != q.shape or lse.shape != (B, L, H)):
+        raise ValueError("shape mismatch")
+    scale = D ** -0.5 if scale is None else float(scale)
+    need = ctypes.c_size_t(0)
+    args = (_ptr(q), _ptr(k), _ptr(v), _ptr(idx), _ptr(n_sel), _ptr(o), _ptr(lse), _ptr(d_o), B, L, n_k, H, D,
+            K_tot, scale)
+    _check("lsa_sparse_attn_backward", lib.lsa_sparse_attn_backward(*args, None, None, None, None, 0,
+                                                                    ctypes.byref(need), None))
+    if ws is None or ws.numel() < need.value:
+        ws = _workspace(need.value, q.device)
+    dq = torch.empty_like(q)
+    dk = torch.empty((B, n_k, D), dtype=torch.float32, device=q.device)
+    dv = torch.empty_like(dk)
+    _check("lsa_sparse_attn_backward", lib.lsa_sparse_attn_backward(*args, _ptr(dq), _ptr(dk), _ptr(dv), _ptr(ws),
+                                                                    ws.numel(), None, _stream()))
+    return dq, dk, dv
+
+
+def lsa_kl_warmup(q, k, idx, n_sel, lse, logits, scale=None):
+    """Warm-up KL of each row's head-averaged attention distribution against
+    the softmax of its indexer logits: q [B, L, H, D] bf16, k [B, n_k, D] bf16,
+    idx [B, L, K_tot], n_sel [B, L], lse [B, L, H] fp32 (the forward's), logits
+    [B, L, K_tot] fp32. Returns (kl [B, L] fp32, dlogits [B, L, K_tot] fp32)."""
+    lib = load()
+    _dev(q, torch.bfloat16, "q")
+    _dev(k, torch.bfloat16, "k")
+    _dev(idx, torch.int32, "idx")
+    _dev(n_sel, torch.int32, "n_sel")
+    _dev(lse, torch.float32, "lse")
+    _dev(logits, torch.float32, "logits")
+    B, Lq, H, D = q.shape
+    n_k = k.shape[1]
+    K_tot = idx.shape[-1]
+    if idx.shape != (B, Lq, K_tot) or n_sel.shape != (B, Lq) or lse.shape != (B, Lq, H) or logits.shape != idx.shape:
+        raise ValueError("shape mismatch")
+    scale = D ** -0.5 if scale is None else float(scale)
+    kl = torch.empty((B, Lq), dtype=torch.float32, device=q.device)
+    dlog = torch.empty((B, Lq, K_tot), dtype=torch.float32, device=q.device)
+    _check("lsa_kl_warmup", lib.lsa_kl_warmup(_ptr(q), _ptr(k), _ptr(idx), _ptr(n_sel), _ptr(lse), _ptr(logits), B,
+                                              Lq, n_k, H, D, K_tot, scale, _ptr(kl), _ptr(dlog), _stream()))
+    return kl, dlog
 
 
 def lsa_sparse_attn_decode_noalloc(q, k_cache, v_cache, idx, n_sel, n_split=8, scale=None, want_lse=False):

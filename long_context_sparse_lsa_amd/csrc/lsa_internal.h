@@ -120,6 +120,40 @@ struct PrefillArgs {
 };
 hipError_t launch_attn_prefill(const PrefillArgs& a, hipStream_t st);
 
+// Sparse attention backward. Row t of sequence b attends over idx[b, t, :n_sel]
+// (unique positions); o and lse are the forward's outputs for the same rows,
+// d_o the gradient of the loss with respect to o. dq (bf16) is written per
+// row; the key gradients are summed into int64 fixed-point accumulators
+// (value * 2^32, rounded to nearest even) dk_acc / dv_acc [B, n_k, 128],
+// which must start at zero, and converted by launch_attn_bwd_finish.
+struct BwdArgs {
+  const uint16_t *q, *k, *v, *o, *d_o;
+  const float* lse;
+  const int32_t *idx, *n_sel;
+  int B, L, n_k, H, K_tot;
+  float sl2;    // scale * log2(e)
+  float scale;
+  uint16_t* dq;
+  int64_t *dk_acc, *dv_acc;
+};
+hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t st);
+hipError_t launch_attn_bwd(const BwdArgs& a, hipStream_t st);
+hipError_t launch_attn_bwd_finish(const int64_t* acc, float* out, size_t n, hipStream_t st);
+
+// Warm-up KL operator: per row, KL(head-averaged attention distribution over
+// the row's list || softmax of the row's logits) and its logit gradient.
+struct KlArgs {
+  const uint16_t *q, *k;
+  const float* lse;
+  const int32_t *idx, *n_sel;
+  const float* logits;
+  int B, L, n_k, H, K_tot;
+  float sl2;  // scale * log2(e)
+  float* kl;
+  float* dlogits;
+};
+hipError_t launch_kl_warmup(const KlArgs& a, hipStream_t st);
+
 struct DecodeArgs {
   const uint16_t *q, *k, *v;
   const int32_t *idx, *n_sel;
