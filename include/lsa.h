@@ -229,15 +229,17 @@ int32_t lsa_sparse_attn_decode(const lsa_bf16* q, const lsa_bf16* k_cache,
  *   writes them)
  *   dq [B, L, H, D] bf16 out; dk, dv [B, n_k, D] fp32 out (keys no row
  *   selected get 0)
- * The key gradients are summed in the workspace as int64 fixed point (each
- * contribution rounded to a multiple of 2^-32, to nearest even) by integer
- * atomic adds, which are associative: the result does not depend on the order
- * rows are processed, so repeated calls are bit-identical, and the only
- * rounding beyond fp32 arithmetic is that 2^-32 per contribution. Every
- * contribution and every partial sum of one element must stay below 2^31 in
- * magnitude (the int64 range); larger values wrap.
- *   ws: 2 * B * n_k * 128 * 8 bytes (size query with ws = NULL)
- * Supported: D = 128; H in {32, 64, 128}; n_k <= 16777215.
+ * Each (row, key) pair's contribution to dk and dv (a sum over the H heads)
+ * is stored once in bf16; the pairs of each key are listed, and each key's
+ * contributions are summed as int64 fixed point (value * 2^32, exact for
+ * values at or above 2^-24 in magnitude). Integer sums do not depend on the
+ * order of their terms, so repeated calls are bit-identical; the rounding
+ * beyond fp32 arithmetic is the bf16 of each contribution. Every partial sum
+ * of one element must stay below 2^31 in magnitude (the int64 range).
+ * Rows are processed in chunks whose contributions fit 8 GiB.
+ *   ws: query with ws = NULL (about 2 * B * n_k * 1 KiB of accumulators plus
+ *   up to 8 GiB of contributions and 8 bytes per (row, slot) of a chunk)
+ * Supported: D = 128; H in {32, 64, 128}; n_k <= 16777215; B * n_k <= 2^24.
  * Errors: LSA_INVALID_ARG for NULL/misaligned pointers or bad sizes,
  * LSA_UNSUPPORTED for other shapes, LSA_WORKSPACE, LSA_HIP. */
 int32_t lsa_sparse_attn_backward(const lsa_bf16* q, const lsa_bf16* k, const lsa_bf16* v,

@@ -16,14 +16,22 @@
 //   dP^T = V . dO^T             A = V rows from LDS, B = dO^T in registers
 //   P^T  = 2^(S^T sl2 - lse2), dS^T = P^T (dP^T - Delta)      (lane = head)
 //   dQ^T += K^T . dS^T          A = K^T by transposed LDS reads, B = dS^T in place
-//   dV    = P . dO              A = P by transposed reads of the wave's P^T tile
-//   dK    = dS . Q (x scale)    A = dS the same way
-// with Delta = sum_d dO . o per head. dQ stays in registers for the whole
-// row. dK and dV of a block are added into int64 fixed-point accumulators
-// (value * 2^32 rounded to nearest even) by integer atomics: integer addition
-// is associative, so the totals are the same whatever order the rows arrive
-// in, and repeated runs are bit-identical with no float atomics. A last pass
-// converts the totals to fp32.
+// with Delta = sum_d dO . o per head; dQ stays in registers for the whole
+// row. The row's waves then put P^T and dS^T into one LDS tile of all H heads
+// and wave gw takes the dims [128 gw / TW, 128 (gw + 1) / TW) over every head:
+//   dV = P . dO,  dK = dS . Q (x scale)   A = P / dS by transposed tile reads
+// so each (row, key) pair's contribution to dk and dv comes out complete
+// (256 values) and is stored once, in bf16, through an LDS transpose that
+// makes the stores 128-byte rows.
+//
+// The scatter of those contributions to the keys is made order-independent
+// rather than ordered: the pairs of each key are listed (integer counts, an
+// exclusive scan, a fill whose order does not matter), and each key's
+// contributions are summed as int64 fixed point (value * 2^32, exact for
+// bf16 values at or above 2^-24 in magnitude). Integer sums do not depend on
+// the order of their terms, so the totals, and the fp32 gradients converted
+// from them, are bit-identical from run to run, with no float atomics. Rows
+// are processed in chunks so that the contribution buffer stays bounded.
 #include <math.h>
 
 #include <algorithm>
@@ -56,11 +64,6 @@ __device__ __forceinline__ uint64_t to_fixed32(float x) {
   const double hi = __builtin_floor(y * (1.0 / 4294967296.0));
   const double lo = __builtin_fma(hi, -4294967296.0, y);
   return ((uint64_t)(uint32_t)(int32_t)hi << 32) | (uint64_t)(uint32_t)lo;
-}
-
-__device__ __forceinline__ void add_fixed(int64_t* p, float x) {
-  __hip_atomic_fetch_add((unsigned long long*)p, (unsigned long long)to_fixed32(x), __ATOMIC_RELAXED,
-                         __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // K and V rows of one 32-key block staged in registers: thread gt = 64 * gw +
@@ -97,14 +100,19 @@ __device__ __forceinline__ void store(const Stage<TW>& s, char* kb, char* vb, in
   }
 }
 
-// Per-row operands of one wave (heads h0 .. h0 + 31 of the row).
+// Per-row operands of one wave (heads h0 .. h0 + 31 of the row for S^T, dP^T
+// and dQ; every head, over the wave's dims d0 .. d0 + 128/TW - 1, for dK, dV).
+template <int TW>
 struct RowOps {
-  v8bf Qb[8], dOb[8];     // B of S^T / dP^T: lane (g, c) head h0 + c, dims 64g + 8j + {0..7}
-  v8bf Qt[4][2], dOt[4][2];  // B of dK / dV: lane (g, c) dim 32nb + c, heads 16js + 4g + {0..3, 8..11}
-  float dlt, lse2;        // Delta and lse * log2(e) of head h0 + c
+  static constexpr int NT = 4 / TW;  // 32-dim tiles of the wave's dims
+  static constexpr int KS = 2 * TW;  // 16-head steps over all H = 32 TW heads
+  v8bf Qb[8], dOb[8];          // lane (g, c): head h0 + c, dims 64g + 8j + {0..7}
+  v8bf Qt[NT][KS], dOt[NT][KS];  // lane (g, c): dim d0 + 32nt + c, heads 16ks + 4g + {0..3, 8..11}
+  float dlt, lse2;             // Delta and lse * log2(e) of head h0 + c
 };
 
-__device__ __forceinline__ void load_row_ops(const BwdArgs& a, int64_t gq, int h0, RowOps& r) {
+template <int TW>
+__device__ __forceinline__ void load_row_ops(const BwdArgs& a, int64_t gq, int h0, int d0, RowOps<TW>& r) {
   const int l = lane_id(), g = l >> 5, c = l & 31;
   const uint16_t* qr = a.q + gq * a.H * kD;
   const uint16_t* dr = a.d_o + gq * a.H * kD;
@@ -121,25 +129,28 @@ __device__ __forceinline__ void load_row_ops(const BwdArgs& a, int64_t gq, int h
   }
   r.dlt = dl + shfl_xor_f(dl, 32);
 #pragma unroll
-  for (int nb = 0; nb < 4; ++nb)
+  for (int nt = 0; nt < RowOps<TW>::NT; ++nt)
 #pragma unroll
-    for (int js = 0; js < 2; ++js) {
+    for (int ks = 0; ks < RowOps<TW>::KS; ++ks) {
       v8bf x, y;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const int h = h0 + 16 * js + 4 * g + (e & 3) + 8 * (e >> 2);
-        x[e] = __builtin_bit_cast(__bf16, qr[h * kD + 32 * nb + c]);
-        y[e] = __builtin_bit_cast(__bf16, dr[h * kD + 32 * nb + c]);
+        const int h = 16 * ks + 4 * g + (e & 3) + 8 * (e >> 2);
+        x[e] = __builtin_bit_cast(__bf16, qr[h * kD + d0 + 32 * nt + c]);
+        y[e] = __builtin_bit_cast(__bf16, dr[h * kD + d0 + 32 * nt + c]);
       }
-      r.Qt[nb][js] = x;
-      r.dOt[nb][js] = y;
+      r.Qt[nt][ks] = x;
+      r.dOt[nt][ks] = y;
     }
   r.lse2 = a.lse[gq * a.H + h0 + c] * kLog2e;
 }
 
-// One 32-key block: lane c (and c + 32) holds the position of key c.
-__device__ __forceinline__ void bwd_block(const BwdArgs& a, const RowOps& r, const char* kb, const char* vb,
-                                          char* ptile, char* stile, int pos, int b, v16f (&dQ)[4]) {
+// Part one of a 32-key block: lane c (and c + 32) holds the position of key
+// c. dQ is updated; P^T and dS^T of the wave's heads go to the row's tiles.
+template <int TW>
+__device__ __forceinline__ void bwd_block_rows(const BwdArgs& a, const RowOps<TW>& r, const char* kb,
+                                               const char* vb, char* ptile, char* stile, int h0, int pos,
+                                               v16f (&dQ)[4]) {
   const int l = lane_id(), g = l >> 5, c = l & 31;
   const bool valid = (unsigned)pos < (unsigned)a.n_k;
   const uint32_t vmask = (uint32_t)__ballot(valid);
@@ -170,40 +181,57 @@ __device__ __forceinline__ void bwd_block(const BwdArgs& a, const RowOps& r, con
 #pragma unroll
     for (int js = 0; js < 2; ++js)
       dQ[mb] = mfma_bf16_32x32x16(read_tr(kb + kt_off + 16 * js * kRowB + 64 * mb, kRowB), Sb[js], dQ[mb]);
-  // the P^T and dS^T tiles of this wave: row = head c, 8-byte runs of keys
-  // 16js + 4g + {0..3} and 16js + 8 + 4g + {0..3}
+  // tile rows h0 + c (head), 8-byte runs of keys 16js + 4g + {0..3} and
+  // 16js + 8 + 4g + {0..3}
 #pragma unroll
   for (int js = 0; js < 2; ++js) {
     const v4u pu = __builtin_bit_cast(v4u, Pb[js]), su = __builtin_bit_cast(v4u, Sb[js]);
-    char* pp = ptile + c * kTileP + (16 * js + 4 * g) * 2;
-    char* sp = stile + c * kTileP + (16 * js + 4 * g) * 2;
+    char* pp = ptile + (h0 + c) * kTileP + (16 * js + 4 * g) * 2;
+    char* sp = stile + (h0 + c) * kTileP + (16 * js + 4 * g) * 2;
     *(v2u*)pp = v2u{pu[0], pu[1]};
     *(v2u*)(pp + 16) = v2u{pu[2], pu[3]};
     *(v2u*)sp = v2u{su[0], su[1]};
     *(v2u*)(sp + 16) = v2u{su[2], su[3]};
   }
-  // the block's keys in accumulator row order, for the scatter
-  int pk[16];
-#pragma unroll
-  for (int i = 0; i < 16; ++i) pk[i] = __shfl(pos, 8 * (i >> 2) + 4 * g + (i & 3), 64);
+}
+
+// Part two, once every wave of the row has written its tile rows: the
+// block's dk and dv contributions over all heads for the wave's dims,
+// through the wave's transpose buffer xb ([32 keys][128 / TW dims] bf16) to
+// 16-byte stores of contrib rows cb + key (keys >= cnt are not stored).
+template <int TW>
+__device__ __forceinline__ void bwd_block_keys(const BwdArgs& a, const RowOps<TW>& r, const char* ptile,
+                                               const char* stile, char* xb, int d0, uint16_t* cb, int cnt) {
+  constexpr int NT = RowOps<TW>::NT, KS = RowOps<TW>::KS, ND = 128 / TW;
+  constexpr int XP = 2 * ND + 16;  // transpose buffer pitch (bytes)
+  const int l = lane_id(), g = l >> 5, c = l & 31;
   const int t_off = tr_lane_off(kTileP);
-  int64_t* dvb = a.dv_acc + (int64_t)b * a.n_k * kD;
-  int64_t* dkb = a.dk_acc + (int64_t)b * a.n_k * kD;
-  // dV = P . dO, then dK = dS . Q: lane (g, c) holds dim 32nb + c of keys pk[i]
 #pragma unroll
-  for (int which = 0; which < 2; ++which) {
-    const char* tile = which == 0 ? ptile : stile;
-    const v8bf A0 = read_tr(tile + t_off, kTileP), A1 = read_tr(tile + t_off + 16 * kTileP, kTileP);
-    int64_t* dst = which == 0 ? dvb : dkb;
-    const float mul = which == 0 ? 1.f : a.scale;
+  for (int which = 0; which < 2; ++which) {  // 0: dk (dS . Q x scale), 1: dv (P . dO)
+    const char* tile = which == 0 ? stile : ptile;
+    v8bf A[KS];
 #pragma unroll
-    for (int nb = 0; nb < 4; ++nb) {
+    for (int ks = 0; ks < KS; ++ks) A[ks] = read_tr(tile + t_off + 16 * ks * kTileP, kTileP);
+    const float mul = which == 0 ? a.scale : 1.f;
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
       v16f acc = v16f{};
-      acc = mfma_bf16_32x32x16(A0, which == 0 ? r.dOt[nb][0] : r.Qt[nb][0], acc);
-      acc = mfma_bf16_32x32x16(A1, which == 0 ? r.dOt[nb][1] : r.Qt[nb][1], acc);
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+        acc = mfma_bf16_32x32x16(A[ks], which == 0 ? r.Qt[nt][ks] : r.dOt[nt][ks], acc);
+      // lane (g, c): dim 32nt + c of the wave's dims, entry i key 8(i/4) + 4g + i%4
 #pragma unroll
       for (int i = 0; i < 16; ++i)
-        if ((unsigned)pk[i] < (unsigned)a.n_k) add_fixed(dst + (int64_t)pk[i] * kD + 32 * nb + c, acc[i] * mul);
+        *(__bf16*)(xb + (8 * (i >> 2) + 4 * g + (i & 3)) * XP + 2 * (32 * nt + c)) = (__bf16)(acc[i] * mul);
+    }
+    // 32 keys x ND dims back as 16-byte pieces: piece q is key q / (ND / 8),
+    // dims 8 (q % (ND / 8)) .. + 7
+#pragma unroll
+    for (int u = 0; u < ND / 16; ++u) {
+      const int q = 64 * u + l;
+      const int key = q / (ND / 8), part = q % (ND / 8);
+      const v4u x = *(const v4u*)(xb + key * XP + 16 * part);
+      if (key < cnt) *(v4u*)(cb + (int64_t)key * 256 + 128 * which + d0 + 8 * part) = x;
     }
   }
 }
@@ -211,27 +239,30 @@ __device__ __forceinline__ void bwd_block(const BwdArgs& a, const RowOps& r, con
 template <int TW>
 __global__ __launch_bounds__(256) void attn_bwd_kernel(BwdArgs a) {
   constexpr int RW = 4 / TW;  // query rows per workgroup
+  constexpr int H = 32 * TW;
+  constexpr int XB = 32 * (2 * (128 / TW) + 16);  // one wave's transpose buffer
   __shared__ __attribute__((aligned(16))) char lds_kv[RW * 2 * kBlkB];
-  __shared__ __attribute__((aligned(16))) char lds_t[4 * 2 * kTileB];
+  __shared__ __attribute__((aligned(16))) char lds_t[RW * 2 * H * kTileP];
+  __shared__ __attribute__((aligned(16))) char lds_x[4 * XB];
   const int wv = wave_id(), gw = wv % TW, sr = wv / TW;
-  // each XCD walks a contiguous range of rows (the grid is a multiple of 8)
+  // each XCD walks a contiguous range of the chunk's rows (the grid is a
+  // multiple of 8)
   const int64_t per = gridDim.x / 8, bx = blockIdx.x;
   const int64_t tile = (bx % 8) * per + bx / 8;
-  const int64_t rows = (int64_t)a.B * a.L;
-  const int64_t gq0 = tile * RW;
-  if (gq0 >= rows) return;  // the same for every wave of the workgroup
-  const bool active = gq0 + sr < rows;
-  const int64_t gq = active ? gq0 + sr : rows - 1;
+  const int64_t gq0 = a.r0 + tile * RW;
+  if (gq0 >= a.r1) return;  // the same for every wave of the workgroup
+  const bool active = gq0 + sr < a.r1;
+  const int64_t gq = active ? gq0 + sr : a.r1 - 1;
   const int b = (int)(gq / a.L);
-  const int l = lane_id(), g = l >> 5, c = l & 31;
-  const int h0 = gw * 32;
+  const int c = lane_id() & 31;
+  const int h0 = gw * 32, d0 = gw * (128 / TW);
   int nmax = 0;
 #pragma unroll
   for (int r = 0; r < RW; ++r)
-    if (gq0 + r < rows) nmax = max(nmax, min(max(a.n_sel[gq0 + r], 0), a.K_tot));
+    if (gq0 + r < a.r1) nmax = max(nmax, min(max(a.n_sel[gq0 + r], 0), a.K_tot));
   const int n = active ? min(max(a.n_sel[gq], 0), a.K_tot) : 0;
-  RowOps ro;
-  load_row_ops(a, gq, h0, ro);
+  RowOps<TW> ro;
+  load_row_ops<TW>(a, gq, h0, d0, ro);
   const int32_t* ids = a.idx + gq * a.K_tot;
   const uint16_t* K = a.k + (int64_t)b * a.n_k * kD;
   const uint16_t* V = a.v + (int64_t)b * a.n_k * kD;
@@ -239,8 +270,10 @@ __global__ __launch_bounds__(256) void attn_bwd_kernel(BwdArgs a) {
   const __amdgpu_buffer_rsrc_t vr = uniform_rsrc(V, (uint32_t)a.n_k * (uint32_t)(kD * 2));
   char* kb = lds_kv + sr * 2 * kBlkB;
   char* vb = kb + kBlkB;
-  char* ptile = lds_t + wv * 2 * kTileB;
-  char* stile = ptile + kTileB;
+  char* ptile = lds_t + sr * 2 * H * kTileP;
+  char* stile = ptile + H * kTileP;
+  char* xb = lds_x + wv * XB;
+  uint16_t* crow = a.contrib + (gq - a.r0) * a.K_tot * 256;
   v16f dQ[4];
 #pragma unroll
   for (int mb = 0; mb < 4; ++mb) dQ[mb] = v16f{};
@@ -249,16 +282,20 @@ __global__ __launch_bounds__(256) void attn_bwd_kernel(BwdArgs a) {
   Stage<TW> stg;
   gather<TW>(kr, vr, pos, gw, stg);
   for (int bi = 0; bi < nblk; ++bi) {
-    __syncthreads();  // the previous block's K / V rows are no longer read
+    __syncthreads();  // the previous block's K / V rows and tiles are no longer read
     store<TW>(stg, kb, vb, gw);
     const int pcur = pos;
     const int s1 = 32 * (bi + 1) + c;
     pos = s1 < n ? ids[s1] : -1;
     gather<TW>(kr, vr, pos, gw, stg);  // the next block's rows load during this one
     __syncthreads();
-    if (32 * bi < n) bwd_block(a, ro, kb, vb, ptile, stile, pcur, b, dQ);
+    const bool live = 32 * bi < n;  // the same for the TW waves of the row
+    if (live) bwd_block_rows<TW>(a, ro, kb, vb, ptile, stile, h0, pcur, dQ);
+    __syncthreads();  // the row's tiles are complete
+    if (live) bwd_block_keys<TW>(a, ro, ptile, stile, xb, d0, crow + (int64_t)32 * bi * 256, min(32, n - 32 * bi));
   }
   if (!active) return;
+  const int g = lane_id() >> 5;
   uint16_t* dqrow = a.dq + (gq * a.H + h0 + c) * kD;
 #pragma unroll
   for (int mb = 0; mb < 4; ++mb)
@@ -269,6 +306,160 @@ __global__ __launch_bounds__(256) void attn_bwd_kernel(BwdArgs a) {
       const uint32_t w1 = pack_bf16x2(D[4 * i4 + 2] * a.scale, D[4 * i4 + 3] * a.scale);
       *(v2u*)(dqrow + 32 * mb + 8 * i4 + 4 * g) = v2u{w0, w1};
     }
+}
+
+// ---------------------------------------------------------------- scatter
+// Pairs of the chunk: p = (row - r0) * K_tot + slot, for slots below the
+// row's n_sel holding a position in [0, n_k); key = b * n_k + position.
+__device__ __forceinline__ int pair_key(const ScatterArgs& a, int64_t p) {
+  const int64_t t = a.r0 + p / a.K_tot;
+  const int j = (int)(p % a.K_tot);
+  const int n = min(max(a.n_sel[t], 0), a.K_tot);
+  if (j >= n) return -1;
+  const int s = a.idx[t * a.K_tot + j];
+  if ((unsigned)s >= (unsigned)a.n_k) return -1;
+  return (int)(t / a.L) * a.n_k + s;
+}
+
+__global__ __launch_bounds__(256) void bwd_count_kernel(ScatterArgs a) {
+  const int64_t np = (a.r1 - a.r0) * a.K_tot;
+  for (int64_t p = (int64_t)blockIdx.x * 256 + threadIdx.x; p < np; p += (int64_t)gridDim.x * 256) {
+    const int key = pair_key(a, p);
+    if (key >= 0) atomicAdd(&a.cnt[key], 1);
+  }
+}
+
+// Exclusive scan of cnt into cur, in blocks of kScanBlock (1024 threads x 4);
+// tot gets each block's sum.
+__global__ __launch_bounds__(1024) void bwd_scan_blocks_kernel(ScatterArgs a) {
+  __shared__ int32_t wsum[16];
+  const int base = blockIdx.x * kScanBlock + threadIdx.x * 4;
+  int v[4], s = 0;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    v[e] = base + e < a.n_keys ? a.cnt[base + e] : 0;
+    s += v[e];
+  }
+  const int incl = wave_incl_scan(s);
+  if (lane_id() == 63) wsum[wave_id()] = incl;
+  __syncthreads();
+  int off = 0, total = 0;
+#pragma unroll
+  for (int w = 0; w < 16; ++w) {
+    off += w < wave_id() ? wsum[w] : 0;
+    total += wsum[w];
+  }
+  int run = off + incl - s;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    if (base + e < a.n_keys) a.cur[base + e] = run;
+    run += v[e];
+  }
+  if (threadIdx.x == 0) a.tot[blockIdx.x] = total;
+}
+
+// Exclusive scan of the block sums (one workgroup; at most kScanBlock).
+__global__ __launch_bounds__(1024) void bwd_scan_totals_kernel(ScatterArgs a, int nb) {
+  __shared__ int32_t wsum[16];
+  const int base = threadIdx.x * 4;
+  int v[4], s = 0;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    v[e] = base + e < nb ? a.tot[base + e] : 0;
+    s += v[e];
+  }
+  const int incl = wave_incl_scan(s);
+  if (lane_id() == 63) wsum[wave_id()] = incl;
+  __syncthreads();
+  int off = 0;
+#pragma unroll
+  for (int w = 0; w < 16; ++w) off += w < wave_id() ? wsum[w] : 0;
+  int run = off + incl - s;
+  __syncthreads();  // every block sum is read before it is replaced
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    if (base + e < nb) a.tot[base + e] = run;
+    run += v[e];
+  }
+}
+
+__global__ __launch_bounds__(256) void bwd_scan_add_kernel(ScatterArgs a) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i < a.n_keys) a.cur[i] += a.tot[i / kScanBlock];
+}
+
+// Each pair takes a slot in its key's segment (the order within a segment
+// varies from run to run; the sums below do not depend on it).
+__global__ __launch_bounds__(256) void bwd_fill_kernel(ScatterArgs a) {
+  const int64_t np = (a.r1 - a.r0) * a.K_tot;
+  for (int64_t p = (int64_t)blockIdx.x * 256 + threadIdx.x; p < np; p += (int64_t)gridDim.x * 256) {
+    const int key = pair_key(a, p);
+    if (key < 0) continue;
+    const int slot = atomicAdd(&a.cur[key], 1);
+    a.lkey[slot] = key;
+    a.lpair[slot] = (int)p;
+  }
+}
+
+// bf16 bits to int64 fixed point (value * 2^32)
+__device__ __forceinline__ uint64_t bf16_fixed(uint32_t bits16) {
+  return to_fixed32(__uint_as_float(bits16 << 16));
+}
+
+__device__ __forceinline__ void flush_key(const ScatterArgs& a, int key, const uint64_t (&acc)[4]) {
+  const int l = lane_id();
+  int64_t* dst = (l < 32 ? a.dk_acc : a.dv_acc) + (int64_t)key * kD + 4 * (l & 31);
+#pragma unroll
+  for (int e = 0; e < 4; ++e)
+    __hip_atomic_fetch_add((unsigned long long*)(dst + e), (unsigned long long)acc[e], __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Wave w sums the listed entries [w * kReduceRun, (w + 1) * kReduceRun) of
+// the total (cur[n_keys - 1] after the fill): lane l keeps the 4 values at
+// 4l of each contribution (lanes 0-31 dk, 32-63 dv) as int64 and adds them
+// to the accumulators whenever the key changes and at the end. Keys are
+// contiguous in the list, so a wave flushes once per key it meets.
+constexpr int kReduceRun = 1024;
+
+__global__ __launch_bounds__(256) void bwd_reduce_kernel(ScatterArgs a) {
+  const int total = a.cur[a.n_keys - 1];  // the fill advanced every segment to its end
+  const int64_t w = (int64_t)blockIdx.x * 4 + wave_id();
+  const int e0 = (int)min<int64_t>(w * kReduceRun, total), e1 = (int)min<int64_t>(e0 + (int64_t)kReduceRun, total);
+  if (e0 >= e1) return;
+  const int l = lane_id();
+  uint64_t acc[4] = {0, 0, 0, 0};
+  int ck = -1;
+  for (int b0 = e0; b0 < e1; b0 += 64) {
+    const int m = min(64, e1 - b0);
+    const int lk = l < m ? a.lkey[b0 + l] : -1;
+    const int lp = l < m ? a.lpair[b0 + l] : 0;
+    for (int i0 = 0; i0 < m; i0 += 8) {
+      v2u x[8];
+      int kk[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        kk[u] = __shfl(lk, i0 + u, 64);
+        const int pr = __shfl(lp, i0 + u, 64);
+        x[u] = i0 + u < m ? *(const v2u*)(a.contrib + (int64_t)pr * 256 + 4 * l) : v2u{0u, 0u};
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        if (i0 + u >= m) break;
+        if (kk[u] != ck) {
+          if (ck >= 0) flush_key(a, ck, acc);
+          ck = kk[u];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[e] = 0;
+        }
+        acc[0] += bf16_fixed(x[u][0] & 0xffffu);
+        acc[1] += bf16_fixed(x[u][0] >> 16);
+        acc[2] += bf16_fixed(x[u][1] & 0xffffu);
+        acc[3] += bf16_fixed(x[u][1] >> 16);
+      }
+    }
+  }
+  if (ck >= 0) flush_key(a, ck, acc);
 }
 
 __global__ __launch_bounds__(256) void fill_zero_kernel(v4u* p, size_t n16) {
@@ -297,12 +488,39 @@ hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t st) {
 
 hipError_t launch_attn_bwd(const BwdArgs& a, hipStream_t st) {
   const int TW = a.H / 32, RW = 4 / TW;
-  const int64_t wgs = ((int64_t)a.B * a.L + RW - 1) / RW;
+  const int64_t wgs = (a.r1 - a.r0 + RW - 1) / RW;
   const dim3 grid((unsigned)((wgs + 7) / 8 * 8));
   KernelTimer kt("attn_bwd_kernel", st);
   if (TW == 1) hipLaunchKernelGGL(attn_bwd_kernel<1>, grid, dim3(256), 0, st, a);
   else if (TW == 2) hipLaunchKernelGGL(attn_bwd_kernel<2>, grid, dim3(256), 0, st, a);
   else hipLaunchKernelGGL(attn_bwd_kernel<4>, grid, dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_scatter(const ScatterArgs& a, hipStream_t st) {
+  if (a.n_keys <= 0 || a.n_keys > kMaxScanKeys) return hipErrorInvalidValue;
+  hipError_t e = launch_fill_zero(a.cnt, ((size_t)a.n_keys * 4 + 15) / 16 * 16, st);
+  if (e != hipSuccess) return e;
+  const int64_t np = (a.r1 - a.r0) * a.K_tot;
+  const unsigned gp = (unsigned)std::min<int64_t>((np + 255) / 256, 256 * 64);
+  const int nb = (a.n_keys + kScanBlock - 1) / kScanBlock;
+  {
+    KernelTimer kt("bwd_count_kernel", st);
+    hipLaunchKernelGGL(bwd_count_kernel, dim3(gp), dim3(256), 0, st, a);
+  }
+  {
+    KernelTimer kt("bwd_scan_kernel", st);
+    hipLaunchKernelGGL(bwd_scan_blocks_kernel, dim3(nb), dim3(1024), 0, st, a);
+    hipLaunchKernelGGL(bwd_scan_totals_kernel, dim3(1), dim3(1024), 0, st, a, nb);
+    hipLaunchKernelGGL(bwd_scan_add_kernel, dim3((a.n_keys + 255) / 256), dim3(256), 0, st, a);
+  }
+  {
+    KernelTimer kt("bwd_fill_kernel", st);
+    hipLaunchKernelGGL(bwd_fill_kernel, dim3(gp), dim3(256), 0, st, a);
+  }
+  KernelTimer kt("bwd_reduce_kernel", st);
+  const int64_t waves = (np + kReduceRun - 1) / kReduceRun;
+  hipLaunchKernelGGL(bwd_reduce_kernel, dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 

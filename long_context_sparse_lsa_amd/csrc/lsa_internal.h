@@ -120,24 +120,42 @@ struct PrefillArgs {
 };
 hipError_t launch_attn_prefill(const PrefillArgs& a, hipStream_t st);
 
-// Sparse attention backward. Row t of sequence b attends over idx[b, t, :n_sel]
-// (unique positions); o and lse are the forward's outputs for the same rows,
-// d_o the gradient of the loss with respect to o. dq (bf16) is written per
-// row; the key gradients are summed into int64 fixed-point accumulators
-// (value * 2^32, rounded to nearest even) dk_acc / dv_acc [B, n_k, 128],
-// which must start at zero, and converted by launch_attn_bwd_finish.
+// Sparse attention backward, in row chunks. Row t of sequence b attends over
+// idx[b, t, :n_sel] (distinct positions); o and lse are the forward's outputs
+// for the same rows, d_o the gradient of the loss with respect to o. Phase 1
+// (launch_attn_bwd) writes dq (bf16) of the chunk's rows [r0, r1) of the
+// B * L rows and, for every (row, list slot) pair, the pair's contribution to
+// the key's gradients: contrib[(row - r0) * K_tot + slot] holds 256 bf16, dk
+// (scaled) then dv. Phase 2 (launch_bwd_scatter) lists the pairs of each key
+// (counts, exclusive scan, fill) and sums each key's contributions as int64
+// fixed point (value * 2^32) into dk_acc / dv_acc [B * n_k, 128], which start
+// at zero before the first chunk; launch_attn_bwd_finish converts them.
 struct BwdArgs {
   const uint16_t *q, *k, *v, *o, *d_o;
   const float* lse;
   const int32_t *idx, *n_sel;
   int B, L, n_k, H, K_tot;
-  float sl2;    // scale * log2(e)
+  float sl2;  // scale * log2(e)
   float scale;
   uint16_t* dq;
+  int64_t r0, r1;
+  uint16_t* contrib;
+};
+struct ScatterArgs {
+  const int32_t *idx, *n_sel;
+  int L, n_k, K_tot;
+  int64_t r0, r1;
+  int n_keys;               // B * n_k
+  int32_t *cnt, *cur, *tot;  // [n_keys], [n_keys], [ceil(n_keys / 4096)]
+  int32_t *lkey, *lpair;    // [(r1 - r0) * K_tot]
+  const uint16_t* contrib;
   int64_t *dk_acc, *dv_acc;
 };
+constexpr int kScanBlock = 4096;
+constexpr int kMaxScanKeys = kScanBlock * kScanBlock;
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t st);
 hipError_t launch_attn_bwd(const BwdArgs& a, hipStream_t st);
+hipError_t launch_bwd_scatter(const ScatterArgs& a, hipStream_t st);
 hipError_t launch_attn_bwd_finish(const int64_t* acc, float* out, size_t n, hipStream_t st);
 
 // Warm-up KL operator: per row, KL(head-averaged attention distribution over
