@@ -42,6 +42,9 @@ def parse():
     p.add_argument("--steps", type=int, default=5)
     p.add_argument("--warmup", type=int, default=2)
     p.add_argument("--config", default="c5", choices=["c1", "c2", "c3", "c4", "c5"])
+    p.add_argument("--op", default="path", choices=["path", "backward", "kl"],
+                   help="path: the hot path of the workload (default); backward / kl: the training "
+                        "operators on a prefill workload's selected lists")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=10.0, help="time budget of the oracle sample")
     p.add_argument("--copy-probe", action="store_true",
@@ -109,7 +112,9 @@ def cpu_threads():
 
 
 KERNELS = ("index_prefill_kernel", "index_decode_kernel", "index_score_kernel", "select_stage_a",
-           "select_stage_b", "attn_prefill_kernel", "attn_decode_partial", "attn_decode_merge")
+           "select_stage_b", "attn_prefill_kernel", "attn_decode_partial", "attn_decode_merge",
+           "fill_zero_kernel", "attn_bwd_kernel", "bwd_count_kernel", "bwd_scan_kernel", "bwd_fill_kernel",
+           "bwd_reduce_kernel", "attn_bwd_finish_kernel", "kl_warmup_kernel")
 
 
 def kernel_times(L, torch, step, steps, park=False):
@@ -293,6 +298,94 @@ def run_prefill(args, wl, torch):
     return out
 
 
+def run_training_op(args, wl, torch):
+    """One training operator on a prefill workload: the selection and the
+    forward (with lse) run once, untimed; a step is one call of the
+    deterministic backward (--op backward) or of the warm-up KL operator
+    (--op kl) over every row of one layer."""
+    import numpy as np
+    from long_context_sparse_lsa_amd import _lib as L
+    from long_context_sparse_lsa_amd import synth
+    dev = "cuda"
+    q_idx, k_idx, w = synth.indexer_inputs(wl, dev)
+    q, k, v = synth.attention_inputs(wl, 0, dev)
+    idx, n_sel = L.lsa_select_topk(q_idx, k_idx, w, wl.n_sink, wl.n_window, wl.k_dyn, q_off=0)
+    o, lse = L.lsa_sparse_attn_prefill(q, k, v, idx, n_sel, want_lse=True)
+    del q_idx
+    if args.op == "backward":
+        d_o = synth.bf16_normal(q.shape, synth.seed_of(wl.name, "d_o"), dev)
+
+        def step():
+            return L.lsa_sparse_attn_backward(q, k, v, idx, n_sel, o, lse, d_o)
+    else:
+        # logits: seeded N(0, 1) per listed key (the indexer's own logits in training)
+        g = torch.Generator(device=dev)
+        g.manual_seed(synth.seed_of(wl.name, "logits"))
+        logits = torch.randn(idx.shape, generator=g, device=dev, dtype=torch.float32)
+
+        def step():
+            return L.lsa_kl_warmup(q, k, idx, n_sel, lse, logits)
+    torch.cuda.synchronize()
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    ms_step = (time.perf_counter() - t0) * 1e3 / args.steps
+    kt = kernel_times(L, torch, step, args.steps)
+    pairs = float(n_sel.sum().item())
+    if args.op == "backward":
+        # five products per (row, key) pair and head: S, dP, dQ, dK, dV
+        work = {"attn_bwd_kernel": ("mfma", 10.0 * wl.H * wl.D * pairs, PEAK_BF16_TFLOPS, "TFLOP/s"),
+                # the bf16 contributions the reduce reads (512 B per pair)
+                "bwd_reduce_kernel": ("hbm", 512.0 * pairs, PEAK_HBM_GBS, "GB/s")}
+        metric = "LSA sparse attention backward tokens/s"
+    else:
+        work = {"kl_warmup_kernel": ("mfma", 2.0 * wl.H * wl.D * pairs, PEAK_BF16_TFLOPS, "TFLOP/s")}
+        metric = "LSA warm-up KL tokens/s"
+    name = dominant(kt, work)
+    bound, wk, peak, unit = work[name]
+    roof = roofline(bound, name, wk, kt, peak, unit)
+    roof["traffic"] = measured_traffic(wl.name + "_" + args.op, name)
+    out = {
+        "metric": metric, "value": round(wl.L * wl.B / (ms_step * 1e-3), 1), "unit": "tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (the workload's seeded inputs; d_o / logits bf16 / fp32 N(0,1))",
+        "config": {"workload": wl.name + "_" + args.op, "global_batch": wl.B, "seq_len": wl.L, "H": wl.H,
+                   "D": wl.D, "K_tot": wl.K_tot, "selected_pairs": int(pairs), "parallelism": "none"},
+        "parts": {"kernels": kernel_parts(kt)},
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        import oracle as O
+        rng = np.random.default_rng(7)
+        qn, kn, vn = (x[0].cpu() for x in (q, k, v))
+        In, Nn = idx[0].cpu().numpy(), n_sel[0].cpu().numpy()
+        kf, vf = kn.double().numpy(), vn.double().numpy()
+        dof = (d_o[0].cpu().double().numpy() if args.op == "backward" else None)
+        lgn = logits[0].cpu().double().numpy() if args.op == "kl" else None
+        n = 0
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < args.cpu_seconds:
+            t = int(rng.integers(wl.K_tot, wl.L))
+            sel = In[t, :Nn[t]]
+            qt = qn[t].double().numpy()
+            if args.op == "backward":
+                O.attend_backward(qt, kf, vf, sel, wl.scale, dof[t])
+            else:
+                O.kl_warmup_row(qt, kf, sel, wl.scale, lgn[t, :Nn[t]])
+            n += 1
+        dt = time.perf_counter() - t0
+        out["cpu_baseline"] = {"value": round(n / dt, 3), "unit": "tokens/s", "cores": cpu_threads(),
+                               "kind": "oracle",
+                               "sample": f"{n} rows drawn uniformly from [{wl.K_tot}, {wl.L}) in {dt:.1f} s; "
+                                         f"each: the oracle's float64 {args.op} of the row"}
+    return out
+
+
 def decode_cpu_baseline(wl, q_idx, k_idx, w, q, kc, vc, seconds, blk_summary):
     """The oracle on whole sequences of the decode step until `seconds` pass."""
     import numpy as np
@@ -439,7 +532,13 @@ def main():
         sys.exit(1)
     L.load()
     wl = configs.BY_ID[args.config]
-    out = run_prefill(args, wl, torch) if wl.kind == "prefill" else run_decode(args, wl, torch)
+    if args.op != "path":
+        if wl.kind != "prefill":
+            print("--op backward / kl run on a prefill workload (c1, c2, c5)", file=sys.stderr)
+            sys.exit(2)
+        out = run_training_op(args, wl, torch)
+    else:
+        out = run_prefill(args, wl, torch) if wl.kind == "prefill" else run_decode(args, wl, torch)
     roof = out["roofline"]
     if roof["bound"] == "mfma":
         # the rate the matrix cores sustain for this dtype on this GPU in this
