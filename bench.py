@@ -45,6 +45,9 @@ def parse():
     p.add_argument("--op", default="path", choices=["path", "backward", "kl"],
                    help="path: the hot path of the workload (default); backward / kl: the training "
                         "operators on a prefill workload's selected lists")
+    p.add_argument("--fused", action="store_true",
+                   help="HI decode (c4): the step as one fused call (lsa_hier_decode_step) instead of "
+                        "lsa_hier_select + lsa_sparse_attn_decode")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=10.0, help="time budget of the oracle sample")
     p.add_argument("--copy-probe", action="store_true",
@@ -114,7 +117,7 @@ def cpu_threads():
 KERNELS = ("index_prefill_kernel", "index_decode_kernel", "index_score_kernel", "select_stage_a",
            "select_stage_b", "attn_prefill_kernel", "attn_decode_partial", "attn_decode_merge",
            "fill_zero_kernel", "attn_bwd_kernel", "bwd_count_kernel", "bwd_scan_kernel", "bwd_fill_kernel",
-           "bwd_reduce_kernel", "attn_bwd_finish_kernel", "kl_warmup_kernel")
+           "bwd_reduce_kernel", "attn_bwd_finish_kernel", "kl_warmup_kernel", "hi_step_kernel")
 
 
 def kernel_times(L, torch, step, steps, park=False):
@@ -416,11 +419,16 @@ def run_decode(args, wl, torch):
     q, kc, vc = synth.attention_inputs(wl, 0, dev)
     q1 = q_idx[:, None].contiguous()
     kblk = L.lsa_block_summary(k_idx, wl.blk) if wl.blk else None
+    step_ws = torch.empty(64 << 20, dtype=torch.uint8, device=dev) if (wl.blk and args.fused) else None
     torch.cuda.synchronize()
     timer = EventTimer(torch)
     N = wl.L
 
     def step(tm):
+        if wl.blk and args.fused:
+            # the whole step in one fused call (its counters in a kept workspace)
+            return tm("step", L.lsa_hier_decode_step, q_idx, k_idx, kblk, w, q, kc, vc, wl.blk, wl.n_blk_recall,
+                      wl.n_sink, wl.n_window, wl.k_dyn, n_split=wl.n_split, ws=step_ws)[2]
         if wl.blk:
             idx, n_sel = tm("select", L.lsa_hier_select, q_idx, k_idx, kblk, w, wl.blk, wl.n_blk_recall,
                             wl.n_sink, wl.n_window, wl.k_dyn)
@@ -443,6 +451,7 @@ def run_decode(args, wl, torch):
     us_eager = (time.perf_counter() - t0) * 1e6 / args.steps
     sel_ms, _ = timer.ms("select")
     attn_ms, _ = timer.ms("attn")
+    fused_ms, _ = timer.ms("step")
     # the timed steps: one decode step captured once as a HIP graph and
     # replayed, as a serving loop runs a fixed-shape step
     graph = torch.cuda.CUDAGraph()
@@ -484,7 +493,8 @@ def run_decode(args, wl, torch):
     # algorithmic bytes of each kernel in one step: the indexer keys it scans,
     # the scores the selection reads, the K/V rows and q the attention reads
     n_scored = (N // wl.blk + wl.n_blk_recall * wl.blk) if wl.blk else N
-    work = {"index_decode_kernel": ("hbm", idx_bytes, PEAK_HBM_GBS, "GB/s"),
+    work = {"hi_step_kernel": ("hbm", step_bytes, PEAK_HBM_GBS, "GB/s"),
+            "index_decode_kernel": ("hbm", idx_bytes, PEAK_HBM_GBS, "GB/s"),
             "select_stage_a": ("hbm", 4.0 * wl.B * n_scored, PEAK_HBM_GBS, "GB/s"),
             "attn_decode_partial": ("hbm", kv_bytes + qo_bytes // 2, PEAK_HBM_GBS, "GB/s")}
     name = dominant(kt, work)
@@ -498,11 +508,12 @@ def run_decode(args, wl, torch):
         "ms_per_step": round(us_step / 1e3, 5),
         "higher_is_better": False, "scaling": "weak", "vs_baseline": None,
         "dtype": "int8+bf16", "data": "synthetic (seeded int8 U[-16,15] indexer, bf16 N(0,1) q and caches)",
-        "config": {"workload": wl.name, "global_batch": wl.B, "context": N, "n_q": wl.n_q, "H": wl.H,
-                   "K_tot": K_tot, "n_split": wl.n_split, "hier_blk": wl.blk, "launch": "hip_graph_replay",
-                   "parallelism": "none"},
+        "config": {"workload": wl.name + ("_fused" if (wl.blk and args.fused) else ""), "global_batch": wl.B,
+                   "context": N, "n_q": wl.n_q, "H": wl.H, "K_tot": K_tot, "n_split": wl.n_split,
+                   "hier_blk": wl.blk, "launch": "hip_graph_replay", "parallelism": "none"},
         "parts": {"eager_us_per_step": round(us_eager, 2), "cold_cache_us_per_step": round(us_cold, 2),
                   "select_us": round(sel_ms * 1e3, 2), "attn_us": round(attn_ms * 1e3, 2),
+                  "fused_step_us": round(fused_ms * 1e3, 2),
                   "step_bytes": step_bytes,
                   "step_hbm_frac": round(step_bytes / (us_step * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
                   "kernels": kernel_parts(kt)},

@@ -165,6 +165,33 @@ int32_t lsa_hier_select_ragged(const int8_t* q_idx, const int8_t* k_idx, const i
                                lsa_select_cfg cfg, int32_t* idx, int32_t* n_sel, void* ws,
                                size_t ws_bytes, size_t* ws_needed, void* stream);
 
+/* Fused HI decode step (a "super kernel": LongCat-2.0 release article, section
+ * "面向国产算力芯片的优化" on fusing small operators into one kernel; the 1.6T
+ * write-up, section "② 设备层"): the block recall, token selection and split-KV
+ * attention of one decode step, with the query at position n_k - 1 of each
+ * sequence, in two launches (a tiny counter fill and one persistent kernel
+ * whose workgroups take the step's work items in dependency order). The
+ * results equal lsa_hier_select followed by lsa_sparse_attn_decode (n_q = 1,
+ * n_idx = 1) bit for bit; idx / n_sel are written as lsa_hier_select writes
+ * them, so later layers can reuse them (CLI).
+ *   q_idx [B, H_I, d_I] int8, k_idx [B, n_k, d_I], k_blk [B, ceil(n_k / blk),
+ *   d_I] (lsa_block_summary), w [H_I] host; q [B, 1, H, D] bf16, k_cache /
+ *   v_cache [B, n_k, D] bf16
+ *   idx [B, K_tot], n_sel [B] out; o [B, 1, H, D] bf16 out; lse [B, 1, H] or NULL
+ * Supported: H_I = 64, d_I = 128, H = 64, D = 128, one query row per
+ * sequence, n_split in [1, 8], blk a multiple of 32 in [32, 1024], at most
+ * 16384 eligible blocks and n_blk_recall * blk <= 16384, n_k > K_tot (shorter
+ * contexts: lsa_hier_select); LSA_UNSUPPORTED otherwise. The workspace's first
+ * 256 bytes hold the step's counters; word 1 is set if a wait ever exceeded
+ * its bound (never in a correct run: the bound only keeps a fault from
+ * hanging the GPU). Errors otherwise as lsa_hier_select. */
+int32_t lsa_hier_decode_step(const int8_t* q_idx, const int8_t* k_idx, const int8_t* k_blk, const int32_t* w,
+                             const lsa_bf16* q, const lsa_bf16* k_cache, const lsa_bf16* v_cache, int32_t B,
+                             int32_t n_k, int32_t H_I, int32_t d_I, int32_t blk, int32_t n_blk_recall,
+                             lsa_select_cfg cfg, int32_t H, int32_t D, int32_t n_split, float scale,
+                             int32_t* idx, int32_t* n_sel, lsa_bf16* o, float* lse, void* ws, size_t ws_bytes,
+                             size_t* ws_needed, void* stream);
+
 /* MTP draft rows that also see the drafts before them (a causal variant of the
  * index reuse across the MTP draft steps, CLI paragraph). The target row of
  * sequence b sits at tgt_pos[b]; draft row j (1 <= j < n_q) sits at

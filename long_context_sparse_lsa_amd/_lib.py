@@ -60,6 +60,8 @@ SIGNATURES = {
     "lsa_sparse_attn_backward": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _P, _P, _P, _P, _Z,
                                       _ZP, _P]),
     "lsa_kl_warmup": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _P, _P, _P]),
+    "lsa_hier_decode_step": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, SelectCfg, _I, _I, _I, _F, _P,
+                                  _P, _P, _P, _P, _Z, _ZP, _P]),
 }
 
 _lib = None
@@ -292,6 +294,43 @@ def lsa_hier_select_ragged(q_idx, k_idx, k_blk, w, ctx_len, blk, n_blk_recall, n
     ctx_len [B] int32 on the device. Returns (idx [B, K_tot], n_sel [B])."""
     return _hier("lsa_hier_select_ragged", q_idx, k_idx, k_blk, w, ctx_len, blk, n_blk_recall, n_sink, n_window,
                  k_dyn)
+
+
+def lsa_hier_decode_step(q_idx, k_idx, k_blk, w, q, k_cache, v_cache, blk, n_blk_recall, n_sink, n_window, k_dyn,
+                         n_split=8, scale=None, want_lse=False, ws=None):
+    """Fused HI decode step: q_idx [B, H_I, d_I] int8, k_idx [B, n_k, d_I],
+    k_blk from lsa_block_summary, w [H_I] host ints, q [B, 1, H, D] bf16,
+    caches [B, n_k, D] bf16. Returns (idx [B, K_tot], n_sel [B], o [B, 1, H, D]
+    bf16[, lse [B, 1, H]]). ws: optional uint8 workspace (its first 256 bytes
+    hold the step's counters; int32 word 1 flags an exceeded wait)."""
+    lib = load()
+    for t, n in ((q_idx, "q_idx"), (k_idx, "k_idx"), (k_blk, "k_blk")):
+        _dev(t, torch.int8, n)
+    for t, n in ((q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache")):
+        _dev(t, torch.bfloat16, n)
+    B, H_I, d_I = q_idx.shape
+    n_k = k_idx.shape[1]
+    _, n_q, H, D = q.shape
+    if n_q != 1 or q.shape[0] != B or k_cache.shape != (B, n_k, D) or v_cache.shape != k_cache.shape:
+        raise ValueError("shape mismatch")
+    wh, wp = _weights(w, H_I)
+    cfg = SelectCfg(n_sink, n_window, k_dyn)
+    K_tot = n_sink + n_window + k_dyn
+    scale = D ** -0.5 if scale is None else float(scale)
+    need = ctypes.c_size_t(0)
+    args = (_ptr(q_idx), _ptr(k_idx), _ptr(k_blk), wp, _ptr(q), _ptr(k_cache), _ptr(v_cache), B, n_k, H_I, d_I, blk,
+            n_blk_recall, cfg, H, D, n_split, scale)
+    _check("lsa_hier_decode_step", lib.lsa_hier_decode_step(*args, None, None, None, None, None, 0,
+                                                            ctypes.byref(need), None))
+    if ws is None or ws.numel() < need.value:
+        ws = _workspace(need.value, q.device)
+    idx = torch.empty((B, K_tot), dtype=torch.int32, device=q.device)
+    n_sel = torch.empty((B,), dtype=torch.int32, device=q.device)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, 1, H), dtype=torch.float32, device=q.device) if want_lse else None
+    _check("lsa_hier_decode_step", lib.lsa_hier_decode_step(*args, _ptr(idx), _ptr(n_sel), _ptr(o), _ptr(lse),
+                                                            _ptr(ws), ws.numel(), None, _stream()))
+    return (idx, n_sel, o, lse) if want_lse else (idx, n_sel, o)
 
 
 def lsa_sparse_attn_prefill(q, k, v, idx, n_sel, scale=None, want_lse=False, out=None):

@@ -36,7 +36,8 @@ _VGPR_FORM = ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]
 # sum chains need no NaN quieting or -0 handling.
 _NO_NAN = ["-fno-honor-nans", "-fno-signed-zeros"]
 FILE_FLAGS = {"index_prefill.hip": _VGPR_FORM, "index_decode.hip": _VGPR_FORM,
-              "attention.hip": _VGPR_FORM + _NO_NAN}
+              "attention.hip": _VGPR_FORM + _NO_NAN, "attention_bwd.hip": _VGPR_FORM, "kl.hip": _VGPR_FORM,
+              "hi_step.hip": _VGPR_FORM + _NO_NAN}
 
 
 def sources():
