@@ -419,6 +419,18 @@ def run_decode(args, wl, torch):
     q, kc, vc = synth.attention_inputs(wl, 0, dev)
     q1 = q_idx[:, None].contiguous()
     kblk = L.lsa_block_summary(k_idx, wl.blk) if wl.blk else None
+    summary_us = None
+    if wl.blk:
+        # the HI block summaries of the whole cache (built once per cache, then
+        # kept current on append): timed apart from the step
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(5):
+            L.lsa_block_summary(k_idx, wl.blk)
+        e1.record()
+        torch.cuda.synchronize()
+        summary_us = e0.elapsed_time(e1) * 1e3 / 5
     step_ws = torch.empty(64 << 20, dtype=torch.uint8, device=dev) if (wl.blk and args.fused) else None
     torch.cuda.synchronize()
     timer = EventTimer(torch)
@@ -514,6 +526,9 @@ def run_decode(args, wl, torch):
         "parts": {"eager_us_per_step": round(us_eager, 2), "cold_cache_us_per_step": round(us_cold, 2),
                   "select_us": round(sel_ms * 1e3, 2), "attn_us": round(attn_ms * 1e3, 2),
                   "fused_step_us": round(fused_ms * 1e3, 2),
+                  "block_summary": None if summary_us is None else {
+                      "us": round(summary_us, 2), "read_bytes": wl.B * N * wl.d_I,
+                      "hbm_frac": round(wl.B * N * wl.d_I / (summary_us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)},
                   "step_bytes": step_bytes,
                   "step_hbm_frac": round(step_bytes / (us_step * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
                   "kernels": kernel_parts(kt)},

@@ -51,6 +51,70 @@ def attend_rows(qrows, kc, vc, sel, scale):
     return O.attend(qrows, f64(kc[t]), f64(vc[t]), np.arange(len(sel)), scale)
 
 
+def half_ulp_bf16(x):
+    """Half a bf16 unit in the last place at |x| (the largest rounding error of
+    a bf16 output whose exact value is x)."""
+    x = np.abs(np.asarray(x, dtype=np.float64))
+    e = np.floor(np.log2(np.maximum(x, 2.0 ** -126)))
+    return 2.0 ** (e - 8)
+
+
+class RowErrors(AttnErrors):
+    """AttnErrors (pooled mean-abs, max-abs) plus the largest error beyond
+    half a bf16 ulp of the exact value: what the kernel's arithmetic adds on
+    top of the rounding that any bf16 output carries."""
+
+    def __init__(self, what):
+        super().__init__(what)
+        self.excess = 0.0
+
+    def add(self, got, ref):
+        super().add(got, ref)
+        err = np.abs(np.asarray(got, dtype=np.float64) - ref)
+        self.excess = max(self.excess, float((err - half_ulp_bf16(ref)).max()))
+
+    def report(self):
+        mx, mean = self.check()
+        return (f"{self.what}: max-abs {mx:.3g}, pooled mean-abs {mean:.3g}, "
+                f"largest error beyond half a bf16 ulp {max(self.excess, 0.0):.3g}")
+
+
+def check_all_rows_topk(idx, n_sel, q_idx, k_idx, w, wl, rows_per_block=32):
+    """Every row's selection is exact: structure (sinks, window, ascending,
+    padding) and the dynamic picks are the k_dyn largest candidates under the
+    oracle's scores by the composite key score * 2^32 + (2^32 - 1 - position),
+    a total order, so the set is unique. Scores come from the oracle in row
+    blocks."""
+    L = wl.L
+    kn = np_(k_idx[0])
+    In, Nn = np_(idx[0]), np_(n_sel[0])
+    ns, W, kd, K_tot = wl.n_sink, wl.n_window, wl.k_dyn, wl.K_tot
+    short = np.arange(min(L, K_tot))
+    for t in short:  # t + 1 <= K_tot: every key 0..t
+        assert Nn[t] == t + 1 and np.array_equal(In[t, : t + 1], np.arange(t + 1)), f"row {t}"
+    pos = np.arange(L, dtype=np.int64)
+    tie = (1 << 32) - 1 - pos
+    for r0 in range(K_tot, L, rows_per_block):
+        r1 = min(L, r0 + rows_per_block)
+        S = O.index_scores(np_(q_idx[0, r0:r1]), kn[:r1], w)           # [rows, r1] exact
+        key = S.astype(np.int64) * (1 << 32) + tie[None, :r1]
+        rows = np.arange(r0, r1)
+        sel = In[r0:r1]
+        assert np.all(Nn[r0:r1] == K_tot), f"rows {r0}..{r1}: n_sel"
+        assert np.all(sel[:, :ns] == np.arange(ns)[None]), "sinks"
+        assert np.all(sel[:, K_tot - W:] == (rows[:, None] - W + 1 + np.arange(W)[None])), "window"
+        dyn = sel[:, ns: ns + kd]
+        assert np.all(np.diff(dyn, axis=1) > 0), "ascending"
+        assert np.all(dyn >= ns) and np.all(dyn <= (rows - W)[:, None]), "candidate range"
+        picked = np.take_along_axis(key, dyn.astype(np.int64), axis=1)
+        kmin = picked.min(axis=1)
+        cand = (pos[None, :r1] >= ns) & (pos[None, :r1] <= (rows - W)[:, None])
+        chosen = np.zeros_like(cand)
+        np.put_along_axis(chosen, dyn.astype(np.int64), True, axis=1)
+        rest = np.where(cand & ~chosen, key, np.iinfo(np.int64).min)
+        assert np.all(rest.max(axis=1) < kmin), f"rows {r0}..{r1}: a left-out candidate outranks a pick"
+
+
 def run_prefill_full(wl, n_rand, seed):
     say(f"{wl.name}: inputs")
     q_idx, k_idx, w = synth.indexer_inputs(wl, DEV)
@@ -61,7 +125,7 @@ def run_prefill_full(wl, n_rand, seed):
     torch.cuda.synchronize()
     rows = sample_rows(wl.L, wl.K_tot, n_rand, seed)
     kn = np_(k_idx[0])
-    errs = [AttnErrors(f"{wl.name} layer {i}") for i in range(wl.n_layers)]
+    errs = [RowErrors(f"{wl.name} layer {i}") for i in range(wl.n_layers)]
     for t in rows:
         n = int(n_sel[0, t])
         got = np_(idx[0, t])
@@ -73,17 +137,20 @@ def run_prefill_full(wl, n_rand, seed):
             ref_o, _ = attend_rows(f64(q[0, t]), k[0], v[0], ref, wl.scale)
             errs[i].add(f64(outs[i][0, t]), ref_o)
     for e in errs:
-        say("  ", e.check())
+        say("  ", e.report())
     return idx, n_sel, outs, (q_idx, k_idx, w, layers)
 
 
 def test_c2_prefill_32k_full():
-    run_prefill_full(configs.C2, n_rand=40, seed=2)
+    wl = configs.C2
+    idx, n_sel, _, (q_idx, k_idx, w, _) = run_prefill_full(wl, n_rand=240, seed=2)
+    say(f"{wl.name}: every row's selection against the oracle's scores")
+    check_all_rows_topk(idx, n_sel, q_idx, k_idx, w, wl)
 
 
 def test_c5_cli_prefill_128k_full_and_deterministic():
     wl = configs.C5
-    idx, n_sel, outs, (q_idx, k_idx, w, layers) = run_prefill_full(wl, n_rand=12, seed=5)
+    idx, n_sel, outs, (q_idx, k_idx, w, layers) = run_prefill_full(wl, n_rand=240, seed=5)
     # run-to-run bit-identical selection and both layers' outputs; the
     # second run recomputes the index, so layer 2 on the reused index equals
     # layer 2 on a recomputed one (CLI)
@@ -108,8 +175,8 @@ def test_c3_mtp_decode_128k_full():
     o2 = L.lsa_sparse_attn_decode(q, kc, vc, idx, n_sel, n_split=wl.n_split)
     torch.cuda.synchronize()
     assert torch.equal(o, o2)
-    err = AttnErrors(wl.name)
-    for b in (0, 1, 37, 63):
+    err = RowErrors(wl.name)
+    for b in range(wl.B):
         say(f"{wl.name}: sequence {b}")
         got = np_(idx[b, 0])
         n = int(n_sel[b, 0])
@@ -118,7 +185,7 @@ def test_c3_mtp_decode_128k_full():
         assert np.array_equal(got[:n], ref), f"sequence {b}: idx differs"
         ref_o, _ = attend_rows(f64(q[b]).reshape(-1, wl.D), kc[b], vc[b], ref, wl.scale)
         err.add(f64(o[b]).reshape(-1, wl.D), ref_o)
-    say("  ", err.check())
+    say("  ", err.report())
 
 
 def test_c4_hi_decode_1m_full():
@@ -131,8 +198,8 @@ def test_c4_hi_decode_1m_full():
                                    wl.k_dyn)
     o = L.lsa_sparse_attn_decode(q, kc, vc, idx[:, None], n_sel[:, None], n_split=wl.n_split)
     torch.cuda.synchronize()
-    err = AttnErrors(wl.name)
-    for b in (0, 3):
+    err = RowErrors(wl.name)
+    for b in range(wl.B):
         say(f"{wl.name}: sequence {b}")
         kn = np_(k_idx[b])
         kb_ref = O.block_summary(kn, wl.blk)
@@ -145,4 +212,4 @@ def test_c4_hi_decode_1m_full():
         assert np.array_equal(got[:n], ref), f"sequence {b}: idx differs"
         ref_o, _ = attend_rows(f64(q[b]).reshape(-1, wl.D), kc[b], vc[b], ref, wl.scale)
         err.add(f64(o[b]).reshape(-1, wl.D), ref_o)
-    say("  ", err.check())
+    say("  ", err.report())
