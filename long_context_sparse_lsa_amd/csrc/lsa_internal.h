@@ -26,9 +26,10 @@ struct SeqShift {
   const int32_t* ctx_len;
   int ctx_rows, ctx_cap;
 };
-__device__ __forceinline__ int seq_shift(const SeqShift& s, int b) {
+__host__ __device__ inline int seq_shift(const SeqShift& s, int b) {
   if (s.ctx_len == nullptr) return 0;
-  return min(max(s.ctx_len[b], s.ctx_rows), s.ctx_cap) - s.ctx_cap;
+  const int L = s.ctx_len[b] < s.ctx_rows ? s.ctx_rows : s.ctx_len[b];
+  return (L < s.ctx_cap ? L : s.ctx_cap) - s.ctx_cap;
 }
 struct ScoreArgs {
   const int8_t* q;

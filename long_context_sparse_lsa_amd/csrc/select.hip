@@ -28,6 +28,7 @@
 #include "lsa_device.h"
 #include "lsa_internal.h"
 #include "select_dev.h"
+#include "select_geom.h"
 
 namespace lsa {
 
@@ -35,55 +36,6 @@ namespace {
 
 constexpr int SEL_NT = 1024;  // threads of a stage-B workgroup (and the widest stage A)
 
-struct RowGeom {
-  int trivial;
-  int t;
-  int c_lo, nc;
-  int k;
-};
-
-__device__ __forceinline__ RowGeom row_geom(const SelectArgs& a, int r) {
-  RowGeom gm{0, 0, 0, 0, 0};
-  if (a.mode == SEL_FLAT) {
-    const int t = a.q_off + (a.row0 + r) % a.n_q + seq_shift(a.shift, (a.row0 + r) / a.n_q);
-    gm.t = t;
-    if (t + 1 <= a.n_sink + a.n_window + a.k_dyn) {
-      gm.trivial = 1;
-      return gm;
-    }
-    gm.c_lo = a.n_sink;
-    gm.nc = t - a.n_window - a.n_sink + 1;
-    gm.k = a.k_dyn;
-  } else if (a.mode == SEL_RAW) {
-    int hi = a.raw_hi;
-    if (a.shift.ctx_len != nullptr) {
-      const int hp = a.raw_hi_pos + seq_shift(a.shift, a.row0 + r);
-      hi = min(hp >= 0 ? hp / a.raw_div : -1, a.raw_hi);
-    }
-    gm.c_lo = a.raw_lo;
-    gm.nc = max(0, hi - a.raw_lo + 1);
-    gm.k = a.raw_k;
-  } else {
-    gm.t = a.t_fixed;
-    gm.c_lo = 0;
-    gm.nc = a.n_virt;
-    gm.k = a.k_dyn;
-    if (a.shift.ctx_len != nullptr) {
-      gm.t += seq_shift(a.shift, a.row0 + r);
-      gm.trivial = gm.t + 1 <= a.n_sink + a.n_window + a.k_dyn;
-    }
-  }
-  return gm;
-}
-
-__device__ __forceinline__ int pos_of(const SelectArgs& a, int r, int v) {
-  if (a.mode != SEL_INDIRECT) return v;
-  const int bi = a.blocks[(int64_t)r * a.nbr + v / a.blk];
-  return bi * a.blk + v % a.blk;
-}
-
-// Exclusive prefix sum over the block in thread order (mod 2^32); *total
-// gets the sum. One barrier: sh.scan_w is written once per workgroup.
 template <int NT>
 __device__ void write_trivial(const SelectArgs& a, int r, int t) {
   int32_t* out = a.idx + (int64_t)r * a.out_ld;
