@@ -86,7 +86,13 @@ int32_t lsa_index_score(const int8_t* q_idx, const int8_t* k_idx, const int32_t*
  *           the call scores q_idx / k_idx / w itself (fused indexer + top-k)
  *   idx     [B, n_q, K_tot] int32 out, ascending, -1 padded
  *   n_sel   [B, n_q] int32 out, min(q_off + i + 1, K_tot)
- * Requires q_off + n_q <= n_k. */
+ * Requires q_off + n_q <= n_k. A row's candidates are selected in chunks of
+ * 32768 whose survivors (k_dyn each, rounded up to a multiple of 4: k_cap)
+ * are reduced in at most two further passes of 32768 entries: rows of up to
+ * (32768 / k_cap)^2 chunks are supported (8388608 candidates at k_dyn =
+ * 2048), longer ones return LSA_UNSUPPORTED. The limit is checked against the
+ * longest row the call can see (for lsa_select_topk_ragged: the cache
+ * capacity n_k). */
 int32_t lsa_select_topk(const int32_t* scores, const int8_t* q_idx, const int8_t* k_idx,
                         const int32_t* w, int32_t B, int32_t n_q, int32_t n_k, int32_t H_I,
                         int32_t d_I, int32_t q_off, lsa_select_cfg cfg, int32_t* idx,
@@ -211,7 +217,11 @@ int32_t lsa_mtp_row_index(const int32_t* idx, const int32_t* n_sel, int32_t B, i
 /* Sparse attention, prefill: query row t of sequence b attends over the keys
  * idx[b, t, 0 .. n_sel[b, t]-1] of its sequence (one KV head shared by H query
  * heads); softmax(scale * q.k) in fp32, output bf16. Passing the same idx to
- * consecutive layers is cross-layer index reuse (CLI paragraph).
+ * consecutive layers is cross-layer index reuse (CLI paragraph). Each row's
+ * list must be strictly ascending with no duplicates, as the selection writes
+ * it: two neighbouring rows whose lists end in runs of consecutive positions
+ * (their SI windows) attend those runs through one shared gather, and a run is
+ * recognised from its first and last entries.
  *   q [B, L, H, D] bf16, k / v [B, n_k, D] bf16, idx [B, L, K_tot], n_sel [B, L]
  *   o [B, L, H, D] bf16 out; lse [B, L, H] fp32 out (natural log) or NULL
  * Supported: D = 128; H in {16, 32, 64, 128}; n_k <= 16777215 (cache rows are

@@ -89,6 +89,11 @@ struct SelectArgs {
   int32_t* ws_pos;
   int32_t* ws_cnt;
   int max_chunks;  // chunks of the longest row (select_plan)
+  // rows whose chunk survivors exceed one stage-B pass first reduce groups of
+  // `group` chunks to k_cap survivors each into ws2 (0: no middle stage)
+  int group;
+  int32_t* ws2_score;
+  int32_t* ws2_pos;
   int chunk_e;     // candidates per thread of a chunk (select_plan)
   int chunk_nt;    // threads of a stage-A workgroup (select_plan)
   int k_cap;
@@ -101,7 +106,8 @@ struct SelectArgs {
 int select_chunks(int64_t max_nc, int k_cap);
 bool select_fits(int64_t max_nc, int k_cap);
 void select_plan(SelectArgs& a, int64_t max_nc);
-// Largest stage-two input (max_chunks * k_cap) the selection supports.
+// Largest input of one reduction pass over chunk survivors; with the middle
+// stage a row may have up to (kSelMaxSurvivors / k_cap)^2 chunks.
 constexpr int64_t kSelMaxSurvivors = 32 * 1024;
 size_t select_ws_bytes(int n_rows, int max_chunks, int k_cap);
 void select_bind_ws(SelectArgs& a, void* ws, int n_rows);

@@ -102,8 +102,49 @@ __global__ __launch_bounds__(NT, MINW) void select_stage_a(SelectArgs a) {
   }
 }
 
+// Chunk groups of the middle stage in the longest row.
+__host__ __device__ inline int mid_groups(const SelectArgs& a) { return (a.max_chunks + a.group - 1) / a.group; }
+
+// Middle stage (rows with more chunk survivors than one pass holds): group g
+// of row r reduces the survivors of chunks [g * group, (g + 1) * group) to
+// their top k, kept as (score, position) pairs in ws2 and padded with
+// INT32_MIN. The survivors are in ascending position order and so are the
+// kept pairs, so ties still go to the lower position.
+template <int E>
+__global__ __launch_bounds__(SEL_NT) void select_stage_m(SelectArgs a, int CH) {
+  __shared__ SelShared<SEL_NT> sh;
+  const int r = blockIdx.x, g = blockIdx.y;
+  const RowGeom gm = row_geom(a, r);
+  if (gm.trivial) return;
+  const int n_chunks = (gm.nc + CH - 1) / CH;
+  const int c0 = g * a.group, c1 = min(n_chunks, c0 + a.group);
+  if (n_chunks <= 1 || c0 >= c1) return;
+  const int n = (c1 - c0) * a.k_cap;
+  const int64_t base = ((int64_t)r * a.max_chunks + c0) * a.k_cap;
+  const int32_t* ws_s = a.ws_score + base;
+  const int32_t* ws_p = a.ws_pos + base;
+  uint32_t u[E];
+  load_keys<E>(ws_s, 0, n, u);
+  int n_valid;
+  uint32_t kmin, kmax, T;
+  chunk_stats<E, SEL_NT>(u, sh, n_valid, kmin, kmax);
+  int shift, r_eq;
+  if (!plan_trivial(gm.k, n_valid, T, shift, r_eq))
+    radix_select<E, SEL_NT>(u, kmin, kmax, gm.k, sh, T, shift, r_eq);
+  const int i0 = threadIdx.x * E;
+  const int64_t ob = ((int64_t)r * mid_groups(a) + g) * a.k_cap;
+  int32_t* os = a.ws2_score + ob;
+  int32_t* op = a.ws2_pos + ob;
+  const int cnt = compact<E, SEL_NT>(u, T, shift, r_eq, sh, [&](int o, int e) {
+    os[o] = ws_s[i0 + e];
+    op[o] = ws_p[i0 + e];
+  });
+  for (int i = cnt + threadIdx.x; i < a.k_cap; i += SEL_NT) os[i] = kMasked;
+}
+
 // Stage B: top-k of the concatenated chunk survivors (n_chunks * k_cap
-// entries, padded with INT32_MIN) of one row.
+// entries, padded with INT32_MIN) of one row, or, after the middle stage, of
+// the row's group survivors.
 template <int E>
 __global__ __launch_bounds__(SEL_NT) void select_stage_b(SelectArgs a, int CH) {
   __shared__ SelShared<SEL_NT> sh;
@@ -112,10 +153,11 @@ __global__ __launch_bounds__(SEL_NT) void select_stage_b(SelectArgs a, int CH) {
   if (gm.trivial) return;
   const int n_chunks = (gm.nc + CH - 1) / CH;
   if (n_chunks <= 1) return;
-  const int n = n_chunks * a.k_cap;
-  const int64_t base = (int64_t)r * a.max_chunks * a.k_cap;
-  const int32_t* ws_s = a.ws_score + base;
-  const int32_t* ws_p = a.ws_pos + base;
+  const bool mid = a.group > 0;
+  const int n = mid ? (n_chunks + a.group - 1) / a.group * a.k_cap : n_chunks * a.k_cap;
+  const int64_t base = (int64_t)r * (mid ? mid_groups(a) : a.max_chunks) * a.k_cap;
+  const int32_t* ws_s = (mid ? a.ws2_score : a.ws_score) + base;
+  const int32_t* ws_p = (mid ? a.ws2_pos : a.ws_pos) + base;
   uint32_t u[E];
   load_keys<E>(ws_s, 0, n, u);
   int n_valid;
@@ -178,8 +220,19 @@ hipError_t launch_e(const SelectArgs& a, hipStream_t st) {
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.max_chunks <= 1) return e;
-  // survivors of one row: max_chunks * k_cap
-  const int64_t nb = (int64_t)a.max_chunks * a.k_cap;
+  if (a.group > 0) {
+    const int64_t nm = (int64_t)a.group * a.k_cap;  // input of one group
+    const dim3 gm(a.n_rows, mid_groups(a));
+    KernelTimer kt("select_stage_m", st);
+    if (nm <= SEL_NT * 4) hipLaunchKernelGGL((select_stage_m<4>), gm, dim3(SEL_NT), 0, st, a, CH);
+    else if (nm <= SEL_NT * 8) hipLaunchKernelGGL((select_stage_m<8>), gm, dim3(SEL_NT), 0, st, a, CH);
+    else if (nm <= SEL_NT * 16) hipLaunchKernelGGL((select_stage_m<16>), gm, dim3(SEL_NT), 0, st, a, CH);
+    else hipLaunchKernelGGL((select_stage_m<32>), gm, dim3(SEL_NT), 0, st, a, CH);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  // survivors of one row: max_chunks * k_cap, or its groups' k_cap each
+  const int64_t nb = (int64_t)(a.group > 0 ? mid_groups(a) : a.max_chunks) * a.k_cap;
   KernelTimer kt("select_stage_b", st);
   if (nb <= SEL_NT * 4) hipLaunchKernelGGL((select_stage_b<4>), dim3(a.n_rows), dim3(SEL_NT), 0, st, a, CH);
   else if (nb <= SEL_NT * 8) hipLaunchKernelGGL((select_stage_b<8>), dim3(a.n_rows), dim3(SEL_NT), 0, st, a, CH);
@@ -194,9 +247,17 @@ int select_chunks(int64_t max_nc, int k_cap) {
   return half_fits(max_nc, k_cap) ? sel_geo_half(max_nc).chunks : sel_geo(max_nc).chunks;
 }
 
+// Chunks per middle-stage group for c chunks of k_cap survivors (0: none).
+static int mid_group(int c, int k_cap) {
+  if (c <= 1 || (int64_t)c * k_cap <= kSelMaxSurvivors) return 0;
+  return (int)(kSelMaxSurvivors / k_cap);
+}
+
 bool select_fits(int64_t max_nc, int k_cap) {
   const int c = sel_geo(max_nc).chunks;
-  return c <= 1 || (int64_t)c * k_cap <= kSelMaxSurvivors;
+  if (c <= 1 || (int64_t)c * k_cap <= kSelMaxSurvivors) return true;
+  const int G = mid_group(c, k_cap);
+  return G >= 1 && (int64_t)((c + G - 1) / G) * k_cap <= kSelMaxSurvivors;
 }
 
 void select_plan(SelectArgs& a, int64_t max_nc) {
@@ -210,27 +271,39 @@ void select_plan(SelectArgs& a, int64_t max_nc) {
   a.chunk_e = g.e;
   a.chunk_nt = g.nt;
   a.max_chunks = g.chunks;
+  a.group = mid_group(g.chunks, a.k_cap);
 }
 
 size_t select_ws_bytes(int n_rows, int max_chunks, int k_cap) {
   if (max_chunks <= 1) return 0;
-  return (size_t)2 * n_rows * max_chunks * k_cap * sizeof(int32_t);
+  size_t b = (size_t)2 * n_rows * max_chunks * k_cap * sizeof(int32_t);
+  const int G = mid_group(max_chunks, k_cap);
+  if (G > 0) b += (size_t)2 * n_rows * ((max_chunks + G - 1) / G) * k_cap * sizeof(int32_t);
+  return b;
 }
 
 void select_bind_ws(SelectArgs& a, void* ws, int n_rows) {
   if (a.max_chunks <= 1 || ws == nullptr) {
-    a.ws_score = a.ws_pos = nullptr;
+    a.ws_score = a.ws_pos = a.ws2_score = a.ws2_pos = nullptr;
     return;
   }
   a.ws_score = (int32_t*)ws;
   a.ws_pos = a.ws_score + (size_t)n_rows * a.max_chunks * a.k_cap;
+  if (a.group > 0) {
+    a.ws2_score = a.ws_pos + (size_t)n_rows * a.max_chunks * a.k_cap;
+    a.ws2_pos = a.ws2_score + (size_t)n_rows * mid_groups(a) * a.k_cap;
+  } else {
+    a.ws2_score = a.ws2_pos = nullptr;
+  }
 }
 
-// The geometry must come from select_plan (k_cap set first), and the stage-B
-// survivor count max_chunks * k_cap must fit 32 * 1024 entries.
+// The geometry must come from select_plan (k_cap set first); one reduction
+// pass over survivors holds at most kSelMaxSurvivors entries.
 hipError_t launch_select(const SelectArgs& a, hipStream_t st) {
   if (a.n_rows <= 0) return hipSuccess;
-  if (a.max_chunks > 1 && (int64_t)a.max_chunks * a.k_cap > kSelMaxSurvivors) return hipErrorInvalidValue;
+  if (a.max_chunks > 1 && (int64_t)a.max_chunks * a.k_cap > kSelMaxSurvivors &&
+      (a.group <= 0 || (int64_t)mid_groups(a) * a.k_cap > kSelMaxSurvivors))
+    return hipErrorInvalidValue;
   if (a.chunk_e == 4) return launch_e<4, SEL_NT>(a, st);
   if (a.chunk_e == 16) return launch_e<16, SEL_NT>(a, st);
   if (a.chunk_nt == 512) return launch_e<32, 512>(a, st);

@@ -108,6 +108,23 @@ def test_select_topk_checks_and_workspace_query():
                                P(FAKE), P(FAKE), P(FAKE), 1 << 30, None, None) == L.LSA_RANGE
 
 
+def test_select_topk_candidate_limit():
+    """Flat selection holds up to (32768 / k_cap)^2 chunks of 32768 keys per row
+    (a middle reduction stage past 16 chunks at k_dyn = 2048): 8388608
+    candidates; one more is unsupported. A 1M-key cache is supported."""
+    lib = L.load()
+    need = ctypes.c_size_t(0)
+    cfg = L.SelectCfg(4, 512, 2048)
+    for n_k, want in ((1 << 20, L.LSA_OK), (8388608 + 516, L.LSA_OK), (8388608 + 517, L.LSA_UNSUPPORTED)):
+        s = lib.lsa_select_topk(P(FAKE), None, None, None, 1, 1, n_k, 0, 0, n_k - 1, cfg,
+                                None, None, None, 0, ctypes.byref(need), None)
+        assert s == want, (n_k, s)
+    w, wp = _w([1] * 64)
+    s = lib.lsa_select_topk_ragged(P(FAKE), P(FAKE), wp, 4, 1, 1 << 20, 64, 128, P(FAKE), cfg,
+                                   None, None, None, 0, ctypes.byref(need), None)
+    assert s == L.LSA_OK
+
+
 def test_select_topk_ragged_checks():
     lib = L.load()
     need = ctypes.c_size_t(0)

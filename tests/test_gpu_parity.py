@@ -123,6 +123,43 @@ def test_select_given_scores_ties_and_chunks(cfg, n_k, hi):
             check_idx(In[b, i], Nn[b, i], ref, K_tot, f"b{b} i{i}")
 
 
+@pytest.mark.parametrize("n_k,kd,hi", [(600000, 2048, 1 << 24), (1 << 20, 2048, 50), (1 << 20, 2048, 1 << 24),
+                                       (290000, 9000, 1 << 24)])
+def test_select_three_levels(n_k, kd, hi):
+    """Rows whose chunk survivors exceed one reduction pass (more than 16
+    chunks of 32768 keys at k_dyn = 2048) go through the middle stage: given
+    scores at up to 1M candidates, with heavy ties, against the oracle."""
+    say(f"select three levels n_k={n_k} k_dyn={kd} hi={hi}")
+    B, n_q, n_sink, W = 1, 2, 4, 512
+    g = torch.Generator(device=DEV)
+    g.manual_seed(n_k + kd)
+    scores = torch.randint(0, hi, (B, n_q, n_k), dtype=torch.int32, generator=g, device=DEV)
+    q_off = n_k - n_q
+    idx, n_sel = L.lsa_select_topk(scores=scores, n_sink=n_sink, n_window=W, k_dyn=kd, q_off=q_off)
+    idx2, n_sel2 = L.lsa_select_topk(scores=scores, n_sink=n_sink, n_window=W, k_dyn=kd, q_off=q_off)
+    torch.cuda.synchronize()
+    assert torch.equal(idx, idx2) and torch.equal(n_sel, n_sel2)
+    Sn, In, Nn = np_(scores), np_(idx), np_(n_sel)
+    for i in range(n_q):
+        ref = O.select_flat(Sn[0, i], q_off + i, n_sink, W, kd)
+        check_idx(In[0, i], Nn[0, i], ref, n_sink + W + kd, f"row {i}")
+
+
+def test_fused_select_decode_1m_flat():
+    """Flat decode selection (scored and selected by one call) over a 1M-key
+    cache: the middle stage in the fused path, against the oracle."""
+    B, n_k, H_I, d_I = 2, 1 << 20, 64, 128
+    say("fused flat decode selection at 1M keys")
+    q_idx = i8((B, 1, H_I, d_I), -16, 15, "m1q")
+    k_idx = i8((B, n_k, d_I), -16, 15, "m1k")
+    w = synth.int_weights(H_I, 1, 8, 91)
+    idx, n_sel = L.lsa_select_topk(q_idx, k_idx, w, 4, 512, 2048, q_off=n_k - 1)
+    torch.cuda.synchronize()
+    for b in range(B):
+        ref = O.decode_select(np_(q_idx[b, 0]), np_(k_idx[b]), w, 4, 512, 2048)
+        check_idx(np_(idx[b, 0]), int(n_sel[b, 0]), ref, 4 + 512 + 2048, f"b{b}")
+
+
 @pytest.mark.parametrize("n_q,n_k", [(720, 41000), (2100, 10000)])
 @pytest.mark.parametrize("hi", [50, 1 << 24])
 def test_select_many_long_rows_half_chunks(hi, n_q, n_k):
