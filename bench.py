@@ -117,7 +117,8 @@ def cpu_threads():
 KERNELS = ("index_prefill_kernel", "index_decode_kernel", "index_score_kernel", "select_stage_a",
            "select_stage_b", "attn_prefill_kernel", "attn_decode_partial", "attn_decode_merge",
            "fill_zero_kernel", "attn_bwd_kernel", "bwd_count_kernel", "bwd_scan_kernel", "bwd_fill_kernel",
-           "bwd_reduce_kernel", "attn_bwd_finish_kernel", "kl_warmup_kernel", "hi_step_kernel")
+           "bwd_reduce_kernel", "attn_bwd_finish_kernel", "kl_warmup_kernel", "hi_step_kernel",
+           "filter_threshold_kernel", "filter_select_kernel", "select_stage_m")
 
 
 def kernel_times(L, torch, step, steps, park=False):

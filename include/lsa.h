@@ -92,7 +92,14 @@ int32_t lsa_index_score(const int8_t* q_idx, const int8_t* k_idx, const int32_t*
  * (32768 / k_cap)^2 chunks are supported (8388608 candidates at k_dyn =
  * 2048), longer ones return LSA_UNSUPPORTED. The limit is checked against the
  * longest row the call can see (for lsa_select_topk_ragged: the cache
- * capacity n_k). */
+ * capacity n_k).
+ * Fused path, one sequence per pass (prefill): rows with at least 16384
+ * candidates first score every 32nd candidate; a high order statistic of that
+ * sample is a per-row threshold, the full scoring pass keeps only the
+ * (score, position) pairs at or above it, and the row's top-k is taken from
+ * those survivors when they number at least k_dyn (then exactly the same
+ * list). Rows where that does not hold are scored and selected again in
+ * full within the same call, so the result never depends on the sample. */
 int32_t lsa_select_topk(const int32_t* scores, const int8_t* q_idx, const int8_t* k_idx,
                         const int32_t* w, int32_t B, int32_t n_q, int32_t n_k, int32_t H_I,
                         int32_t d_I, int32_t q_off, lsa_select_cfg cfg, int32_t* idx,

@@ -9,6 +9,7 @@
 #include <stdint.h>
 
 #include <algorithm>
+#include <cmath>
 #include <mutex>
 
 #include "lsa.h"
@@ -119,74 +120,241 @@ extern "C" int32_t lsa_index_score(const int8_t* q_idx, const int8_t* k_idx, con
   return hip_status(launch_index_score(a, (hipStream_t)stream));
 }
 
+// Thresholded selection (FilterArgs): rows with at least kFilterMinCand
+// candidates, in passes of one sequence (prefill), score a sample of every
+// kSampM-th position first; the sample's threshold lets the full scoring pass
+// keep about (lam + 6 sqrt(lam) + 10) * kSampM pairs per row (lam = k / kSampM)
+// instead of writing every score, and the survivors' top-k is exact whenever
+// they number at least k; other rows are redone by the dense path.
+constexpr int kSampM = 32;
+constexpr int kFilterMinCand = 16384;
+
+struct FilterPlan {
+  bool on = false;
+  int64_t surv = 0;  // expected survivors of a row, at most
+  int max_surv = 0;  // survivors the survivor selection holds (twice surv)
+};
+
+FilterPlan filter_plan(const lsa_select_cfg& cfg, int H_I, int d_I) {
+  FilterPlan p;
+  const int k = cfg.k_dyn;
+  if (k < 64 || (H_I != 32 && H_I != 64) || (d_I != 64 && d_I != 128)) return p;
+  // the sample of a row holds at most nc / m + 1 of its nc >= kFilterMinCand candidates
+  const double lam = (double)k / kSampM + (double)k / kFilterMinCand;
+  const double jstar = std::ceil(lam + 6.0 * std::sqrt(lam) + 10.0);
+  p.surv = (int64_t)std::ceil(jstar * (kSampM + 1));
+  p.on = 2 * p.surv <= filter_select_capacity();
+  p.max_surv = (int)(2 * p.surv);
+  return p;
+}
+
+// Pairs one (row, chunk) segment holds: survivors of a chunk of ck keys in a
+// row of at least nc_min candidates number about mu = surv * min(1, ck /
+// nc_min); the capacity leaves room for the threshold's spread.
+int seg_cap_of(const FilterPlan& p, int ck, int64_t nc_min) {
+  const double mu = (double)p.surv * std::min(1.0, (double)ck / (double)nc_min);
+  const int64_t cap = (int64_t)std::ceil(1.6 * mu + 8.0 * std::sqrt(mu) + 64.0);
+  return (int)std::min<int64_t>(ck, (cap + 63) / 64 * 64);
+}
+
+// Workspace of the fused path for passes of `rows` rows: the dense score
+// buffer (which the filtered rows' segments share), the selection's chunk
+// workspace, then the sample scores, thresholds, fail flags and segment counts.
+struct FusedWs {
+  size_t sbuf, sel, samp, tau, fail, cnt, total;
+  int64_t samp_ld;
+  int max_segs;
+};
+FusedWs fused_ws(int64_t rows, int n_k, int64_t max_nc, int k_cap, bool filter) {
+  FusedWs w{};
+  w.sbuf = align_up((size_t)rows * n_k * sizeof(int32_t));
+  w.sel = align_up(select_ws_bytes((int)rows, chunks_of(max_nc, k_cap), k_cap));
+  if (filter) {
+    w.samp_ld = ((int64_t)n_k / kSampM + 1 + 3) / 4 * 4;
+    w.max_segs = (n_k + 4095) / 4096;
+    w.samp = align_up((size_t)rows * w.samp_ld * sizeof(int32_t));
+    w.tau = align_up((size_t)rows * sizeof(int32_t));
+    w.fail = w.tau;
+    w.cnt = align_up((size_t)rows * w.max_segs * sizeof(int32_t));
+  }
+  w.total = w.sbuf + w.sel + w.samp + w.tau + w.fail + w.cnt;
+  return w;
+}
+
 // Fused path of the flat selection: score a pass of rows (candidates only)
 // into the workspace, then select. A pass covers nb sequences times one range
 // of Rr query rows. ctx_len (device, per sequence, or null): ragged lengths,
 // row i of sequence b at position clamp(ctx_len[b], n_q, n_k) - n_q + i
-// (q_off is then n_k - n_q).
+// (q_off is then n_k - n_q). Passes of one sequence without ctx_len take the
+// thresholded selection for their rows of at least kFilterMinCand candidates.
 static int32_t fused_select(const int8_t* q_idx, const int8_t* k_idx, const WArgs& wa, int B, int n_q, int n_k,
                             int H_I, int d_I, int q_off, const lsa_select_cfg& cfg, int R, int nb_pass,
                             const int32_t* ctx_len, int32_t* idx, int32_t* n_sel, void* ws, hipStream_t st) {
   const int K_tot = cfg.n_sink + cfg.n_window + cfg.k_dyn;
-  int32_t s = LSA_OK;
+  const int k_cap = k_cap_of(cfg.k_dyn);
+  const FilterPlan fp = ctx_len == nullptr && nb_pass == 1 ? filter_plan(cfg, H_I, d_I) : FilterPlan{};
+  const int64_t max_nc = (int64_t)q_off + n_q - cfg.n_window - cfg.n_sink;
+  const FusedWs wl = fused_ws((int64_t)R * nb_pass, n_k, max_nc, k_cap, fp.on);
+  int32_t* sbuf = (int32_t*)ws;
+  void* sel_ws = (char*)ws + wl.sbuf;
+  int32_t* samp = (int32_t*)((char*)sel_ws + wl.sel);
+  int32_t* tau = (int32_t*)((char*)samp + wl.samp);
+  int32_t* fail = (int32_t*)((char*)tau + wl.tau);
+  int32_t* seg_cnt = (int32_t*)((char*)fail + wl.fail);
+
   SelectArgs sa{};
   sa.mode = SEL_FLAT;
   sa.n_sink = cfg.n_sink;
   sa.n_window = cfg.n_window;
   sa.k_dyn = cfg.k_dyn;
   sa.out_ld = K_tot;
-  sa.k_cap = k_cap_of(cfg.k_dyn);
-  int32_t* sbuf = (int32_t*)ws;
-  void* sel_ws = (char*)ws + align_up((size_t)R * nb_pass * n_k * sizeof(int32_t));
+  sa.k_cap = k_cap;
+
+  // the indexer launch over rows [r0, r0 + Rr) of sequences b0 .. b0 + nb - 1
+  auto score_args = [&](int b0, int nb, int r0, int Rr) {
+    const int t_last = q_off + r0 + Rr - 1;
+    ScoreArgs a{};
+    a.w = wa;
+    a.q = q_idx + ((int64_t)b0 * n_q + r0) * H_I * d_I;
+    a.k = k_idx + (int64_t)b0 * n_k * d_I;
+    a.B = nb;
+    a.n_q = Rr;
+    a.n_k = n_k;
+    a.H_I = H_I;
+    a.d_I = d_I;
+    a.q_bstride = (int64_t)n_q * H_I * d_I;
+    a.k_bstride = (int64_t)n_k * d_I;
+    a.s_bstride = (int64_t)Rr * n_k;
+    a.ld = n_k;
+    a.n_keys = (int)std::min<int64_t>(n_k, (int64_t)t_last - cfg.n_window + 1);
+    a.mask_off = q_off + r0 - cfg.n_window;
+    a.pos_lo = cfg.n_sink;
+    a.fill_masked = 0;
+    a.scores = sbuf;
+    a.shift = SeqShift{ctx_len ? ctx_len + b0 : nullptr, n_q, n_k};
+    return a;
+  };
+
+  // dense: every candidate score of the rows, then the chunked selection
+  // (only the rows flagged in `flags`, when given)
+  auto dense_rows = [&](int b0, int nb, int r0, int Rr, const int32_t* flags) -> int32_t {
+    const int t_last = q_off + r0 + Rr - 1;
+    const int64_t nc_last = (int64_t)t_last - cfg.n_window - cfg.n_sink + 1;
+    if (nc_last > 0 && t_last + 1 > K_tot) {
+      ScoreArgs a = score_args(b0, nb, r0, Rr);
+      a.row_flags = flags;
+      if (a.n_keys > 0) {
+        const int32_t s = hip_status(launch_index_score(a, st));
+        if (s != LSA_OK) return s;
+      }
+    }
+    // rows of the pass: sequence b0 + j, query r0 + i at row j * Rr + i
+    SelectArgs d = sa;
+    d.scores = sbuf;
+    d.ld = n_k;
+    d.n_rows = nb * Rr;
+    d.n_q = Rr;
+    d.q_off = q_off + r0;
+    d.row0 = 0;
+    d.shift = SeqShift{ctx_len ? ctx_len + b0 : nullptr, n_q, n_k};
+    d.row_flags = flags;
+    select_plan(d, nc_last);
+    select_bind_ws(d, sel_ws, nb * Rr);
+    // nb > 1 only when Rr == n_q (r0 == 0), so the pass's output rows are
+    // contiguous in idx / n_sel
+    d.idx = idx + ((int64_t)b0 * n_q + r0) * K_tot;
+    d.n_sel = n_sel + (int64_t)b0 * n_q + r0;
+    return hip_status(launch_select(d, st));
+  };
+
+  // thresholded: rows [r0, r0 + Rr) of sequence b0, every one non-trivial
+  // with at least kFilterMinCand candidates. Returns LSA_UNSUPPORTED (before
+  // any launch) when its buffers do not fit the dense ones.
+  auto filtered_rows = [&](int b0, int r0, int Rr) -> int32_t {
+    const int t_first = q_off + r0, t_last = q_off + r0 + Rr - 1;
+    const int64_t nc_first = (int64_t)t_first - cfg.n_window - cfg.n_sink + 1;
+    ScoreArgs a = score_args(b0, 1, r0, Rr);
+    const int ck = index_prefill_auto_chunk(a);
+    const int nsg = (a.n_keys + ck - 1) / ck;
+    const int cap = seg_cap_of(fp, ck, nc_first);
+    const int J = (t_last - cfg.n_window) / kSampM + 1;  // sampled positions 0, m, .., (J - 1) m
+    if (nsg > wl.max_segs || nsg > 256 || (size_t)Rr * nsg * cap * 8 > std::min<size_t>(wl.sbuf, (size_t)1 << 31) ||
+        J > 32768 || (int64_t)J > wl.samp_ld)
+      return LSA_UNSUPPORTED;
+    // 1. the sample: every row against positions j * m, j < J (no mask; the
+    //    threshold kernel takes each row's own candidates)
+    ScoreArgs sm = a;
+    sm.kstride = kSampM;
+    sm.n_keys = J;
+    sm.mask_off = J;
+    sm.pos_lo = 0;
+    sm.scores = samp;
+    sm.ld = wl.samp_ld;
+    sm.s_bstride = (int64_t)Rr * wl.samp_ld;
+    {
+      const int64_t n_qt = (Rr + 15) / 16;
+      int cks = 1024;
+      while (cks < 16384 && (int64_t)((J + 2 * cks - 1) / (2 * cks)) * n_qt >= 1024) cks *= 2;
+      sm.chunk_keys = cks;
+    }
+    int32_t s = hip_status(launch_index_score(sm, st));
+    if (s != LSA_OK) return s;
+    // 2. thresholds
+    FilterArgs f{};
+    f.sel = sa;
+    f.sel.n_rows = Rr;
+    f.sel.n_q = Rr;
+    f.sel.q_off = t_first;
+    f.sel.row0 = 0;
+    f.sel.idx = idx + ((int64_t)b0 * n_q + r0) * K_tot;
+    f.sel.n_sel = n_sel + (int64_t)b0 * n_q + r0;
+    f.samp = samp;
+    f.samp_ld = wl.samp_ld;
+    f.samp_m = kSampM;
+    f.tau = tau;
+    f.seg = sbuf;
+    f.seg_cnt = seg_cnt;
+    f.seg_chunks = nsg;
+    f.seg_cap = cap;
+    f.fail = fail;
+    s = hip_status(launch_filter_threshold(f, J, st));
+    if (s != LSA_OK) return s;
+    // 3. the full scoring pass, keeping the pairs at or above the thresholds
+    a.chunk_keys = ck;
+    a.tau = tau;
+    a.seg = sbuf;
+    a.seg_cnt = seg_cnt;
+    a.seg_chunks = nsg;
+    a.seg_cap = cap;
+    s = hip_status(launch_index_score(a, st));
+    if (s != LSA_OK) return s;
+    // 4. top-k of the survivors; 5. the dense path for the rows that failed
+    s = hip_status(launch_filter_select(f, fp.max_surv, st));
+    if (s != LSA_OK) return s;
+    return dense_rows(b0, 1, r0, Rr, fail);
+  };
+
   for (int b0 = 0; b0 < B; b0 += nb_pass) {
     const int nb = std::min(nb_pass, B - b0);
-    const SeqShift shift{ctx_len ? ctx_len + b0 : nullptr, n_q, n_k};
     for (int r0 = 0; r0 < n_q; r0 += R) {
       const int Rr = std::min(R, n_q - r0);
-      const int t_last = q_off + r0 + Rr - 1;
-      const int64_t nc_last = (int64_t)t_last - cfg.n_window - cfg.n_sink + 1;
-      if (nc_last > 0 && t_last + 1 > K_tot) {
-        ScoreArgs a{};
-        a.w = wa;
-        a.q = q_idx + ((int64_t)b0 * n_q + r0) * H_I * d_I;
-        a.k = k_idx + (int64_t)b0 * n_k * d_I;
-        a.B = nb;
-        a.n_q = Rr;
-        a.n_k = n_k;
-        a.H_I = H_I;
-        a.d_I = d_I;
-        a.q_bstride = (int64_t)n_q * H_I * d_I;
-        a.k_bstride = (int64_t)n_k * d_I;
-        a.s_bstride = (int64_t)Rr * n_k;
-        a.ld = n_k;
-        a.n_keys = std::min<int64_t>(n_k, (int64_t)t_last - cfg.n_window + 1);
-        a.mask_off = q_off + r0 - cfg.n_window;
-        a.pos_lo = cfg.n_sink;
-        a.blocks = nullptr;
-        a.fill_masked = 0;
-        a.scores = sbuf;
-        a.shift = shift;
-        if (a.n_keys > 0) {
-          s = hip_status(launch_index_score(a, st));
-          if (s != LSA_OK) return s;
-        }
+      // first row of the pass with kFilterMinCand candidates
+      int rf = Rr;
+      if (fp.on && nb == 1) {
+        const int64_t t_f = (int64_t)kFilterMinCand + cfg.n_window + cfg.n_sink - 1;
+        rf = (int)std::min<int64_t>(Rr, std::max<int64_t>(0, t_f - (q_off + r0)));
+        if (Rr - rf < 16 || (int64_t)q_off + r0 + rf + 1 <= K_tot) rf = Rr;
       }
-      // rows of the pass: sequence b0 + j, query r0 + i at row j * Rr + i
-      sa.scores = sbuf;
-      sa.ld = n_k;
-      sa.n_rows = nb * Rr;
-      sa.n_q = Rr;
-      sa.q_off = q_off + r0;
-      sa.row0 = 0;
-      sa.shift = shift;
-      select_plan(sa, nc_last);
-      select_bind_ws(sa, sel_ws, nb * Rr);
-      // nb > 1 only when Rr == n_q (r0 == 0), so the pass's output rows are
-      // contiguous in idx / n_sel
-      sa.idx = idx + ((int64_t)b0 * n_q + r0) * K_tot;
-      sa.n_sel = n_sel + (int64_t)b0 * n_q + r0;
-      s = hip_status(launch_select(sa, st));
-      if (s != LSA_OK) return s;
+      int32_t s = LSA_OK;
+      if (rf < Rr) {
+        s = filtered_rows(b0, r0 + rf, Rr - rf);
+        if (s == LSA_UNSUPPORTED) rf = Rr;  // nothing launched: the whole pass goes dense
+        else if (s != LSA_OK) return s;
+      }
+      if (rf > 0) {
+        s = dense_rows(b0, nb, r0, rf, nullptr);
+        if (s != LSA_OK) return s;
+      }
     }
   }
   return LSA_OK;
@@ -225,8 +393,7 @@ extern "C" int32_t lsa_select_topk(const int32_t* scores, const int8_t* q_idx, c
     need = select_ws_bytes(rows_pass, chunks_of(max_nc, k_cap), k_cap);
   } else {
     fused_pass(B, n_q, n_k, R, nb_pass);
-    const size_t rows = (size_t)R * nb_pass;
-    need = align_up(rows * n_k * sizeof(int32_t)) + select_ws_bytes((int)rows, chunks_of(max_nc, k_cap), k_cap);
+    need = fused_ws((int64_t)R * nb_pass, n_k, max_nc, k_cap, nb_pass == 1 && filter_plan(cfg, H_I, d_I).on).total;
   }
   need = align_up(std::max<size_t>(need, 1));
   if (ws_needed) *ws_needed = need;
@@ -285,8 +452,7 @@ extern "C" int32_t lsa_select_topk_ragged(const int8_t* q_idx, const int8_t* k_i
   if (s != LSA_OK) return s;
   int R = 0, nb_pass = 1;
   fused_pass(B, n_q, n_k, R, nb_pass);
-  const size_t rows = (size_t)R * nb_pass;
-  size_t need = align_up(rows * n_k * sizeof(int32_t)) + select_ws_bytes((int)rows, chunks_of(max_nc, k_cap), k_cap);
+  size_t need = fused_ws((int64_t)R * nb_pass, n_k, max_nc, k_cap, false).total;
   need = align_up(std::max<size_t>(need, 1));
   if (ws_needed) *ws_needed = need;
   if (ws == nullptr) return ws_needed ? LSA_OK : LSA_WORKSPACE;  // size query

@@ -27,6 +27,14 @@
 // weights in the epilogue (max + 24-bit multiply-add, weights read from LDS).
 // Both are exact, so the choice never changes a score.
 //
+// Filtered output: with a per-row threshold tau, a pair of queries' 32
+// scores (one per lane half) is kept where score >= tau of the lane's query.
+// A ballot gives the kept lanes, their rank within the half (mbcnt) their
+// place after the row's running count, and one 8-byte buffer store per lane
+// writes (score, position) (dropped lanes store out of range, so there is no
+// branch); each row's keys are visited by one wave in key order, so each
+// (row, chunk) segment is in ascending position order.
+//
 // Output layout of the 32x32x32 int8 MFMA: lane l holds key column l % 32 and
 // rows 8 * (i / 4) + 4 * (l / 32) + i % 4 of register i. A query owns H_I
 // consecutive rows (H_I / 32 whole M-blocks), so its head sum is a per-lane
@@ -112,16 +120,49 @@ __device__ __forceinline__ void read_b(const char* tile, int nb, v4i (&Bk)[KS]) 
   for (int j = 0; j < KS; ++j) Bk[j] = *(const v4i*)(tile + tile_off<DI>(32 * nb + c, g * (G::kParts / 2) + j));
 }
 
+// Filtered-output state of a wave: for query pair p (queries 2p, 2p + 1 of
+// the wave), lane half g holds query 2p + g's threshold and the byte offset
+// of its segment; cnt0 / cnt1 are the two queries' running counts
+// (wave-uniform). Stores go through a buffer resource over the segment
+// array, so a lane that keeps nothing stores to an offset past its end,
+// which the hardware drops: the epilogue has no branch.
+struct FiltState {
+  int tau[kQW / 2];
+  uint32_t segoff[kQW / 2];
+  int cnt0[kQW / 2], cnt1[kQW / 2];
+};
+constexpr uint32_t kDropOffset = 0x80000000u;  // segment arrays are at most 2 GiB
+
+// Keeps this lane's score s of key v (query 2p + g of the wave) when it is
+// visible and at least the query's threshold.
+__device__ __forceinline__ void filt_put(const ScoreArgs& a, FiltState& fs, int p, int s, int v, bool vis) {
+  const int g = lane_id() >> 5;
+  const bool keep = vis && s >= fs.tau[p];
+  const uint64_t m = __ballot(keep);
+  const uint32_t lo = (uint32_t)m, hi = (uint32_t)(m >> 32);
+  const int n_lo = __popc(lo);
+  // rank among the kept lanes of the whole wave; half 1 discounts half 0's
+  const int rank = (int)__builtin_amdgcn_mbcnt_hi(hi, __builtin_amdgcn_mbcnt_lo(lo, 0u));
+  const int off = rank + (g ? fs.cnt1[p] - n_lo : fs.cnt0[p]);
+  const uint32_t voff = keep && off < a.seg_cap ? fs.segoff[p] + 8u * (uint32_t)off : kDropOffset;
+  const __amdgpu_buffer_rsrc_t res =
+      uniform_rsrc(a.seg, (uint32_t)((int64_t)a.n_q * a.seg_chunks * a.seg_cap * 8));
+  __builtin_amdgcn_raw_buffer_store_b64(v2u{(uint32_t)s, (uint32_t)v}, res, voff, 0, 0);
+  fs.cnt0[p] += n_lo;
+  fs.cnt1[p] += __popc(hi);
+}
+
 // Scores of this wave's queries row0 .. row0+3 against keys [v_begin, v_end).
-template <int HI, int DI, bool FOLD>
+template <int HI, int DI, bool FOLD, bool FILT>
 __device__ __forceinline__ void score_chunk(const ScoreArgs& a, const v4i (&A)[kQW][HI / 32][DI / 32],
                                             const int* wl, const int8_t* kb, char* lds0, char* lds1,
-                                            int v_begin, int v_end, int row0, int32_t* sc) {
+                                            int v_begin, int v_end, int row0, int32_t* sc, FiltState& fs) {
   using G = TileGeom<DI>;
   constexpr int MB = HI / 32, KS = DI / 32;
   const int l = lane_id(), g = l >> 5, c = l & 31;
   const int vis_lo_wave = a.mask_off + row0;  // last key visible to every query of the wave
   const bool rows_ok = row0 + kQW <= a.n_q;
+  const int ks = a.kstride > 1 ? a.kstride : 1;
 
   // direct global -> LDS loads of one tile into a stage: load u of wave w
   // fills rows [8 (w * kPerWave + u), +8) (DI = 128) of the stage
@@ -129,17 +170,20 @@ __device__ __forceinline__ void score_chunk(const ScoreArgs& a, const v4i (&A)[k
   // not depend on the load, every load starting at a multiple of 8 rows), the
   // tile position goes in the scalar offset, and rows past the batch's keys
   // read as zero (range-checked by the buffer; such keys are never stored).
+  // (with a key stride, virtual key v is row v * ks: the same LDS layout,
+  // each lane's row and the tile position scaled by ks)
   const int wbase = __builtin_amdgcn_readfirstlane(wave_id() * G::kPerWave);
   const int lane_key = l / G::kParts;
-  const int lane_off = lane_key * DI + 16 * ((l % G::kParts) ^ ((lane_key / G::kRowsPerLine) & (G::kParts - 1)));
+  const int lane_off =
+      lane_key * ks * DI + 16 * ((l % G::kParts) ^ ((lane_key / G::kRowsPerLine) & (G::kParts - 1)));
   const __amdgpu_buffer_rsrc_t kres =
       __builtin_amdgcn_make_buffer_rsrc((void*)kb, (short)0, (int)((int64_t)a.n_k * DI), 0x00020000);
-  auto fetch = [&](int v0, char* stage) {
+  auto fetch = [&](int v0, char* stage) __attribute__((always_inline)) {
 #pragma unroll
     for (int u = 0; u < G::kPerWave; ++u) {
       const int n = wbase + u;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(kres, (__attribute__((address_space(3))) void*)(stage + n * 1024), 16,
-                                               lane_off, (v0 + n * (64 / G::kParts)) * DI, 0, 0);
+                                               lane_off, (v0 + n * (64 / G::kParts)) * ks * DI, 0, 0);
     }
   };
 
@@ -147,12 +191,12 @@ __device__ __forceinline__ void score_chunk(const ScoreArgs& a, const v4i (&A)[k
   // stages are separate LDS arrays, and the loop below names each one
   // explicitly, so the compiler can tell the next tile's loads apart from
   // this tile's reads and does not wait for them before reading.
-  auto step = [&](int v0, const char* tile, char* next) {
+  auto step = [&](int v0, const char* tile, char* next) __attribute__((always_inline)) {
     const bool more = v0 + kTileKeys < v_end;
     if (more) fetch(v0 + kTileKeys, next);
     // per block: each query's MFMAs and epilogue in turn, one 64-lane store
     // per pair of queries; the other wave on the SIMD fills the MFMA pipe
-    auto fast_block = [&](int nb) {
+    auto fast_block = [&](int nb) __attribute__((always_inline)) {
       v4i Bk[KS];
       read_b<DI, KS>(tile, nb, Bk);
 #pragma unroll
@@ -170,7 +214,10 @@ __device__ __forceinline__ void score_chunk(const ScoreArgs& a, const v4i (&A)[k
         const int s0 = head_sum<MB, FOLD>(acc0, wl);
         const int s1 = head_sum<MB, FOLD>(acc1, wl);
         // lane half g ends with query qp + g's full sum
-        sc[(int64_t)(row0 + qp + g) * a.ld + v0 + 32 * nb + c] = pair_sum32(s0, s1);
+        if constexpr (FILT)
+          filt_put(a, fs, qp / 2, pair_sum32(s0, s1), v0 + 32 * nb + c, true);
+        else
+          sc[(int64_t)(row0 + qp + g) * a.ld + v0 + 32 * nb + c] = pair_sum32(s0, s1);
       }
     };
     // every key of the tile visible to every query of the wave
@@ -206,7 +253,9 @@ __device__ __forceinline__ void score_chunk(const ScoreArgs& a, const v4i (&A)[k
             const int s1 = head_sum<MB, FOLD>(acc, wl);
             full = pair_sum32(s0, s1);
           }
-          if (row < a.n_q && v < v_end) {
+          if constexpr (FILT) {
+            filt_put(a, fs, qp / 2, full, v, row < a.n_q && v < v_end && v >= a.pos_lo && v <= a.mask_off + row);
+          } else if (row < a.n_q && v < v_end) {
             int32_t* dst = sc + (int64_t)row * a.ld + v;
             if (v >= a.pos_lo && v <= a.mask_off + row) *dst = full;
             else if (a.fill_masked) *dst = kMasked;
@@ -232,7 +281,7 @@ __device__ __forceinline__ void score_chunk(const ScoreArgs& a, const v4i (&A)[k
 // consecutive workgroups (which the dispatcher deals to the 8 XCDs in turn)
 // take consecutive query tiles of one key chunk, so every XCD gets the same
 // mix of chunks and the chunk's keys are shared in each XCD's L2.
-template <int HI, int DI>
+template <int HI, int DI, bool FILT>
 __global__ __launch_bounds__(kThreads, 2) void index_prefill_kernel(ScoreArgs a, int fold_ok, int chunk_keys) {
   using G = TileGeom<DI>;
   constexpr int MB = HI / 32, KS = DI / 32;
@@ -254,9 +303,18 @@ __global__ __launch_bounds__(kThreads, 2) void index_prefill_kernel(ScoreArgs a,
   int32_t* sc = a.scores + (int64_t)b * a.s_bstride;
   const int l = lane_id(), g = l >> 5, c = l & 31;
 
+  // only tiles with a flagged row run (a redo of some rows)
+  if (a.row_flags != nullptr) {
+    const int r = q0 + (int)threadIdx.x;
+    const int f = threadIdx.x < kQT && r <= last_row ? a.row_flags[r] : 0;
+    if (!__syncthreads_or(f)) return;
+  }
   // whole chunk invisible to every row of the workgroup
   if (v_begin > a.mask_off + last_row || v_end <= a.pos_lo) {
-    if (a.fill_masked) {
+    if constexpr (FILT) {
+      const int r = q0 + (int)threadIdx.x;
+      if (threadIdx.x < kQT && r <= last_row) a.seg_cnt[(int64_t)r * a.seg_chunks + chunk] = 0;
+    } else if (a.fill_masked) {
       for (int r = q0; r <= last_row; ++r)
         for (int v = v_begin + threadIdx.x; v < v_end; v += kThreads) sc[(int64_t)r * a.ld + v] = kMasked;
     }
@@ -290,6 +348,16 @@ __global__ __launch_bounds__(kThreads, 2) void index_prefill_kernel(ScoreArgs a,
   }
   const bool fold = __all(ok);
   const int8_t* kb = a.k + (int64_t)b * a.k_bstride;
+  FiltState fs;
+  if constexpr (FILT) {
+#pragma unroll
+    for (int p = 0; p < kQW / 2; ++p) {
+      const int r = min(row0 + 2 * p + g, a.n_q - 1);
+      fs.tau[p] = a.tau[r];
+      fs.segoff[p] = (uint32_t)(((int64_t)r * a.seg_chunks + chunk) * a.seg_cap * 8);
+      fs.cnt0[p] = fs.cnt1[p] = 0;
+    }
+  }
   if (fold) {
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
@@ -299,32 +367,51 @@ __global__ __launch_bounds__(kThreads, 2) void index_prefill_kernel(ScoreArgs a,
 #pragma unroll
         for (int j = 0; j < KS; ++j) A[q][mb][j] = scale_bytes(A[q][mb][j], wh);
     }
-    score_chunk<HI, DI, true>(a, A, wl, kb, lds0, lds1, v_begin, v_end, row0, sc);
+    score_chunk<HI, DI, true, FILT>(a, A, wl, kb, lds0, lds1, v_begin, v_end, row0, sc, fs);
   } else {
-    score_chunk<HI, DI, false>(a, A, wl, kb, lds0, lds1, v_begin, v_end, row0, sc);
+    score_chunk<HI, DI, false, FILT>(a, A, wl, kb, lds0, lds1, v_begin, v_end, row0, sc, fs);
+  }
+  if constexpr (FILT) {
+    // lane 0 of each half: the count of its query (rows past n_q store nothing)
+#pragma unroll
+    for (int p = 0; p < kQW / 2; ++p) {
+      const int r = row0 + 2 * p + g;
+      if (c == 0 && r < a.n_q) a.seg_cnt[(int64_t)r * a.seg_chunks + chunk] = g ? fs.cnt1[p] : fs.cnt0[p];
+    }
   }
 }
 
 template <int HI, int DI>
 hipError_t launch_t(const ScoreArgs& a, int fold_ok, hipStream_t st) {
-  // longer chunks load each query's A operand fewer times; they are taken
-  // while the grid still fills the chip for several rounds
   const int64_t n_qt = (a.n_q + kQT - 1) / kQT;
-  int ck = kMinChunkKeys;
-  while (ck < kMaxChunkKeys && (int64_t)((a.n_keys + 2 * ck - 1) / (2 * ck)) * n_qt * a.B >= kFullGrid) ck *= 2;
+  const int ck = a.chunk_keys > 0 ? a.chunk_keys : index_prefill_auto_chunk(a);
   const int64_t n_chunks = (a.n_keys + ck - 1) / ck;
   if (n_chunks * n_qt > INT32_MAX) return hipErrorInvalidValue;
+  if (a.tau != nullptr && (a.B != 1 || a.seg_chunks != n_chunks)) return hipErrorInvalidValue;
   dim3 grid((unsigned)n_chunks, (unsigned)n_qt, a.B);
   KernelTimer kt("index_prefill_kernel", st);
-  hipLaunchKernelGGL((index_prefill_kernel<HI, DI>), grid, dim3(kThreads), 0, st, a, fold_ok, ck);
+  if (a.tau != nullptr)
+    hipLaunchKernelGGL((index_prefill_kernel<HI, DI, true>), grid, dim3(kThreads), 0, st, a, fold_ok, ck);
+  else
+    hipLaunchKernelGGL((index_prefill_kernel<HI, DI, false>), grid, dim3(kThreads), 0, st, a, fold_ok, ck);
   return hipGetLastError();
 }
 
 }  // namespace
 
+// Longer chunks load each query's A operand fewer times; they are taken
+// while the grid still fills the chip for several rounds.
+int index_prefill_auto_chunk(const ScoreArgs& a) {
+  const int64_t n_qt = (a.n_q + kQT - 1) / kQT;
+  int ck = kMinChunkKeys;
+  while (ck < kMaxChunkKeys && (int64_t)((a.n_keys + 2 * ck - 1) / (2 * ck)) * n_qt * a.B >= kFullGrid) ck *= 2;
+  return ck;
+}
+
 bool index_prefill_supported(const ScoreArgs& a) {
   return a.blocks == nullptr && a.shift.ctx_len == nullptr && (a.H_I == 32 || a.H_I == 64) &&
-         (a.d_I == 64 || a.d_I == 128) && a.n_q >= kQT;
+         (a.d_I == 64 || a.d_I == 128) && a.n_q >= kQT && (a.chunk_keys <= 0 || a.chunk_keys % kTileKeys == 0) &&
+         (int64_t)(a.n_keys - 1) * (a.kstride > 1 ? a.kstride : 1) < a.n_k;
 }
 
 hipError_t launch_index_prefill(const ScoreArgs& a, hipStream_t st) {

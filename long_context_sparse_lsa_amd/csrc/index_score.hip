@@ -167,6 +167,8 @@ static hipError_t launch_t(const ScoreArgs& a, hipStream_t st) {
 
 hipError_t launch_index_score(const ScoreArgs& a, hipStream_t st) {
   if (index_prefill_supported(a)) return launch_index_prefill(a, st);
+  // key strides, row flags and filtered output exist only in the many-row variant
+  if (a.kstride > 1 || a.row_flags != nullptr || a.tau != nullptr || a.chunk_keys > 0) return hipErrorInvalidValue;
   if (index_decode_supported(a)) return launch_index_decode(a, st);
 #define LSA_CASE(h, d) \
   if (a.H_I == h && a.d_I == d) return launch_t<h, d>(a, st);

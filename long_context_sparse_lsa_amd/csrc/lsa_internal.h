@@ -44,12 +44,31 @@ struct ScoreArgs {
   int fill_masked;
   int32_t* scores;
   SeqShift shift;
+  // Many-row variant only (index_prefill below):
+  // virtual key v is row v * kstride of k (0 or 1: row v);
+  int kstride;
+  // keys per workgroup (a multiple of 256; 0: the launch chooses);
+  int chunk_keys;
+  // non-null: only query tiles holding a row i with row_flags[i] != 0 run;
+  const int32_t* row_flags;
+  // non-null: filtered output. Instead of dense scores, row i keeps the
+  // (score, position) pairs of its visible keys with score >= tau[i], in key
+  // order, in the segment of its key chunk c = v / chunk_keys:
+  // seg[2 * ((i * seg_chunks + c) * seg_cap + n)] for n < seg_cap, and
+  // seg_cnt[i * seg_chunks + c] counts all of them (it may exceed seg_cap).
+  // Needs B == 1 and chunk_keys set.
+  const int32_t* tau;
+  int32_t* seg;
+  int32_t* seg_cnt;
+  int seg_chunks, seg_cap;
 };
 hipError_t launch_index_score(const ScoreArgs& a, hipStream_t st);
 // Many-row variant (LDS-shared key tiles); covers direct keys (no blocks),
 // H_I in {32, 64}, n_q >= 16, no ragged shift.
 bool index_prefill_supported(const ScoreArgs& a);
 hipError_t launch_index_prefill(const ScoreArgs& a, hipStream_t st);
+// The keys per workgroup a launch of a with chunk_keys == 0 would take.
+int index_prefill_auto_chunk(const ScoreArgs& a);
 // Few-row variant (long per-wave key ranges streamed through registers);
 // direct keys or a block table with blk >= 32, H_I in {32, 64, 128}.
 bool index_decode_supported(const ScoreArgs& a);
@@ -97,6 +116,8 @@ struct SelectArgs {
   int chunk_e;     // candidates per thread of a chunk (select_plan)
   int chunk_nt;    // threads of a stage-A workgroup (select_plan)
   int k_cap;
+  // non-null: rows r with row_flags[r] == 0 are skipped
+  const int32_t* row_flags;
 };
 // Chunk geometry for rows of at most max_nc candidates keeping k_cap each:
 // the largest chunk count a plan can pick for such rows (workspace sizing),
@@ -112,6 +133,33 @@ constexpr int64_t kSelMaxSurvivors = 32 * 1024;
 size_t select_ws_bytes(int n_rows, int max_chunks, int k_cap);
 void select_bind_ws(SelectArgs& a, void* ws, int n_rows);
 hipError_t launch_select(const SelectArgs& a, hipStream_t st);
+
+// Thresholded selection of long FLAT rows (B == 1, no ragged shift). A sample
+// of every row's candidates (positions j * samp_m, scored exactly into
+// samp[r * samp_ld + j]) gives a per-row score threshold tau[r] (a high-rank
+// sample order statistic, INT32_MIN when the sample is too small); the full
+// scoring pass then keeps only the pairs at or above it (ScoreArgs::tau), and
+// the top-k of the row is the top-k of those survivors whenever they number
+// at least k (and no segment overflowed): the selection is then exact. Rows
+// where that fails get fail[r] = 1 and are redone by the dense path
+// (row_flags of the score and select launches); the others get 0.
+struct FilterArgs {
+  SelectArgs sel;  // FLAT geometry and outputs of the rows (row0 == 0, no shift)
+  const int32_t* samp;
+  int64_t samp_ld;
+  int samp_m;
+  int32_t* tau;
+  const int32_t* seg;
+  const int32_t* seg_cnt;
+  int seg_chunks, seg_cap;
+  int32_t* fail;
+};
+// The sampled candidates of the rows number at most max_ns (<= 32768).
+hipError_t launch_filter_threshold(const FilterArgs& f, int max_ns, hipStream_t st);
+// Rows with more than max_surv survivors (<= filter_select_capacity()) are
+// redone; seg_chunks <= 256.
+int filter_select_capacity();
+hipError_t launch_filter_select(const FilterArgs& f, int max_surv, hipStream_t st);
 
 // Sparse attention launches (bf16 bit patterns as uint16_t; sl2 is
 // scale * log2(e): softmax runs in base 2). K/V rows of one sequence are

@@ -67,6 +67,7 @@ __global__ __launch_bounds__(NT, MINW) void select_stage_a(SelectArgs a) {
   __shared__ SelShared<NT> sh;
   constexpr int CH = NT * E;
   const int r = blockIdx.x, j = blockIdx.y;
+  if (a.row_flags != nullptr && a.row_flags[r] == 0) return;
   const RowGeom gm = row_geom(a, r);
   if (gm.trivial) {
     if (j == 0) write_trivial<NT>(a, r, gm.t);
@@ -114,6 +115,7 @@ template <int E>
 __global__ __launch_bounds__(SEL_NT) void select_stage_m(SelectArgs a, int CH) {
   __shared__ SelShared<SEL_NT> sh;
   const int r = blockIdx.x, g = blockIdx.y;
+  if (a.row_flags != nullptr && a.row_flags[r] == 0) return;
   const RowGeom gm = row_geom(a, r);
   if (gm.trivial) return;
   const int n_chunks = (gm.nc + CH - 1) / CH;
@@ -149,6 +151,7 @@ template <int E>
 __global__ __launch_bounds__(SEL_NT) void select_stage_b(SelectArgs a, int CH) {
   __shared__ SelShared<SEL_NT> sh;
   const int r = blockIdx.x;
+  if (a.row_flags != nullptr && a.row_flags[r] == 0) return;
   const RowGeom gm = row_geom(a, r);
   if (gm.trivial) return;
   const int n_chunks = (gm.nc + CH - 1) / CH;
@@ -170,6 +173,108 @@ __global__ __launch_bounds__(SEL_NT) void select_stage_b(SelectArgs a, int CH) {
   int32_t* out = a.idx + (int64_t)r * a.out_ld + (a.mode == SEL_RAW ? 0 : a.n_sink);
   const int cnt = compact<E, SEL_NT>(u, T, shift, r_eq, sh, [&](int o, int e) { out[o] = ws_p[i0 + e]; });
   finalize<SEL_NT>(a, r, gm, cnt);
+}
+
+// Threshold of a row's sampled candidates: the j*-th largest sampled score,
+// j* = ceil(lam + 6 sqrt(lam) + 10) with lam = k * n_s / nc the expected
+// number of the row's top k among its n_s sampled candidates (of nc). Fewer
+// than j* of the top k fall in the sample except with odds far below 1e-9
+// for a sample that behaves like a random one, and then at least k
+// candidates score at or above the threshold; about j* * nc / n_s do. When
+// the sample holds j* or fewer scores, every candidate is kept.
+template <int E, int NT>
+__global__ __launch_bounds__(NT) void filter_threshold_kernel(FilterArgs f) {
+  __shared__ SelShared<NT> sh;
+  const SelectArgs& a = f.sel;
+  const int r = blockIdx.x;
+  const RowGeom gm = row_geom(a, r);
+  const int m = f.samp_m;
+  int32_t tau = INT32_MIN;
+  const int j_lo = (gm.c_lo + m - 1) / m;
+  const int j_hi = gm.trivial ? -1 : (gm.c_lo + gm.nc - 1) / m;
+  const int n_s = max(0, j_hi - j_lo + 1);
+  if (n_s > 0) {
+    uint32_t u[E];
+    load_keys<E>(f.samp + (int64_t)r * f.samp_ld, j_lo, n_s, u);
+    int n_valid;
+    uint32_t kmin, kmax;
+    chunk_stats<E, NT>(u, sh, n_valid, kmin, kmax);
+    const float lam = (float)gm.k * (float)n_s / (float)gm.nc;
+    const int jstar = (int)ceilf(lam + 6.0f * sqrtf(lam) + 10.0f);
+    if (jstar < n_valid) {
+      uint32_t T;
+      int shift, r_eq;
+      radix_select<E, NT>(u, kmin, kmax, jstar, sh, T, shift, r_eq);
+      // T has zeros below `shift`: every sampled key >= T is among the kept
+      tau = (int32_t)(T ^ 0x80000000u);
+    }
+  }
+  if (threadIdx.x == 0) f.tau[r] = tau;
+}
+
+// Top-k of a row's survivors: segments (row, chunk) of (score, position)
+// pairs in ascending position order, concatenated in chunk order, E per
+// thread (blocked). The row fails (fail = 1, outputs left to the redo) when
+// a segment overflowed, the survivors do not fit or are fewer than k.
+template <int E, int NT>
+__global__ __launch_bounds__(NT) void filter_select_kernel(FilterArgs f) {
+  __shared__ SelShared<NT> sh;
+  __shared__ int pref[NT + 1];
+  const SelectArgs& a = f.sel;
+  const int r = blockIdx.x, tid = threadIdx.x;
+  const RowGeom gm = row_geom(a, r);
+  if (gm.trivial) {
+    write_trivial<NT>(a, r, gm.t);
+    if (tid == 0) f.fail[r] = 0;
+    return;
+  }
+  const int nsg = f.seg_chunks;
+  const int cnt = tid < nsg ? f.seg_cnt[(int64_t)r * nsg + tid] : 0;
+  uint32_t total;
+  const uint32_t off = block_excl_scan<NT>((uint32_t)min(cnt, f.seg_cap + 1), sh, &total);
+  if (tid < nsg) pref[tid] = (int)off;
+  if (tid == 0) pref[nsg] = (int)total;
+  const int over = __syncthreads_or(cnt > f.seg_cap);
+  if (over || (int)total < gm.k || total > (uint32_t)(NT * E)) {
+    if (tid == 0) f.fail[r] = 1;
+    return;
+  }
+  // entries [i0, i0 + E) of the concatenation
+  const int i0 = tid * E;
+  int sg = 0;
+  for (int lo = 0, hi = nsg - 1; lo <= hi;) {  // last segment starting at or before i0
+    const int mid = (lo + hi) >> 1;
+    if (pref[mid] <= i0) {
+      sg = mid;
+      lo = mid + 1;
+    } else {
+      hi = mid - 1;
+    }
+  }
+  uint32_t u[E];
+  int pos[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const int i = i0 + e;
+    u[e] = 0u;
+    pos[e] = -1;
+    if (i < (int)total) {
+      while (pref[sg + 1] <= i) ++sg;
+      const int32_t* ent = f.seg + (((int64_t)r * nsg + sg) * f.seg_cap + (i - pref[sg])) * 2;
+      const v2u x = *(const v2u*)ent;
+      u[e] = score_key((int32_t)x[0]);
+      pos[e] = (int)x[1];
+    }
+  }
+  int n_valid;
+  uint32_t kmin, kmax, T;
+  chunk_stats<E, NT>(u, sh, n_valid, kmin, kmax);
+  int shift, r_eq;
+  if (!plan_trivial(gm.k, n_valid, T, shift, r_eq)) radix_select<E, NT>(u, kmin, kmax, gm.k, sh, T, shift, r_eq);
+  int32_t* out = a.idx + (int64_t)r * a.out_ld + a.n_sink;
+  const int kept = compact<E, NT>(u, T, shift, r_eq, sh, [&](int o, int e) { out[o] = pos[e]; });
+  finalize<NT>(a, r, gm, kept);
+  if (tid == 0) f.fail[r] = 0;
 }
 
 // Chunk geometry: E candidates per thread of a workgroup of NT threads.
@@ -295,6 +400,35 @@ void select_bind_ws(SelectArgs& a, void* ws, int n_rows) {
   } else {
     a.ws2_score = a.ws2_pos = nullptr;
   }
+}
+
+hipError_t launch_filter_threshold(const FilterArgs& f, int max_ns, hipStream_t st) {
+  if (f.sel.n_rows <= 0) return hipSuccess;
+  const dim3 grid(f.sel.n_rows);
+  KernelTimer kt("filter_threshold_kernel", st);
+  if (max_ns <= 256 * 16) hipLaunchKernelGGL((filter_threshold_kernel<16, 256>), grid, dim3(256), 0, st, f);
+  else if (max_ns <= 256 * 32) hipLaunchKernelGGL((filter_threshold_kernel<32, 256>), grid, dim3(256), 0, st, f);
+  else if (max_ns <= SEL_NT * 32) hipLaunchKernelGGL((filter_threshold_kernel<32, SEL_NT>), grid, dim3(SEL_NT), 0, st, f);
+  else return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+// Survivor capacity of the survivor selection: 256 threads (several rows per
+// CU at once) up to 8192 survivors, then wider workgroups.
+int filter_select_capacity() { return 32 * SEL_NT; }
+
+hipError_t launch_filter_select(const FilterArgs& f, int max_surv, hipStream_t st) {
+  if (f.sel.n_rows <= 0) return hipSuccess;
+  if (f.seg_chunks < 1 || f.seg_chunks > 256) return hipErrorInvalidValue;
+  const dim3 grid(f.sel.n_rows);
+  KernelTimer kt("filter_select_kernel", st);
+  if (max_surv <= 256 * 8) hipLaunchKernelGGL((filter_select_kernel<8, 256>), grid, dim3(256), 0, st, f);
+  else if (max_surv <= 256 * 16) hipLaunchKernelGGL((filter_select_kernel<16, 256>), grid, dim3(256), 0, st, f);
+  else if (max_surv <= 256 * 32) hipLaunchKernelGGL((filter_select_kernel<32, 256>), grid, dim3(256), 0, st, f);
+  else if (max_surv <= 512 * 32) hipLaunchKernelGGL((filter_select_kernel<32, 512>), grid, dim3(512), 0, st, f);
+  else if (max_surv <= SEL_NT * 32) hipLaunchKernelGGL((filter_select_kernel<32, SEL_NT>), grid, dim3(SEL_NT), 0, st, f);
+  else return hipErrorInvalidValue;
+  return hipGetLastError();
 }
 
 // The geometry must come from select_plan (k_cap set first); one reduction
