@@ -313,11 +313,15 @@ def test_fused_select_ragged_batch(n_q, H_I):
 
 
 # ------------------------------------------------------------------ HI
-@pytest.mark.parametrize("blk", [32, 64, 128])
-def test_block_summary(blk):
-    say(f"block summary blk={blk}")
+@pytest.mark.parametrize("blk,d_I", [(32, 128), (64, 128), (128, 128), (256, 128), (300, 128), (1024, 128),
+                                     (64, 64), (96, 64)])
+def test_block_summary(blk, d_I):
+    """Blocks of up to 256 rows take the 16-bit packed sums, longer ones the
+    plain sums; full blocks of a power-of-two size round by shifts, partial
+    tails and other sizes by division."""
+    say(f"block summary blk={blk} d_I={d_I}")
     n_k = blk * 37 + 13
-    k = i8((2, n_k, 128), -128, 127, "bs", blk)
+    k = i8((2, n_k, d_I), -128, 127, "bs", blk, d_I)
     kb = L.lsa_block_summary(k, blk)
     for b in range(2):
         assert np.array_equal(np_(kb[b]).astype(np.int64), O.block_summary(np_(k[b]), blk))
