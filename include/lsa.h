@@ -94,7 +94,7 @@ int32_t lsa_index_score(const int8_t* q_idx, const int8_t* k_idx, const int32_t*
  * longest row the call can see (for lsa_select_topk_ragged: the cache
  * capacity n_k).
  * Fused path, one sequence per pass (prefill): rows with at least 16384
- * candidates first score every 32nd candidate; a high order statistic of that
+ * candidates first score every 64th candidate; a high order statistic of that
  * sample is a per-row threshold, the full scoring pass keeps only the
  * (score, position) pairs at or above it, and the row's top-k is taken from
  * those survivors when they number at least k_dyn (then exactly the same

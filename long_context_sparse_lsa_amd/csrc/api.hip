@@ -126,7 +126,7 @@ extern "C" int32_t lsa_index_score(const int8_t* q_idx, const int8_t* k_idx, con
 // keep about (lam + 6 sqrt(lam) + 10) * kSampM pairs per row (lam = k / kSampM)
 // instead of writing every score, and the survivors' top-k is exact whenever
 // they number at least k; other rows are redone by the dense path.
-constexpr int kSampM = 32;
+constexpr int kSampM = 64;
 constexpr int kFilterMinCand = 16384;
 
 struct FilterPlan {

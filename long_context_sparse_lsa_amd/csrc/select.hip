@@ -213,9 +213,12 @@ __global__ __launch_bounds__(NT) void filter_threshold_kernel(FilterArgs f) {
 }
 
 // Top-k of a row's survivors: segments (row, chunk) of (score, position)
-// pairs in ascending position order, concatenated in chunk order, E per
-// thread (blocked). The row fails (fail = 1, outputs left to the redo) when
-// a segment overflowed, the survivors do not fit or are fewer than k.
+// pairs in ascending position order, concatenated in chunk order. Thread t
+// takes the ee = ceil(total / NT) consecutive entries from t * ee (blocked:
+// thread order is position order, every thread holding some); their
+// addresses come first, then all loads issue back to back. The row fails
+// (fail = 1, outputs left to the redo) when a segment overflowed, the
+// survivors do not fit or are fewer than k.
 template <int E, int NT>
 __global__ __launch_bounds__(NT) void filter_select_kernel(FilterArgs f) {
   __shared__ SelShared<NT> sh;
@@ -239,40 +242,42 @@ __global__ __launch_bounds__(NT) void filter_select_kernel(FilterArgs f) {
     if (tid == 0) f.fail[r] = 1;
     return;
   }
-  // entries [i0, i0 + E) of the concatenation
-  const int i0 = tid * E;
+  const int n = (int)total;
+  const int ee = (n + NT - 1) / NT;  // entries per thread (<= E)
+  const int i0 = tid * ee;
+  // segment of entry i0, then the entry offsets of [i0, i0 + ee) (clamped to
+  // the last entry: loads past it read a valid pair and are masked below)
   int sg = 0;
-  for (int lo = 0, hi = nsg - 1; lo <= hi;) {  // last segment starting at or before i0
+  for (int lo = 0, hi = nsg - 1; lo <= hi;) {
     const int mid = (lo + hi) >> 1;
-    if (pref[mid] <= i0) {
+    if (pref[mid] <= min(i0, n - 1)) {
       sg = mid;
       lo = mid + 1;
     } else {
       hi = mid - 1;
     }
   }
-  uint32_t u[E];
-  int pos[E];
+  int eoff[E];
 #pragma unroll
   for (int e = 0; e < E; ++e) {
-    const int i = i0 + e;
-    u[e] = 0u;
-    pos[e] = -1;
-    if (i < (int)total) {
-      while (pref[sg + 1] <= i) ++sg;
-      const int32_t* ent = f.seg + (((int64_t)r * nsg + sg) * f.seg_cap + (i - pref[sg])) * 2;
-      const v2u x = *(const v2u*)ent;
-      u[e] = score_key((int32_t)x[0]);
-      pos[e] = (int)x[1];
-    }
+    const int i = min(i0 + min(e, ee - 1), n - 1);
+    while (pref[sg + 1] <= i) ++sg;
+    eoff[e] = (sg * f.seg_cap + (i - pref[sg])) * 2;
   }
+  const int32_t* seg_r = f.seg + (int64_t)r * nsg * f.seg_cap * 2;
+  v2u x[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) x[e] = *(const v2u*)(seg_r + eoff[e]);
+  uint32_t u[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) u[e] = e < ee && i0 + e < n ? score_key((int32_t)x[e][0]) : 0u;
   int n_valid;
   uint32_t kmin, kmax, T;
   chunk_stats<E, NT>(u, sh, n_valid, kmin, kmax);
   int shift, r_eq;
   if (!plan_trivial(gm.k, n_valid, T, shift, r_eq)) radix_select<E, NT>(u, kmin, kmax, gm.k, sh, T, shift, r_eq);
   int32_t* out = a.idx + (int64_t)r * a.out_ld + a.n_sink;
-  const int kept = compact<E, NT>(u, T, shift, r_eq, sh, [&](int o, int e) { out[o] = pos[e]; });
+  const int kept = compact<E, NT, true>(u, T, shift, r_eq, sh, [&](int o, int e) { out[o] = (int)x[e][1]; });
   finalize<NT>(a, r, gm, kept);
   if (tid == 0) f.fail[r] = 0;
 }

@@ -184,8 +184,10 @@ __device__ void radix_select(const uint32_t (&u)[E], uint32_t kmin, uint32_t kma
 // builds bit masks of its entries above and equal to the threshold; one
 // scan of the packed counts (above << 16 | equal; each at most 32768) gives
 // both prefixes, and an entry equal to the threshold is kept while fewer
-// than r_eq equal entries precede it. Only the kept entries are visited.
-template <int E, int NT, class Emit>
+// than r_eq equal entries precede it. Only the kept entries are visited
+// (STATIC: every e in turn, so that emit may index a register array by e
+// without a per-lane index).
+template <int E, int NT, bool STATIC = false, class Emit>
 __device__ int compact(const uint32_t (&u)[E], uint32_t T, int shift, int r_eq, SelShared<NT>& sh, Emit emit) {
   static_assert(E <= 32, "one mask bit per entry");
   const uint32_t Ts = T >> shift;
@@ -206,10 +208,16 @@ __device__ int compact(const uint32_t (&u)[E], uint32_t T, int shift, int r_eq, 
     keep |= em & (0u - em);  // lowest remaining equal entry
     em &= em - 1u;
   }
-  while (keep != 0u) {
-    const int e = __ffs(keep) - 1;
-    keep &= keep - 1u;
-    emit(o++, e);
+  if constexpr (STATIC) {
+#pragma unroll
+    for (int e = 0; e < E; ++e)
+      if ((keep >> e) & 1u) emit(o++, e);
+  } else {
+    while (keep != 0u) {
+      const int e = __ffs(keep) - 1;
+      keep &= keep - 1u;
+      emit(o++, e);
+    }
   }
   return (int)(tot >> 16) + min((int)(tot & 0xffffu), r_eq);
 }

@@ -1,7 +1,7 @@
 """GPU parity of the thresholded prefill selection (lsa_select_topk, fused).
 
 Rows with at least 16384 candidates take a threshold from an exactly scored
-sample of their candidates (every 32nd position), and the full scoring pass
+sample of their candidates (every 64th position), and the full scoring pass
 keeps only the (score, position) pairs at or above it; the top-k of those
 survivors is the row's top-k whenever they number at least k_dyn. Rows where
 that cannot be shown (too few survivors, a full segment) are redone by the
@@ -73,9 +73,10 @@ def test_filter_random_rows_two_sequences():
 
 
 def test_filter_planted_sample_keys_force_redo():
-    """Keys at the sampled positions (multiples of 32) are made to dominate
-    the scores of every third row: their samples then set a threshold that
-    only about j* keys reach, fewer than k_dyn, and those rows are redone."""
+    """Keys at every multiple of 32 (a superset of the sampled positions) are
+    made to dominate the scores of every third row: their samples then set a
+    threshold that only a few times j* keys reach, fewer than k_dyn, and
+    those rows are redone."""
     Lq = 20480
     say(f"filter planted L={Lq}")
     q = i8((1, Lq, 64, 128), -16, 15, "pq")
