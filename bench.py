@@ -423,15 +423,17 @@ def run_decode(args, wl, torch):
     summary_us = None
     if wl.blk:
         # the HI block summaries of the whole cache (built once per cache, then
-        # kept current on append): timed apart from the step
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for _ in range(5):
+        # kept current on append): timed apart from the step, as the kernel's
+        # own launch time (the library's event timing)
+        for _ in range(3):  # warm-up, as for the step
             L.lsa_block_summary(k_idx, wl.blk)
-        e1.record()
         torch.cuda.synchronize()
-        summary_us = e0.elapsed_time(e1) * 1e3 / 5
+        L.lsa_kernel_timing(True)
+        for _ in range(20):
+            L.lsa_block_summary(k_idx, wl.blk)
+        torch.cuda.synchronize()
+        summary_us = L.lsa_kernel_time("block_summary_kernel")[0] * 1e3
+        L.lsa_kernel_timing(False)
     step_ws = torch.empty(64 << 20, dtype=torch.uint8, device=dev) if (wl.blk and args.fused) else None
     torch.cuda.synchronize()
     timer = EventTimer(torch)
