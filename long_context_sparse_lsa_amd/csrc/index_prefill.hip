@@ -6,18 +6,20 @@
 // head weights, int32 result -- is fixed by this library.)
 //
 // GEMM view: M = (query, head) rows, N = keys, K = d_I. A workgroup of 4 waves
-// (one per SIMD) owns 16 consecutive queries, 4 per wave, and walks a chunk
-// of 4096 to 16384 keys in tiles of 256 keys that are staged once in LDS
-// (double-buffered) and read by all four waves. A wave keeps its 4 queries'
-// rows (4 * H_I rows) in registers as the A operand for the whole chunk, so
-// every 16-byte LDS read of the key operand feeds 4 * H_I / 32 MFMAs, and the
+// (one per SIMD) owns 8 consecutive queries, 2 per wave, and walks a chunk
+// of 4096 to 16384 keys in tiles of 128 keys that are staged once in LDS
+// (double-buffered) and read by all four waves. A wave keeps its 2 queries'
+// rows (2 * H_I rows) in registers as the A operand for the whole chunk, so
+// every 16-byte LDS read of the key operand feeds 2 * H_I / 32 MFMAs, and the
 // A operand is loaded once per chunk (the longest chunk that still leaves
 // several rounds of workgroups).
 //
-// Per 32-key block a wave runs, for each of its 4 queries, H_I/32 * d_I/32
+// Per 32-key block a wave runs, for each of its 2 queries, H_I/32 * d_I/32
 // MFMAs and a ReLU / head-sum epilogue on the VALU. The MFMA pipe and the
-// VALU overlap across waves, not within one: two workgroups share a CU, so
-// each SIMD holds two waves and one's epilogue runs under the other's MFMAs.
+// VALU overlap across waves, not within one: three workgroups share a CU (at
+// most 168 registers per lane, 33 KB of LDS each), so each SIMD holds three
+// waves and their epilogues run under one another's MFMAs (2.3% faster at
+// the 128K prefill than two waves of 4 queries with 256-key tiles).
 //
 // Weight folding: w[h] * max(0, x) == max(0, w[h] * x) for w[h] >= 0, and
 // (w[h] q) . k == w[h] (q . k). When every weight is >= 0 and every product
@@ -48,14 +50,14 @@ namespace lsa {
 
 namespace {
 
-constexpr int kTileKeys = 256;  // keys per LDS tile
+constexpr int kTileKeys = 128;  // keys per LDS tile
 constexpr int kWaves = 4;
-constexpr int kQW = 4;                   // queries per wave
+constexpr int kQW = 2;                   // queries per wave
 constexpr int kQT = kWaves * kQW;        // queries per workgroup
 constexpr int kThreads = 64 * kWaves;
 constexpr int kMinChunkKeys = 4096;      // keys per workgroup: 4096, 8192 or 16384
 constexpr int kMaxChunkKeys = 16384;
-constexpr int kFullGrid = 2048;           // workgroups of four rounds over the chip
+constexpr int kFullGrid = 2048;           // workgroups of about three rounds over the chip
 constexpr int kBlocks = kTileKeys / 32;  // 32-key blocks per tile
 
 // A key tile in LDS: rows of DI bytes, unpadded, written by direct
@@ -282,7 +284,7 @@ __device__ __forceinline__ void score_chunk(const ScoreArgs& a, const v4i (&A)[k
 // take consecutive query tiles of one key chunk, so every XCD gets the same
 // mix of chunks and the chunk's keys are shared in each XCD's L2.
 template <int HI, int DI, bool FILT>
-__global__ __launch_bounds__(kThreads, 2) void index_prefill_kernel(ScoreArgs a, int fold_ok, int chunk_keys) {
+__global__ __launch_bounds__(kThreads, 3) void index_prefill_kernel(ScoreArgs a, int fold_ok, int chunk_keys) {
   using G = TileGeom<DI>;
   constexpr int MB = HI / 32, KS = DI / 32;
   __shared__ __attribute__((aligned(16))) char lds0[G::kBytes];
