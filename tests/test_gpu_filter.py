@@ -38,12 +38,13 @@ def i8(shape, lo, hi, *seed):
     return synth.int8_uniform(shape, lo, hi, synth.seed_of("filter", *seed), DEV)
 
 
-def check_rows_against_dense(q_idx, k_idx, w, q_off, what, oracle_rows=()):
+def check_rows_against_dense(q_idx, k_idx, w, q_off, what, oracle_rows=(), cfg=(NS, W, KD)):
     """Fused (thresholded) lists == dense lists from the full score matrix."""
-    idx, n_sel = L.lsa_select_topk(q_idx, k_idx, w, NS, W, KD, q_off=q_off)
-    idx2, n_sel2 = L.lsa_select_topk(q_idx, k_idx, w, NS, W, KD, q_off=q_off)
+    ns, win, kd = cfg
+    idx, n_sel = L.lsa_select_topk(q_idx, k_idx, w, ns, win, kd, q_off=q_off)
+    idx2, n_sel2 = L.lsa_select_topk(q_idx, k_idx, w, ns, win, kd, q_off=q_off)
     S = L.lsa_index_score(q_idx, k_idx, w, q_off=q_off)
-    ref, ref_n = L.lsa_select_topk(scores=S, n_sink=NS, n_window=W, k_dyn=KD, q_off=q_off)
+    ref, ref_n = L.lsa_select_topk(scores=S, n_sink=ns, n_window=win, k_dyn=kd, q_off=q_off)
     torch.cuda.synchronize()
     assert torch.equal(idx, idx2) and torch.equal(n_sel, n_sel2), f"{what}: not deterministic"
     bad = (idx != ref).any(dim=-1) | (n_sel != ref_n)
@@ -55,7 +56,7 @@ def check_rows_against_dense(q_idx, k_idx, w, q_off, what, oracle_rows=()):
         t = q_off + i
         qn, kn = np_(q_idx[b, i:i + 1]), np_(k_idx[b, : t + 1])
         s_t = O.index_scores(qn, kn, w, q_off=t)[0]
-        exp = O.select_flat(s_t, t, NS, W, KD)
+        exp = O.select_flat(s_t, t, ns, win, kd)
         assert int(n_sel[b, i]) == len(exp) and np.array_equal(np_(idx[b, i, : len(exp)]), exp), \
             f"{what}: b{b} t{t} differs from the oracle"
     say(f"  {what}: {B}x{q_idx.shape[1]} rows equal the dense selection")
@@ -122,3 +123,16 @@ def test_filter_h32_d64():
     wmax = ((1 << 31) - 1) // (64 * 16384 * 32)
     w = synth.int_weights(32, -wmax, wmax, synth.seed_of("filter-w", 5))
     check_rows_against_dense(q, k, w, 0, "h32d64", [(0, 18999), (0, 17500)])
+
+
+@pytest.mark.parametrize("ns,win,kd", [(0, 0, 1020), (4, 64, 4096), (1, 1, 300)])
+def test_filter_budgets(ns, win, kd):
+    """No sinks and no window; a large k_dyn (the widest survivor kernel); a
+    small k_dyn whose sample threshold keeps several times k."""
+    Lq = 20480
+    say(f"filter budgets ns={ns} W={win} k={kd}")
+    q = i8((1, Lq, 64, 128), -16, 15, "bq", kd)
+    k = i8((1, Lq, 128), -16, 15, "bk", kd)
+    w = synth.int_weights(64, 1, 8, synth.seed_of("filter-w", 6, kd))
+    rows = [(0, 16384 + win + ns), (0, Lq - 1)]
+    check_rows_against_dense(q, k, w, 0, f"budget {ns}+{win}+{kd}", rows, cfg=(ns, win, kd))
