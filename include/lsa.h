@@ -362,10 +362,15 @@ int32_t lsa_sparse_attn_decode_mtp(const lsa_bf16* q, const lsa_bf16* k_cache,
  *   lsa_kernel_time(name, ms_mean, launches): mean duration in ms and count
  *     of the recorded launches of kernel `name` (waits for their events).
  *     Names: "index_prefill_kernel", "index_decode_kernel",
- *     "index_score_kernel", "select_stage_a", "select_stage_b",
+ *     "index_score_kernel", "select_stage_a", "select_stage_m",
+ *     "select_stage_b", "filter_threshold_kernel", "filter_select_kernel",
  *     "attn_prefill_kernel", "attn_decode_partial", "attn_decode_merge",
- *     "block_summary_kernel", "mtp_index_kernel". An unknown name reports 0
- *     launches.
+ *     "block_summary_kernel", "mtp_index_kernel", "hi_step_kernel",
+ *     "attn_bwd_kernel", "bwd_count_kernel", "bwd_scan_kernel",
+ *     "bwd_fill_kernel", "bwd_reduce_kernel", "attn_bwd_finish_kernel",
+ *     "kl_warmup_kernel", "fill_zero_kernel". An unknown name reports 0
+ *     launches. While timing is off (the default) no event is created and
+ *     a launch pays one relaxed load.
  * Errors: LSA_INVALID_ARG for NULL pointers, LSA_HIP for a failed event call.
  * Not for concurrent use from several host threads while launches run. */
 int32_t lsa_kernel_timing(int32_t on);
