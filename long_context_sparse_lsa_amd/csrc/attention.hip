@@ -250,7 +250,20 @@ hipError_t launch_attn_prefill(const PrefillArgs& a, hipStream_t st) {
 template <int TW, int KS>
 __global__ __launch_bounds__(64 * TW * KS) void attn_decode_partial(DecodeArgs a) {
   __shared__ __attribute__((aligned(16))) char lds_all[DecodeCfg<TW, KS>::kBytes];
-  decode_partial_body<TW, KS>(a, blockIdx.x, blockIdx.y, blockIdx.z, lds_all);
+  int bx = blockIdx.x, split = blockIdx.y, b = blockIdx.z;
+  const int nx = gridDim.x, ny = gridDim.y;
+  const int64_t total = (int64_t)nx * ny * gridDim.z;
+  if (nx == 2 && total % 16 == 0) {
+    // workgroups go to the 8 XCDs in turn: the two workgroups of a part
+    // (which gather the same blocks) take consecutive slots of one XCD, so
+    // the second finds the blocks in that XCD's L2
+    const int64_t id = blockIdx.x + (int64_t)nx * (blockIdx.y + (int64_t)ny * blockIdx.z);
+    const int64_t j = (id % 8) * (total / 8) + id / 8;
+    bx = (int)(j % 2);
+    split = (int)((j / 2) % ny);
+    b = (int)(j / 2 / ny);
+  }
+  decode_partial_body<TW, KS>(a, bx, split, b, lds_all);
 }
 
 // One row per 16 threads, 8 output dims per thread.
