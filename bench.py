@@ -87,6 +87,14 @@ class EventTimer:
         return sum(a.elapsed_time(b) for a, b in ev) / max(1, len(ev)), len(ev)
 
 
+def spread(xs):
+    """Median, min and max of per-step times (event-timed)."""
+    xs = sorted(xs)
+    n = len(xs)
+    med = xs[n // 2] if n % 2 else 0.5 * (xs[n // 2 - 1] + xs[n // 2])
+    return {"median": round(med, 4), "min": round(xs[0], 4), "max": round(xs[-1], 4)}
+
+
 def copy_gbs(torch, nbytes=1 << 30, reps=5):
     """Read + write GB/s of a plain 1 GiB device-to-device copy (event-timed)."""
     src = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
@@ -249,11 +257,17 @@ def run_prefill(args, wl, torch):
         step(plain)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    step_ev = []
     for _ in range(args.steps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
         idx, n_sel = step(timer)
+        e1.record()
+        step_ev.append((e0, e1))
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_step = wall * 1e3 / args.steps
+    step_stats = spread([a.elapsed_time(b) for a, b in step_ev])
     sel_ms, _ = timer.ms("select")
     attn_ms, n_attn = timer.ms("attn")
 
@@ -288,6 +302,7 @@ def run_prefill(args, wl, torch):
                   "scored_pairs": pairs,
                   "attn_ms_per_layer": round(attn_ms, 4), "attn_bf16_tflops": round(attn_tflops, 1),
                   "attn_gather_gbs": round(gathered / (attn_ms * 1e-3) / 1e9, 1),
+                  "step_ms": step_stats,
                   "kernels": kernel_parts(kt)},
         "roofline": roof,
     }
@@ -296,6 +311,7 @@ def run_prefill(args, wl, torch):
         rate, n, dt = prefill_cpu_baseline(wl, q_idx, k_idx, w, q, k, v, args.cpu_seconds)
         out["cpu_baseline"] = {"value": round(rate, 3), "unit": "tokens/s", "cores": cpu_threads(),
                                "kind": "oracle",
+                               "extrapolated_s_per_step": round(wl.L / rate, 1),
                                "sample": f"{n} query rows drawn uniformly from [{wl.K_tot}, {wl.L}) in {dt:.1f} s; "
                                          f"each: exact scores against all earlier keys, top-k, "
                                          f"{wl.n_layers}x float64 attention"}
@@ -479,6 +495,17 @@ def run_decode(args, wl, torch):
         graph.replay()
     torch.cuda.synchronize()
     us_step = (time.perf_counter() - t0) * 1e6 / args.steps
+    # the spread of single replays, from a separate untimed pass (events
+    # between replays would add their host latency to the timed loop)
+    step_ev = []
+    for _ in range(args.steps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        graph.replay()
+        e1.record()
+        step_ev.append((e0, e1))
+    torch.cuda.synchronize()
+    step_stats = spread([a.elapsed_time(b) * 1e3 for a, b in step_ev])
     # the same replays with the last-level cache (256 MB MALL) flushed before
     # each one by reading 512 MB, untimed: a step that follows other work (a
     # read leaves clean lines, so the step pays no write-back of the flush)
@@ -527,6 +554,7 @@ def run_decode(args, wl, torch):
                    "context": N, "n_q": wl.n_q, "H": wl.H, "K_tot": K_tot, "n_split": wl.n_split,
                    "hier_blk": wl.blk, "launch": "hip_graph_replay", "parallelism": "none"},
         "parts": {"eager_us_per_step": round(us_eager, 2), "cold_cache_us_per_step": round(us_cold, 2),
+                  "step_us": step_stats,
                   "select_us": round(sel_ms * 1e3, 2), "attn_us": round(attn_ms * 1e3, 2),
                   "fused_step_us": round(fused_ms * 1e3, 2),
                   "block_summary": None if summary_us is None else {
