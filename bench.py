@@ -153,20 +153,49 @@ def kernel_times(L, torch, step, steps, park=False):
     return out
 
 
-def measured_mfma_peak(torch, L, kind, n_wg=256 * 8, iters=2048, reps=3):
+def measured_mfma_peak(torch, L, kind, data=None, n_wg=256 * 8, iters=2048, reps=3):
     """TOP/s (kind 0, int8) or TFLOP/s (kind 1, bf16) of the library's
-    matrix-core probe: register-only MFMA chains on every CU, event-timed."""
+    matrix-core probe: register-only MFMA chains on every CU (two waves per
+    SIMD, one round), event-timed. With data = (a, b), the operands are fragments of
+    those device tensors (a different pair for every instruction) instead of
+    constants."""
     sink = torch.empty(n_wg, dtype=torch.int32, device="cuda")
-    L.lsa_probe_mfma(kind, n_wg, iters // 8, sink)  # warm the clock up
+
+    def launch(it):
+        if data is None:
+            return L.lsa_probe_mfma(kind, n_wg, it, sink)
+        return L.lsa_probe_mfma_data(kind, n_wg, it, data[0], data[1], sink)
+
+    launch(iters // 8)  # warm the clock up
     best = 0.0
     for _ in range(reps):
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
-        ops = L.lsa_probe_mfma(kind, n_wg, iters, sink)
+        ops = launch(iters)
         e1.record()
         torch.cuda.synchronize()
         best = max(best, ops / (e0.elapsed_time(e1) * 1e-3) / 1e12)
     return best
+
+
+def probe_operands(torch, wl, kind):
+    """Operand bytes with the workload's value distribution, for the probe:
+    int8 -- the indexer's A operand (query bytes times the head weight, as the
+    kernel folds them when every product fits int8) and its key bytes; bf16 --
+    N(0, 1) keys and queries as the attention kernels multiply them."""
+    from long_context_sparse_lsa_amd import synth
+    if kind == 0:
+        q = synth.int8_uniform((1024, wl.H_I, wl.d_I), wl.qk_lo, wl.qk_hi, synth.seed_of("probe", "q"), "cuda")
+        w = torch.as_tensor(synth.int_weights(wl.H_I, wl.w_lo, wl.w_hi, synth.seed_of("probe", "w")),
+                            dtype=torch.int32, device="cuda")
+        a = q.to(torch.int32) * w.view(1, -1, 1)
+        if wl.w_lo >= 0 and int(a.min()) >= -128 and int(a.max()) <= 127:
+            q = a.to(torch.int8)
+        k = synth.int8_uniform((16384, wl.d_I), wl.qk_lo, wl.qk_hi, synth.seed_of("probe", "k"), "cuda")
+        return q.contiguous(), k
+    a = synth.bf16_normal((16384, 128), synth.seed_of("probe", "bk"), "cuda")
+    b = synth.bf16_normal((16384, 128), synth.seed_of("probe", "bq"), "cuda")
+    return a, b
 
 
 def roofline(bound, name, work_per_step, kt, peak, unit):
@@ -605,6 +634,17 @@ def main():
         mp = measured_mfma_peak(torch, L, kind)
         roof["measured_peak"] = round(mp, 1)
         roof["frac_of_measured"] = round(roof["achieved"] / mp, 4)
+        # the same on operands with the workload's values: the chip lowers
+        # its clock under the power of switching operand bits, so this is
+        # the ceiling for the kernel's own data
+        mpd = measured_mfma_peak(torch, L, kind, data=probe_operands(torch, wl, kind))
+        roof["measured_peak_data"] = round(mpd, 1)
+        roof["frac_of_measured_data"] = round(roof["achieved"] / mpd, 4)
+    if "attn_bf16_tflops" in out.get("parts", {}):
+        # prefill attention against the bf16 probe on N(0, 1) operands
+        mpa = measured_mfma_peak(torch, L, 1, data=probe_operands(torch, wl, 1))
+        out["parts"]["attn_bf16_measured_peak_data"] = round(mpa, 1)
+        out["parts"]["attn_frac_of_measured_data"] = round(out["parts"]["attn_bf16_tflops"] / mpa, 4)
     if roof["bound"] == "hbm":
         # the bandwidth a plain device copy reaches on this GPU in this run: the
         # attainable ceiling next to the 8 TB/s figure

@@ -389,6 +389,24 @@ int32_t lsa_kernel_time(const char* name, float* ms_mean, int32_t* launches);
  * sizes, LSA_UNSUPPORTED for another kind, LSA_HIP for a launch error. */
 int32_t lsa_probe_mfma(int32_t kind, int32_t n_wg, int32_t iters, int32_t* sink, double* ops, void* stream);
 
+/* The same probe with operands from caller data: every lane loads 8 A and 8
+ * B fragments of 16 bytes (lane t of the grid reads 16-byte units
+ * 8t .. 8t + 7 of a and 8t + 3 .. 8t + 10 of b, each index taken modulo the
+ * array's unit count) and chain j multiplies A fragment j by B fragment
+ * j + 1, so consecutive instructions see different operands. Passing arrays
+ * of the kernel's own operands (the indexer's folded query bytes and key
+ * bytes; bf16 keys and queries) gives the rate the matrix cores sustain on
+ * that data: their power draw, and the clock the chip holds under it, grow
+ * with the number of operand bits that switch between instructions.
+ *   kind, n_wg, iters, sink, ops, stream: as lsa_probe_mfma
+ *   a, b: DEVICE, 16-byte aligned, read only; a_bytes, b_bytes >= 16 (a
+ *     trailing part shorter than 16 bytes is not read)
+ * Errors: LSA_INVALID_ARG for NULL or misaligned pointers, sizes below 16 or
+ * non-positive counts, LSA_UNSUPPORTED for another kind, LSA_HIP for a
+ * launch error. */
+int32_t lsa_probe_mfma_data(int32_t kind, int32_t n_wg, int32_t iters, const void* a, int64_t a_bytes, const void* b,
+                            int64_t b_bytes, int32_t* sink, double* ops, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -55,6 +55,8 @@ SIGNATURES = {
     "lsa_kernel_timing": (_I, [_I]),
     "lsa_kernel_time": (_I, [ctypes.c_char_p, ctypes.POINTER(_F), ctypes.POINTER(_I)]),
     "lsa_probe_mfma": (_I, [_I, _I, _I, _P, ctypes.POINTER(ctypes.c_double), _P]),
+    "lsa_probe_mfma_data": (_I, [_I, _I, _I, _P, ctypes.c_int64, _P, ctypes.c_int64, _P,
+                                 ctypes.POINTER(ctypes.c_double), _P]),
     "lsa_sparse_attn_decode_noalloc": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _F, _P, _P, _P]),
     "lsa_noalloc_scratch_bytes": (_Z, []),
     "lsa_sparse_attn_backward": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _P, _P, _P, _P, _Z,
@@ -516,4 +518,22 @@ def lsa_probe_mfma(kind, n_wg, iters, sink):
     ops = ctypes.c_double(0.0)
     _check("lsa_probe_mfma", load().lsa_probe_mfma(int(kind), int(n_wg), int(iters), _ptr(sink), ctypes.byref(ops),
                                                    _stream()))
+    return float(ops.value)
+
+
+def lsa_probe_mfma_data(kind, n_wg, iters, a, b, sink):
+    """The probe with operands drawn from device tensors a and b (any dtype,
+    contiguous, 16-byte aligned, at least 16 bytes): kind 0 reads them as
+    int8 fragments, kind 1 as bf16. Returns the operations one launch
+    performs."""
+    _dev(sink, torch.int32, "sink")
+    if sink.numel() < n_wg:
+        raise ValueError("sink needs n_wg entries")
+    for t, nm in ((a, "a"), (b, "b")):
+        if not (t.is_cuda and t.is_contiguous()):
+            raise ValueError(f"{nm} must be a contiguous device tensor")
+    ops = ctypes.c_double(0.0)
+    _check("lsa_probe_mfma_data",
+           load().lsa_probe_mfma_data(int(kind), int(n_wg), int(iters), _ptr(a), a.numel() * a.element_size(), _ptr(b),
+                                      b.numel() * b.element_size(), _ptr(sink), ctypes.byref(ops), _stream()))
     return float(ops.value)

@@ -262,3 +262,24 @@ def test_kernel_timing_without_launches():
     assert lib.lsa_kernel_time(b"attn_prefill_kernel", ctypes.byref(ms), ctypes.byref(n)) == L.LSA_OK
     assert n.value == 0 and ms.value == 0.0
     assert lib.lsa_kernel_timing(0) == L.LSA_OK
+
+
+def test_probe_argument_checks():
+    """Both matrix-core probes reject bad arguments before any launch."""
+    lib = L.load()
+    f, ops = P(FAKE), ctypes.c_double(0.0)
+    assert lib.lsa_probe_mfma(0, 8, 4, None, ctypes.byref(ops), None) == L.LSA_INVALID_ARG
+    assert lib.lsa_probe_mfma(0, 8, 4, P(FAKE + 2), ctypes.byref(ops), None) == L.LSA_INVALID_ARG
+    assert lib.lsa_probe_mfma(0, 0, 4, f, ctypes.byref(ops), None) == L.LSA_INVALID_ARG
+    assert lib.lsa_probe_mfma(2, 8, 4, f, ctypes.byref(ops), None) == L.LSA_UNSUPPORTED
+    ok = [0, 8, 4, f, 64, f, 64, f]
+    bad = list(ok); bad[3] = None
+    assert lib.lsa_probe_mfma_data(*bad, ctypes.byref(ops), None) == L.LSA_INVALID_ARG
+    bad = list(ok); bad[5] = P(FAKE + 8)      # b not 16-byte aligned
+    assert lib.lsa_probe_mfma_data(*bad, ctypes.byref(ops), None) == L.LSA_INVALID_ARG
+    bad = list(ok); bad[4] = 15               # fewer than one 16-byte fragment
+    assert lib.lsa_probe_mfma_data(*bad, ctypes.byref(ops), None) == L.LSA_INVALID_ARG
+    bad = list(ok); bad[2] = 0
+    assert lib.lsa_probe_mfma_data(*bad, ctypes.byref(ops), None) == L.LSA_INVALID_ARG
+    bad = list(ok); bad[0] = 3
+    assert lib.lsa_probe_mfma_data(*bad, ctypes.byref(ops), None) == L.LSA_UNSUPPORTED
