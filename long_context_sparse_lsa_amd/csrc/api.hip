@@ -128,6 +128,10 @@ extern "C" int32_t lsa_index_score(const int8_t* q_idx, const int8_t* k_idx, con
 // they number at least k; other rows are redone by the dense path.
 constexpr int kSampM = 64;
 constexpr int kFilterMinCand = 16384;
+// Thresholded rows go in passes of up to this many dense passes' rows (the
+// segments are far smaller than dense scores), which halves or quarters the
+// launches per row and the part of each launch spent draining its last round.
+constexpr int kFiltPassMul = 4;
 
 struct FilterPlan {
   bool on = false;
@@ -159,7 +163,8 @@ int seg_cap_of(const FilterPlan& p, int ck, int64_t nc_min) {
 
 // Workspace of the fused path for passes of `rows` rows: the dense score
 // buffer (which the filtered rows' segments share), the selection's chunk
-// workspace, then the sample scores, thresholds, fail flags and segment counts.
+// workspace, then the sample scores, thresholds, fail flags and segment counts
+// (these four for thresholded passes of up to kFiltPassMul * rows rows).
 struct FusedWs {
   size_t sbuf, sel, samp, tau, fail, cnt, total;
   int64_t samp_ld;
@@ -170,12 +175,13 @@ FusedWs fused_ws(int64_t rows, int n_k, int64_t max_nc, int k_cap, bool filter) 
   w.sbuf = align_up((size_t)rows * n_k * sizeof(int32_t));
   w.sel = align_up(select_ws_bytes((int)rows, chunks_of(max_nc, k_cap), k_cap));
   if (filter) {
+    const int64_t fr = rows * kFiltPassMul;
     w.samp_ld = ((int64_t)n_k / kSampM + 1 + 3) / 4 * 4;
     w.max_segs = (n_k + 4095) / 4096;
-    w.samp = align_up((size_t)rows * w.samp_ld * sizeof(int32_t));
-    w.tau = align_up((size_t)rows * sizeof(int32_t));
+    w.samp = align_up((size_t)fr * w.samp_ld * sizeof(int32_t));
+    w.tau = align_up((size_t)fr * sizeof(int32_t));
     w.fail = w.tau;
-    w.cnt = align_up((size_t)rows * w.max_segs * sizeof(int32_t));
+    w.cnt = align_up((size_t)fr * w.max_segs * sizeof(int32_t));
   }
   w.total = w.sbuf + w.sel + w.samp + w.tau + w.fail + w.cnt;
   return w;
@@ -267,9 +273,10 @@ static int32_t fused_select(const int8_t* q_idx, const int8_t* k_idx, const WArg
     return hip_status(launch_select(d, st));
   };
 
-  // thresholded: rows [r0, r0 + Rr) of sequence b0, every one non-trivial
-  // with at least kFilterMinCand candidates. Returns LSA_UNSUPPORTED (before
-  // any launch) when its buffers do not fit the dense ones.
+  // thresholded: rows [r0, r0 + Rr) of sequence b0 (Rr <= kFiltPassMul * R),
+  // every one non-trivial with at least kFilterMinCand candidates. Returns
+  // LSA_UNSUPPORTED (before any launch) when its segments do not fit the
+  // dense score buffer.
   auto filtered_rows = [&](int b0, int r0, int Rr) -> int32_t {
     const int t_first = q_off + r0, t_last = q_off + r0 + Rr - 1;
     const int64_t nc_first = (int64_t)t_first - cfg.n_window - cfg.n_sink + 1;
@@ -278,8 +285,9 @@ static int32_t fused_select(const int8_t* q_idx, const int8_t* k_idx, const WArg
     const int nsg = (a.n_keys + ck - 1) / ck;
     const int cap = seg_cap_of(fp, ck, nc_first);
     const int J = (t_last - cfg.n_window) / kSampM + 1;  // sampled positions 0, m, .., (J - 1) m
-    if (nsg > wl.max_segs || nsg > 256 || (size_t)Rr * nsg * cap * 8 > std::min<size_t>(wl.sbuf, (size_t)1 << 31) ||
-        J > 32768 || (int64_t)J > wl.samp_ld)
+    if (Rr > kFiltPassMul * R || nsg > wl.max_segs || nsg > 256 ||
+        (size_t)Rr * nsg * cap * 8 > std::min<size_t>(wl.sbuf, (size_t)1 << 31) || J > 32768 ||
+        (int64_t)J > wl.samp_ld)
       return LSA_UNSUPPORTED;
     // 1. the sample: every row against positions j * m, j < J (no mask; the
     //    threshold kernel takes each row's own candidates)
@@ -328,15 +336,20 @@ static int32_t fused_select(const int8_t* q_idx, const int8_t* k_idx, const WArg
     a.seg_cap = cap;
     s = hip_status(launch_index_score(a, st));
     if (s != LSA_OK) return s;
-    // 4. top-k of the survivors; 5. the dense path for the rows that failed
+    // 4. top-k of the survivors; 5. the dense path for the rows that failed,
+    //    in passes of at most R rows (the dense buffer's size)
     s = hip_status(launch_filter_select(f, fp.max_surv, st));
     if (s != LSA_OK) return s;
-    return dense_rows(b0, 1, r0, Rr, fail);
+    for (int x = 0; x < Rr; x += R) {
+      s = dense_rows(b0, 1, r0 + x, std::min(R, Rr - x), fail + x);
+      if (s != LSA_OK) return s;
+    }
+    return LSA_OK;
   };
 
   for (int b0 = 0; b0 < B; b0 += nb_pass) {
     const int nb = std::min(nb_pass, B - b0);
-    for (int r0 = 0; r0 < n_q; r0 += R) {
+    for (int r0 = 0; r0 < n_q;) {
       const int Rr = std::min(R, n_q - r0);
       // first row of the pass with kFilterMinCand candidates
       int rf = Rr;
@@ -346,8 +359,17 @@ static int32_t fused_select(const int8_t* q_idx, const int8_t* k_idx, const WArg
         if (Rr - rf < 16 || (int64_t)q_off + r0 + rf + 1 <= K_tot) rf = Rr;
       }
       int32_t s = LSA_OK;
+      int r_next = r0 + Rr;
       if (rf < Rr) {
-        s = filtered_rows(b0, r0 + rf, Rr - rf);
+        // the thresholded rows from r0 + rf on, through the next passes' rows
+        // while their segments fit (the longest of kFiltPassMul, 2, 1 passes)
+        s = LSA_UNSUPPORTED;
+        for (int m = kFiltPassMul; m >= 1 && s == LSA_UNSUPPORTED; m /= 2) {
+          const int f_end = (int)std::min<int64_t>(n_q, (int64_t)r0 + (int64_t)m * R);
+          if (m > 1 && f_end <= r0 + Rr) continue;
+          s = filtered_rows(b0, r0 + rf, f_end - (r0 + rf));
+          if (s == LSA_OK) r_next = f_end;
+        }
         if (s == LSA_UNSUPPORTED) rf = Rr;  // nothing launched: the whole pass goes dense
         else if (s != LSA_OK) return s;
       }
@@ -355,6 +377,7 @@ static int32_t fused_select(const int8_t* q_idx, const int8_t* k_idx, const WArg
         s = dense_rows(b0, nb, r0, rf, nullptr);
         if (s != LSA_OK) return s;
       }
+      r0 = r_next;
     }
   }
   return LSA_OK;

@@ -136,3 +136,33 @@ def test_filter_budgets(ns, win, kd):
     w = synth.int_weights(64, 1, 8, synth.seed_of("filter-w", 6, kd))
     rows = [(0, 16384 + win + ns), (0, Lq - 1)]
     check_rows_against_dense(q, k, w, 0, f"budget {ns}+{win}+{kd}", rows, cfg=(ns, win, kd))
+
+
+def test_filter_multi_pass_rows():
+    """A sequence of several dense passes (10922 rows each at 48K keys): the
+    thresholded rows go in passes of two dense passes' rows where four would
+    overflow the segment buffer, then of the remaining rows at once; every
+    list equals the dense selection."""
+    Lq = 49152
+    say(f"filter multi-pass L={Lq}")
+    q = i8((1, Lq, 64, 128), -16, 15, "mq")
+    k = i8((1, Lq, 128), -16, 15, "mk")
+    w = synth.int_weights(64, 1, 8, synth.seed_of("filter-w", 7))
+    rows = [(0, 17500), (0, 21843), (0, 32765), (0, 32766), (0, 49151)]
+    check_rows_against_dense(q, k, w, 0, "multi-pass", rows)
+
+
+def test_filter_multi_pass_redo():
+    """Planted sample keys defeat the threshold of every third row of a
+    multi-pass sequence: the failed rows of a long thresholded pass are redone
+    in dense-pass pieces, each with its own part of the fail flags."""
+    Lq = 49152
+    say(f"filter multi-pass planted L={Lq}")
+    q = i8((1, Lq, 64, 128), -16, 15, "mpq")
+    k = i8((1, Lq, 128), -16, 15, "mpk")
+    k[0, ::32, :64] = 15
+    hit = torch.arange(Lq, device=DEV) % 3 == 0
+    q[0, hit, :, :64] = 15
+    w = synth.int_weights(64, 1, 8, synth.seed_of("filter-w", 8))
+    rows = [(0, 21843), (0, 21844), (0, 43689), (0, 49149)]
+    check_rows_against_dense(q, k, w, 0, "multi-pass planted", rows)
