@@ -29,7 +29,7 @@ KERNELS = ("index_prefill_kernel", "index_decode_kernel", "index_score_kernel", 
            "block_summary_kernel", "mtp_index_kernel", "attn_bwd_kernel", "bwd_count_kernel",
            "bwd_scan_blocks_kernel", "bwd_scan_totals_kernel", "bwd_scan_add_kernel", "bwd_fill_kernel",
            "bwd_reduce_kernel", "attn_bwd_finish_kernel", "fill_zero_kernel", "kl_warmup_kernel",
-           "mfma_probe_kernel", "hi_step_kernel", "filter_threshold_kernel",
+           "mfma_probe_kernel", "mfma_probe_data_kernel", "hi_step_kernel", "filter_threshold_kernel",
            "filter_select_kernel", "select_stage_m")
 
 
