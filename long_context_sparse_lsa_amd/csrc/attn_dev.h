@@ -537,6 +537,9 @@ __device__ __forceinline__ void decode_partial_body(const DecodeArgs& a, int bx,
 // Merge of row brow (of B * n_q * H), dims d .. d + 7.
 template <int NS>
 __device__ __forceinline__ void decode_merge_row(const DecodeArgs& a, int64_t brow, int d) {
+  // products and sums each rounded to fp32 (no fused multiply-add), so the
+  // result is set by the tree alone
+#pragma clang fp contract(off)
   const int R = a.n_q * a.H;
   const int b = (int)(brow / R), r = (int)(brow % R);
   const int64_t row0 = (int64_t)b * a.n_split * R + r;
@@ -544,41 +547,47 @@ __device__ __forceinline__ void decode_merge_row(const DecodeArgs& a, int64_t br
   const float* pl = a.ws_l + row0;
   const _Float16* po = a.ws_o + row0 * kD + d;
   float mj[NS], lv[NS];
-  v8h ov[NS];
 #pragma unroll
   for (int j = 0; j < NS; ++j) {
     const bool in = j < a.n_split;
     const int jr = in ? j * R : 0;
     mj[j] = in ? pm[jr] : -INFINITY;
     lv[j] = in ? pl[jr] : 0.f;
-    ov[j] = in ? *(const v8h*)(po + (int64_t)jr * kD) : v8h{};
   }
   float M = -INFINITY;
 #pragma unroll
   for (int j = 0; j < NS; ++j) M = fmaxf(M, mj[j]);
   // each part's normalised output weighed by l * 2^(m - M), summed in a
-  // fixed binary tree in fp32
-  float acc[NS][8];
+  // fixed binary tree in fp32 (pairs of parts, then pairs of pairs, ...).
+  // The tree is evaluated part by part, keeping one pending subtree sum per
+  // level: part j closes the subtrees of the levels where j has a one bit.
+  constexpr int LG = NS <= 1 ? 0 : NS <= 2 ? 1 : NS <= 4 ? 2 : NS <= 8 ? 3 : NS <= 16 ? 4 : NS <= 32 ? 5 : 6;
+  static_assert((1 << LG) == NS, "NS is a power of two up to 64");
+  float sl[LG + 1], so[LG + 1][8];
 #pragma unroll
   for (int j = 0; j < NS; ++j) {
-    const float wj = (j < a.n_split && M != -INFINITY) ? __builtin_amdgcn_exp2f(mj[j] - M) : 0.f;
-    lv[j] *= wj;
+    const bool in = j < a.n_split;
+    const v8h ov = in ? *(const v8h*)(po + (int64_t)j * R * kD) : v8h{};
+    const float wj = (in && M != -INFINITY) ? __builtin_amdgcn_exp2f(mj[j] - M) : 0.f;
+    float cl = lv[j] * wj, co[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) acc[j][e] = (float)ov[j][e] * lv[j];
-  }
+    for (int e = 0; e < 8; ++e) co[e] = (float)ov[e] * cl;
+    int lvl = 0;
 #pragma unroll
-  for (int s = 1; s < NS; s <<= 1)
+    for (; lvl < LG && ((j >> lvl) & 1); ++lvl) {
+      cl = sl[lvl] + cl;
 #pragma unroll
-    for (int j = 0; j + s < NS; j += 2 * s) {
-      lv[j] += lv[j + s];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) acc[j][e] += acc[j + s][e];
+      for (int e = 0; e < 8; ++e) co[e] = so[lvl][e] + co[e];
     }
-  const float Lam = lv[0];
+    sl[lvl] = cl;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) so[lvl][e] = co[e];
+  }
+  const float Lam = sl[LG];
   const float inv = Lam > 0.f ? 1.f / Lam : 0.f;
   v4u out;
 #pragma unroll
-  for (int e = 0; e < 4; ++e) out[e] = pack_bf16x2(acc[0][2 * e] * inv, acc[0][2 * e + 1] * inv);
+  for (int e = 0; e < 4; ++e) out[e] = pack_bf16x2(so[LG][2 * e] * inv, so[LG][2 * e + 1] * inv);
   *(v4u*)(a.o + brow * kD + d) = out;
   if (a.lse && d == 0) a.lse[brow] = Lam > 0.f ? (M + log2f(Lam)) * 0.69314718055994531f : -INFINITY;
 }
