@@ -607,8 +607,8 @@ def run_decode(args, wl, torch):
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(the sharding design is described in DESIGN.md). Run with --gpus 1.", file=sys.stderr)
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
+              "(how it would shard is a design note, not code). Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
     import torch
     from long_context_sparse_lsa_amd import configs
