@@ -166,3 +166,16 @@ def test_filter_multi_pass_redo():
     w = synth.int_weights(64, 1, 8, synth.seed_of("filter-w", 8))
     rows = [(0, 21843), (0, 21844), (0, 43689), (0, 49149)]
     check_rows_against_dense(q, k, w, 0, "multi-pass planted", rows)
+
+
+def test_filter_multi_pass_two_sequences():
+    """Two sequences of several dense passes each, with a chunk of rows at
+    the end of a longer cache (q_off > 0): the thresholded passes of the
+    second sequence start from its own rows, keys and outputs."""
+    n_k, n_q = 49152, 40000
+    say(f"filter multi-pass B=2 n_k={n_k} n_q={n_q}")
+    q = i8((2, n_q, 64, 128), -16, 15, "m2q")
+    k = i8((2, n_k, 128), -16, 15, "m2k")
+    w = synth.int_weights(64, 1, 8, synth.seed_of("filter-w", 9))
+    rows = [(0, 0), (1, 0), (1, 12000), (0, 25000), (1, 39999)]
+    check_rows_against_dense(q, k, w, n_k - n_q, "multi-pass B=2", rows)
