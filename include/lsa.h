@@ -396,8 +396,8 @@ int32_t lsa_probe_mfma(int32_t kind, int32_t n_wg, int32_t iters, int32_t* sink,
  * j + 1, so consecutive instructions see different operands. Passing arrays
  * of the kernel's own operands (the indexer's folded query bytes and key
  * bytes; bf16 keys and queries) gives the rate the matrix cores sustain on
- * that data: their power draw, and the clock the chip holds under it, grow
- * with the number of operand bits that switch between instructions.
+ * that data: their power draw grows with the number of operand bits that
+ * switch between instructions, and the clock the chip holds falls with it.
  *   kind, n_wg, iters, sink, ops, stream: as lsa_probe_mfma
  *   a, b: DEVICE, 16-byte aligned, read only; a_bytes, b_bytes >= 16 (a
  *     trailing part shorter than 16 bytes is not read)
